@@ -1,0 +1,445 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference of the local MoE forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU
+ * baseline may load this library.  It shares no source, header, helper or table with the
+ * GPU library and includes nothing from it.
+ *
+ * Source: "ruDNN" user guide (docs.rs, ruDNN 0.1.72, German README):
+ *   section 3 "MoE-Workflow"        -- the sequence logits -> softmax/top-k -> compact
+ *                                      dispatch -> SwiGLU experts -> weighted combine;
+ *   section 4 "Routing-Vertrag"     -- logits [T,E] in F32/F16/BF16, 1 <= top_k <= E, FP32
+ *                                      softmax over all experts before top-k, ties to the
+ *                                      lower expert id, optional renormalisation then a cast
+ *                                      to the logits dtype, NaN weights for rows with NaN,
+ *                                      +inf or only -inf, indices U32 [T,top_k];
+ *   section 5 "Expertengewichte und Verteilung" -- tokens [T,H], gate/up [E,I,H],
+ *                                      down [E,H,I], no capacity drops, order inside an
+ *                                      expert unspecified, a stored map restores order;
+ *   section 6 "MoE aufrufen"        -- the staged call forms and the full forward.
+ *
+ * Arithmetic: every value is widened exactly to double; sums, exp and divisions run in
+ * double; a result is rounded once (round-to-nearest-even) to its storage dtype at the
+ * points where the method stores a tensor (routing weights, the SwiGLU hidden activation,
+ * the expert output, the combined output).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - A "NaN row" is a row with any NaN, any +inf, or all entries -inf.  Its k indices are
+ *    0..k-1 (all probabilities are NaN, none exceeds another: treated as tied, lower id
+ *    first) and its k weights are NaN, with or without renormalisation.
+ *  - The k selected experts of a row are listed by descending probability, equal
+ *    probabilities by ascending id.
+ *  - The weight cast to the logits dtype happens whether or not renormalisation is on.
+ *  - Rows inside one expert are ordered by (token, slot) ascending -- one of the valid
+ *    orders; any order is correct per section 5.
+ *  - token_map[t][j] is the dispatched row that holds copy j of token t (combine gathers).
+ *  - SwiGLU: h = silu(gate . x) * (up . x), silu(z) = z / (1 + exp(-z)); y = down . h;
+ *    no biases (section 5: "bias-freie Expertengewichte").
+ *  - An index >= E given to dispatch gets map -1 and its token's combined row is NaN.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+
+/* ------------------------------------------------------------------------------------ */
+/* Codecs, written from the IEEE 754-2008 binary16 definition and the bfloat16 definition  */
+/* (the upper 16 bits of an IEEE binary32).                                                */
+/* ------------------------------------------------------------------------------------ */
+
+static double dec_f16(uint16_t b) {
+    int s = b >> 15, e = (b >> 10) & 0x1f, m = b & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/2^10) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+static double dec_bf16(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Round x to the nearest number with p significand bits and minimum normal exponent emin
+ * (values below 2^emin share the fixed quantum 2^(emin-p+1)), ties to even; beyond maxval
+ * the result is +-inf. */
+static double round_fmt(double x, int p, int emin, double maxval) {
+    if (isnan(x) || isinf(x) || x == 0.0) return x;
+    int e;
+    frexp(fabs(x), &e);                 /* |x| = f * 2^e with f in [0.5, 1) */
+    int lead = e - 1;                    /* exponent of the leading bit */
+    if (lead < emin) lead = emin;
+    double q = ldexp(1.0, lead - (p - 1));
+    double r = nearbyint(x / q) * q;     /* x / q is exact; nearbyint rounds half to even */
+    if (fabs(r) > maxval) r = copysign(INFINITY, x);
+    return r;
+}
+
+static uint16_t enc_bf16(double x) {
+    if (isnan(x)) return 0x7fc0;
+    double r = round_fmt(x, 8, -126, ldexp(255.0, 120)); /* max = (2 - 2^-7) * 2^127 */
+    float f = (float)r;                   /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+static uint16_t enc_f16(double x) {
+    if (isnan(x)) return 0x7e00;
+    double r = round_fmt(x, 11, -14, 65504.0);
+    uint16_t s = signbit(r) ? 0x8000 : 0;
+    double a = fabs(r);
+    if (isinf(a)) return s | 0x7c00;
+    if (a == 0.0) return s;
+    if (a < ldexp(1.0, -14)) return s | (uint16_t)(a / ldexp(1.0, -24)); /* subnormal */
+    int e;
+    frexp(a, &e);
+    int lead = e - 1;
+    uint16_t m = (uint16_t)(a / ldexp(1.0, lead - 10) - 1024.0);
+    return s | (uint16_t)((lead + 15) << 10) | m;
+}
+
+static double load_val(const void* p, int dt, int64_t i) {
+    switch (dt) {
+    case OR_F32: return (double)((const float*)p)[i];
+    case OR_F16: return dec_f16(((const uint16_t*)p)[i]);
+    default: return dec_bf16(((const uint16_t*)p)[i]);
+    }
+}
+
+/* One rounding of a double to the storage dtype, returned as the stored value (double). */
+static double round_to(double x, int dt) {
+    switch (dt) {
+    case OR_F32: return (double)(float)x;  /* C conversion rounds to nearest even */
+    case OR_F16: return dec_f16(enc_f16(x));
+    default: return dec_bf16(enc_bf16(x));
+    }
+}
+
+static void store_val(void* p, int dt, int64_t i, double x) {
+    switch (dt) {
+    case OR_F32: ((float*)p)[i] = (float)x; break;
+    case OR_F16: ((uint16_t*)p)[i] = enc_f16(x); break;
+    default: ((uint16_t*)p)[i] = enc_bf16(x); break;
+    }
+}
+
+static size_t dt_size(int dt) { return dt == OR_F32 ? 4 : 2; }
+
+int oracle_dtype_size(int dt) { return (int)dt_size(dt); }
+
+void oracle_decode(const void* src, int dt, int64_t n, double* dst) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = load_val(src, dt, i);
+}
+
+void oracle_encode(const double* src, int dt, int64_t n, void* dst) {
+    for (int64_t i = 0; i < n; ++i) store_val(dst, dt, i, src[i]);
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Route (user guide section 4).                                                          */
+/* ------------------------------------------------------------------------------------ */
+
+/* Softmax over all E experts of one row, in double: p_e = exp(x_e - m) / sum exp(x_i - m),
+ * m = max_i x_i.  Returns 1 and leaves p untouched for a NaN row. */
+static int row_softmax(const double* x, int64_t E, double* p) {
+    int any_nan_or_posinf = 0, all_neginf = 1;
+    for (int64_t e = 0; e < E; ++e) {
+        if (isnan(x[e]) || x[e] == INFINITY) any_nan_or_posinf = 1;
+        if (x[e] != -INFINITY) all_neginf = 0;
+    }
+    if (any_nan_or_posinf || all_neginf) return 1;
+    double m = -INFINITY;
+    for (int64_t e = 0; e < E; ++e)
+        if (x[e] > m) m = x[e];
+    double s = 0.0;
+    for (int64_t e = 0; e < E; ++e) {
+        p[e] = exp(x[e] - m); /* exp(-inf) = 0 exactly */
+        s += p[e];
+    }
+    for (int64_t e = 0; e < E; ++e) p[e] /= s;
+    return 0;
+}
+
+/* Top-k by brute force: k passes, each taking the largest not-yet-taken probability; a
+ * strictly-greater test while scanning ids upward makes the lower id win a tie. */
+static void row_topk(const double* p, int64_t E, int64_t k, unsigned char* taken, uint32_t* idx) {
+    memset(taken, 0, (size_t)E);
+    for (int64_t j = 0; j < k; ++j) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || p[e] > p[best]) best = e;
+        }
+        taken[best] = 1;
+        idx[j] = (uint32_t)best;
+    }
+}
+
+/* logits [T,E] (ldt) -> expert_indices [T,k] u32, weights [T,k] (ldt).  If weights_exact is
+ * not NULL it receives the double weights before the cast.  Returns 0, or -1 on bad args. */
+int oracle_route(const void* logits, int ldt, int64_t T, int64_t E, int64_t k, int renormalize,
+                 uint32_t* expert_indices, void* weights, double* weights_exact) {
+    if (T < 0 || E < 1 || k < 1 || k > E) return -1;
+#pragma omp parallel
+    {
+        double* x = (double*)malloc(sizeof(double) * (size_t)E);
+        double* p = (double*)malloc(sizeof(double) * (size_t)E);
+        unsigned char* taken = (unsigned char*)malloc((size_t)E);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            for (int64_t e = 0; e < E; ++e) x[e] = load_val(logits, ldt, t * E + e);
+            uint32_t* idx = expert_indices + t * k;
+            if (row_softmax(x, E, p)) {
+                for (int64_t j = 0; j < k; ++j) {
+                    idx[j] = (uint32_t)j;
+                    store_val(weights, ldt, t * k + j, NAN);
+                    if (weights_exact) weights_exact[t * k + j] = NAN;
+                }
+                continue;
+            }
+            row_topk(p, E, k, taken, idx);
+            double den = 0.0;
+            for (int64_t j = 0; j < k; ++j) den += p[idx[j]];
+            for (int64_t j = 0; j < k; ++j) {
+                double v = p[idx[j]];
+                if (renormalize) v /= den;
+                store_val(weights, ldt, t * k + j, v);
+                if (weights_exact) weights_exact[t * k + j] = v;
+            }
+        }
+        free(x);
+        free(p);
+        free(taken);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Dispatch (user guide section 5): capacity-free grouping by expert plus the stored map. */
+/* ------------------------------------------------------------------------------------ */
+
+/* counts[e] = number of (t,j) with index e; offsets = exclusive prefix sum (E+1 entries);
+ * rows of one expert are assigned in (t,j) order.  token_map[t*k+j] = assigned row, or -1
+ * for an index >= E.  dispatched[token_map[t*k+j]] = input[t], bytes copied verbatim. */
+int oracle_dispatch(const uint32_t* expert_indices, int64_t T, int64_t k, int64_t E,
+                    const void* input, int dt, int64_t H, void* dispatched,
+                    int32_t* expert_offsets, int32_t* token_map, int32_t* counts) {
+    if (T < 0 || k < 1 || E < 1 || H < 1) return -1;
+    int64_t* cnt = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    for (int64_t a = 0; a < T * k; ++a)
+        if (expert_indices[a] < (uint64_t)E) cnt[expert_indices[a]]++;
+    int64_t* cursor = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+    int64_t run = 0;
+    for (int64_t e = 0; e < E; ++e) {
+        expert_offsets[e] = (int32_t)run;
+        if (counts) counts[e] = (int32_t)cnt[e];
+        cursor[e] = run;
+        run += cnt[e];
+    }
+    expert_offsets[E] = (int32_t)run;
+    size_t row_bytes = (size_t)H * dt_size(dt);
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < k; ++j) {
+            uint32_t e = expert_indices[t * k + j];
+            if (e >= (uint64_t)E) {
+                token_map[t * k + j] = -1;
+                continue;
+            }
+            int64_t row = cursor[e]++;
+            token_map[t * k + j] = (int32_t)row;
+            if (dispatched)
+                memcpy((char*)dispatched + (size_t)row * row_bytes,
+                       (const char*)input + (size_t)t * row_bytes, row_bytes);
+        }
+    free(cnt);
+    free(cursor);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* SwiGLU experts (user guide sections 3 and 5).                                          */
+/* ------------------------------------------------------------------------------------ */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Rows x[0..n) (dtype dt, [n,H]) all go through expert e:
+ *   g_i = sum_h gate[e,i,h] x[h],  u_i = sum_h up[e,i,h] x[h]   (i < I)
+ *   h_i = dt(silu(g_i) * u_i)
+ *   y_c = dt(sum_i down[e,c,i] h_i)                              (c < H)
+ * hidden (optional, [n,I], dt) receives h.  Rows are taken in blocks so that each weight row
+ * is decoded once per block; every sum is still the plain sum over its index. */
+#define ROW_BLOCK 64
+static void expert_rows(const void* x, int64_t n, int dt, const void* gate, const void* up,
+                        const void* down, int64_t e, int64_t H, int64_t I, void* y, void* hidden) {
+    for (int64_t r0 = 0; r0 < n; r0 += ROW_BLOCK) {
+        int64_t nb = n - r0 < ROW_BLOCK ? n - r0 : ROW_BLOCK;
+        double* xb = (double*)malloc(sizeof(double) * (size_t)(nb * H));
+        double* hb = (double*)malloc(sizeof(double) * (size_t)(nb * I));
+        for (int64_t r = 0; r < nb; ++r)
+            for (int64_t c = 0; c < H; ++c) xb[r * H + c] = load_val(x, dt, (r0 + r) * H + c);
+#pragma omp parallel
+        {
+            double* wg = (double*)malloc(sizeof(double) * (size_t)H);
+            double* wu = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < I; ++i) {
+                for (int64_t c = 0; c < H; ++c) {
+                    wg[c] = load_val(gate, dt, (e * I + i) * H + c);
+                    wu[c] = load_val(up, dt, (e * I + i) * H + c);
+                }
+                for (int64_t r = 0; r < nb; ++r) {
+                    const double* xr = xb + r * H;
+                    double g = 0.0, u = 0.0;
+                    for (int64_t c = 0; c < H; ++c) {
+                        g += wg[c] * xr[c];
+                        u += wu[c] * xr[c];
+                    }
+                    hb[r * I + i] = round_to(silu(g) * u, dt);
+                }
+            }
+            free(wg);
+            free(wu);
+        }
+        if (hidden)
+            for (int64_t r = 0; r < nb; ++r)
+                for (int64_t i = 0; i < I; ++i) store_val(hidden, dt, (r0 + r) * I + i, hb[r * I + i]);
+#pragma omp parallel
+        {
+            double* wd = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(static)
+            for (int64_t c = 0; c < H; ++c) {
+                for (int64_t i = 0; i < I; ++i) wd[i] = load_val(down, dt, (e * H + c) * I + i);
+                for (int64_t r = 0; r < nb; ++r) {
+                    const double* hr = hb + r * I;
+                    double s = 0.0;
+                    for (int64_t i = 0; i < I; ++i) s += wd[i] * hr[i];
+                    store_val(y, dt, (r0 + r) * H + c, s);
+                }
+            }
+            free(wd);
+        }
+        free(xb);
+        free(hb);
+    }
+}
+
+/* Arbitrary rows through arbitrary experts: row r of x goes through expert expert_of_row[r].
+ * Used to check sampled rows of large workloads one by one. */
+int oracle_expert_rows(const void* x, int64_t n, int dt, const void* gate, const void* up,
+                       const void* down, int64_t E, int64_t H, int64_t I,
+                       const int32_t* expert_of_row, void* y, void* hidden) {
+    size_t es = dt_size(dt);
+    for (int64_t r = 0; r < n; ++r)
+        if (expert_of_row[r] < 0 || expert_of_row[r] >= E) return -1;
+    /* consecutive rows of one expert go through it together */
+    for (int64_t r = 0; r < n;) {
+        int64_t r1 = r + 1;
+        while (r1 < n && expert_of_row[r1] == expert_of_row[r]) ++r1;
+        expert_rows((const char*)x + (size_t)r * H * es, r1 - r, dt, gate, up, down, expert_of_row[r], H, I,
+                    (char*)y + (size_t)r * H * es, hidden ? (char*)hidden + (size_t)r * I * es : NULL);
+        r = r1;
+    }
+    return 0;
+}
+
+/* Grouped form: rows [offsets[e], offsets[e+1]) of dispatched go through expert e. */
+int oracle_experts_forward(const void* dispatched, const int32_t* expert_offsets, int64_t E, int dt,
+                           const void* gate, const void* up, const void* down, int64_t H, int64_t I,
+                           void* expert_output, void* hidden) {
+    size_t es = dt_size(dt);
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t a = expert_offsets[e], b = expert_offsets[e + 1];
+        if (b < a) return -1;
+        if (b == a) continue;
+        expert_rows((const char*)dispatched + (size_t)a * H * es, b - a, dt, gate, up, down, e, H, I,
+                    (char*)expert_output + (size_t)a * H * es,
+                    hidden ? (char*)hidden + (size_t)a * I * es : NULL);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Combine (user guide sections 3 and 6): restore token order through the map and sum the */
+/* k expert outputs weighted by the routing weights, j ascending, in double.              */
+/* ------------------------------------------------------------------------------------ */
+
+int oracle_combine(const void* expert_output, int dt, const int32_t* token_map, const void* weights,
+                   int wdt, int64_t T, int64_t k, int64_t H, void* output) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        int bad = 0;
+        for (int64_t j = 0; j < k; ++j)
+            if (token_map[t * k + j] < 0) bad = 1;
+        for (int64_t c = 0; c < H; ++c) {
+            double s = 0.0;
+            if (bad) {
+                s = NAN;
+            } else {
+                for (int64_t j = 0; j < k; ++j) {
+                    double w = load_val(weights, wdt, t * k + j);
+                    s += w * load_val(expert_output, dt, (int64_t)token_map[t * k + j] * H + c);
+                }
+            }
+            store_val(output, dt, t * H + c, s);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Full local forward (user guide sections 3 and 6): route -> dispatch -> experts ->      */
+/* combine.  gate == NULL means identity experts (expert output = dispatched rows).       */
+/* ------------------------------------------------------------------------------------ */
+
+int oracle_forward(const void* input, int dt, const void* logits, int ldt, int64_t T, int64_t E,
+                   int64_t k, int renormalize, const void* gate, const void* up, const void* down,
+                   int64_t H, int64_t I, void* output) {
+    if (T < 0 || E < 1 || k < 1 || k > E) return -1;
+    if (T == 0) return 0;
+    size_t es = dt_size(dt);
+    uint32_t* idx = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(T * k));
+    void* w = malloc(dt_size(ldt) * (size_t)(T * k));
+    int32_t* offs = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t* map = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
+    void* disp = malloc(es * (size_t)(T * k * H));
+    void* y = gate ? malloc(es * (size_t)(T * k * H)) : disp;
+    int rc = oracle_route(logits, ldt, T, E, k, renormalize, idx, w, NULL);
+    if (!rc) rc = oracle_dispatch(idx, T, k, E, input, dt, H, disp, offs, map, NULL);
+    if (!rc && gate) rc = oracle_experts_forward(disp, offs, E, dt, gate, up, down, H, I, y, NULL);
+    if (!rc) rc = oracle_combine(y, dt, map, w, ldt, T, k, H, output);
+    if (gate) free(y);
+    free(disp);
+    free(map);
+    free(offs);
+    free(w);
+    free(idx);
+    return rc;
+}

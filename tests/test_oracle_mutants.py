@@ -1,0 +1,46 @@
+"""Each plausible mistake planted in a copy of the oracle must fail at least one pin.
+
+The copies are built on the CPU from ``oracle/oracle.c`` with one textual change each and
+run against ``test_oracle_pins.py`` in a subprocess; the real oracle is never modified."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "tie_to_higher_id": ("if (best < 0 || p[e] > p[best]) best = e;", "if (best < 0 || p[e] >= p[best]) best = e;"),
+    "softmax_unnormalised": ("for (int64_t e = 0; e < E; ++e) p[e] /= s;", "(void)s;"),
+    "renorm_wrong_terms": ("for (int64_t j = 0; j < k; ++j) den += p[idx[j]];", "for (int64_t j = 0; j < k; ++j) den += p[j];"),
+    # (dropping the explicit +inf / all -inf test is not a mistake: the max-subtracted
+    # softmax of such rows is NaN everywhere anyway, so that copy is equivalent)
+    "nan_row_uniform": ("store_val(weights, ldt, t * k + j, NAN);", "store_val(weights, ldt, t * k + j, 1.0 / (double)E);"),
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "gate_up_swapped": ("hb[r * I + i] = round_to(silu(g) * u, dt);", "hb[r * I + i] = round_to(silu(u) * g, dt);"),
+    "down_transposed": ("wd[i] = load_val(down, dt, (e * H + c) * I + i);", "wd[i] = load_val(down, dt, (e * I + i) * H + c);"),
+    "combine_one_weight": ("double w = load_val(weights, wdt, t * k + j);", "double w = load_val(weights, wdt, t * k);"),
+    "combine_drops_last": ("for (int64_t j = 0; j < k; ++j) {\n                    double w", "for (int64_t j = 0; j + 1 < k; ++j) {\n                    double w"),
+    "dispatch_skips_first": ("for (int64_t a = 0; a < T * k; ++a)\n        if (expert_indices[a]", "for (int64_t a = 1; a < T * k; ++a)\n        if (expert_indices[a]"),
+    "rounding_truncates": ("double r = nearbyint(x / q) * q;", "double r = trunc(x / q) * q;"),
+    "hidden_not_rounded": ("hb[r * I + i] = round_to(silu(g) * u, dt);", "hb[r * I + i] = silu(g) * u;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_fails_a_pin(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    mut = tmp_path / "oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-w", "-o", str(lib), str(mut), "-lm"],
+                   check=True)
+    env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="4")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
