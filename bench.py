@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Throughput of the local MoE forward (route -> dispatch -> SwiGLU experts -> combine) on one
+MI355X, through the C ABI of librudnn_moe.so.
+
+One step = one ``rudnn_moe_forward`` over one batch of the Mixtral-shaped layer (T=4096 tokens,
+H=4096, I=14336, E=8, top_k=2, renormalised, bf16), all inputs resident in HBM.  Prints one
+JSON line with tokens/s, the roofline of the dominant kernel (the gate/up expert GEMM, timed
+with HIP events on its launch stream during the timed steps), a per-kernel breakdown, the HBM
+rates of route / dispatch / combine on the routing+dispatch workload (T=65536, E=128, k=8,
+H=2048, bf16, identity experts), and the CPU oracle timed on a bounded sample of the same layer.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s (1 GPU); expert-GEMM MFMA %; route/dispatch/combine GB/s"
+HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense; fp32 = vector FMA peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["mixture_experts_layer_23_amd/csrc/experts.hip", "mixture_experts_layer_23_amd/csrc/device.hpp",
+                  "mixture_experts_layer_23_amd/csrc/internal.hpp"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """HIP events through the runtime torch already loaded (same soname as the library's)."""
+
+    def __init__(self):
+        self.L = ctypes.CDLL("libamdhip64.so.7")
+        self.L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.L.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.L.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        self.L.hipEventSynchronize(b)
+        v = ctypes.c_float()
+        assert self.L.hipEventElapsedTime(ctypes.byref(v), a, b) == 0
+        return float(v.value)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed PMC summary, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = d.get(f"{kernel}@{workload}")
+    if not ent or ent.get("source_sha256") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8,
+                    help="tokens of the layer the CPU oracle runs for the baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm-stages", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (scale for FETCH_SIZE/WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this library is a single-GPU local MoE forward with no "
+              "multi-GPU path, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_23_amd import moe
+    from mixture_experts_layer_23_amd.inputs import WORKLOADS, make_experts, make_logits, make_tokens
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    moe.lib()
+
+    # ---------------- the Mixtral-shaped layer ----------------
+    w = WORKLOADS["mixtral"]
+    renorm = w.renormalize[0]
+    log("generating", w.name)
+    logits_cpu, _ = make_logits(w)
+    logits = logits_cpu.to(dev)
+    x = make_tokens(w, dev)
+    gate, up, down = make_experts(w, dev)
+    ex = moe.SwiGluExperts(gate, up, down)
+    out = torch.empty_like(x)
+    ws = torch.empty(moe.forward_workspace_size(ex, w.T, w.top_k, logits.dtype), dtype=torch.uint8, device=dev)
+
+    def step():
+        ex.forward(x, logits, w.top_k, renorm, out=out, workspace=ws)
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps back to back; HIP events around every gate/up GEMM launch
+    K = args.steps
+    gu_ev = [(hip.event(), hip.event()) for _ in range(K)]
+    t_start, t_stop = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hip.record(t_start, stream)
+    for i in range(K):
+        moe.time_next_launch("experts_gate_up", *gu_ev[i])
+        step()
+    hip.record(t_stop, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = hip.ms(t_start, t_stop)
+    ms_per_step = ms_total / K
+    tokens_per_s = w.T / (ms_per_step / 1e3)
+    gu_ms = float(np.mean([hip.ms(a, b) for a, b in gu_ev]))
+    log(f"{K} steps: {ms_per_step:.3f} ms/step (host wall {wall / K * 1e3:.3f} ms), gate/up {gu_ms:.3f} ms")
+
+    T, H, I, E, k = w.T, w.H, w.I, w.E, w.top_k
+    s = 2
+    gu_flops = 4.0 * T * k * H * I
+    dn_flops = 2.0 * T * k * H * I
+    gu_tflops = gu_flops / (gu_ms / 1e3) / 1e12
+
+    # per-kernel breakdown (separate pass, every kernel timed)
+    stage_ev = {kn: [(hip.event(), hip.event()) for _ in range(max(3, K // 4))] for kn in moe.KERNELS}
+    for i in range(max(3, K // 4)):
+        for kn in moe.KERNELS:
+            moe.time_next_launch(kn, *stage_ev[kn][i])
+        step()
+    torch.cuda.synchronize()
+    stage_ms = {kn: float(np.mean([hip.ms(a, b) for a, b in v])) for kn, v in stage_ev.items()}
+    dispatch_bytes = T * k * 4 * 2 + T * H * s + T * k * H * s + T * k * 4 + 4 * (E + 1)
+    stages = {
+        "route": {"us": stage_ms["route"] * 1e3, "bytes": T * E * s + T * k * (4 + s)},
+        "dispatch": {"us": sum(stage_ms[f"dispatch_{p}"] for p in ("count", "scan", "rank", "copy")) * 1e3,
+                     "bytes": dispatch_bytes},
+        "experts_gate_up": {"us": stage_ms["experts_gate_up"] * 1e3, "flops": gu_flops},
+        "experts_down": {"us": stage_ms["experts_down"] * 1e3, "flops": dn_flops},
+        "experts_plan": {"us": stage_ms["experts_plan"] * 1e3},
+        "combine": {"us": stage_ms["combine"] * 1e3, "bytes": T * k * H * s + T * k * (s + 4) + T * H * s},
+    }
+    for v in stages.values():
+        if "bytes" in v:
+            v["GBps"] = v["bytes"] / (v["us"] / 1e6) / 1e9
+            v["hbm_frac"] = v["GBps"] / HBM_PEAK_GBS
+        if "flops" in v:
+            v["TFLOPps"] = v["flops"] / (v["us"] / 1e6) / 1e12
+            v["mfma_frac"] = v["TFLOPps"] / MFMA_PEAK_TFLOPS[w.dtype]
+    experts_us = stages["experts_gate_up"]["us"] + stages["experts_down"]["us"] + stages["experts_plan"]["us"]
+    stages["experts_total"] = {"us": experts_us, "TFLOPps": (gu_flops + dn_flops) / (experts_us / 1e6) / 1e12}
+    stages["experts_total"]["mfma_frac"] = stages["experts_total"]["TFLOPps"] / MFMA_PEAK_TFLOPS[w.dtype]
+
+    # ---------------- CPU oracle on a bounded sample of the same layer ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        n = args.cpu_sample_tokens
+        log("cpu baseline:", n, "tokens through the oracle")
+        g_c, u_c, d_c = gate.cpu(), up.cpu(), down.cpu()
+        xs, ls = x[:n].cpu(), logits_cpu[:n]
+        t0 = time.perf_counter()
+        oracle.forward(xs, ls, k, renorm, g_c, u_c, d_c)
+        dt = time.perf_counter() - t0
+        cpu = {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"first {n} of the {T} tokens of the Mixtral-shaped layer, whole forward "
+                         f"(route, dispatch, SwiGLU experts, combine) in the fp64 oracle; {dt:.1f} s"}
+        del g_c, u_c, d_c
+
+    # ---------------- HBM-bound stages on the routing+dispatch workload ----------------
+    hbm = None
+    if not args.no_hbm_stages:
+        del ws, out
+        torch.cuda.empty_cache()
+        w2 = WORKLOADS["route_dispatch"]
+        log("generating", w2.name)
+        lg2_cpu, _ = make_logits(w2)
+        lg2 = lg2_cpu.to(dev)
+        x2 = make_tokens(w2, dev)
+        T2, E2, k2, H2 = w2.T, w2.E, w2.top_k, w2.H
+        idx2 = torch.empty(T2, k2, dtype=torch.int32, device=dev)
+        wt2 = torch.empty(T2, k2, dtype=lg2.dtype, device=dev)
+        d2 = moe.Dispatched(torch.empty(T2 * k2, H2, dtype=x2.dtype, device=dev),
+                            torch.empty(E2 + 1, dtype=torch.int32, device=dev),
+                            torch.empty(T2, k2, dtype=torch.int32, device=dev))
+        dws = torch.empty(max(moe.lib().rudnn_moe_dispatch_workspace_size(T2, k2, E2), 1), dtype=torch.uint8,
+                          device=dev)
+        o2 = torch.empty_like(x2)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # 2x the 256 MB Infinity Cache
+        reps = 5
+        ev = {n_: [(hip.event(), hip.event()) for _ in range(reps)] for n_ in ("route", "dispatch", "combine")}
+        for i in range(reps + 1):
+            rec = i > 0
+            for name, fn in (("route", lambda: moe.lib().rudnn_moe_route(
+                                 lg2.data_ptr(), 2, T2, E2, moe.RoutingOptions(k2, 1), idx2.data_ptr(), wt2.data_ptr(),
+                                 stream)),
+                             ("dispatch", lambda: moe.dispatch(idx2, x2, E2, out=d2, workspace=dws)),
+                             ("combine", lambda: moe.combine(d2.dispatched, d2.token_map, wt2, out=o2))):
+                flush.fill_(i & 0xff)
+                if rec:
+                    hip.record(ev[name][i - 1][0], stream)
+                rc = fn()
+                if isinstance(rc, int):
+                    assert rc == 0, rc
+                if rec:
+                    hip.record(ev[name][i - 1][1], stream)
+        torch.cuda.synchronize()
+        pk = T2 * k2
+        hbm_bytes = {"route": T2 * E2 * s + pk * (4 + s),
+                     "dispatch": pk * 4 * 2 + T2 * H2 * s + pk * H2 * s + pk * 4 + 4 * (E2 + 1),
+                     "combine": pk * H2 * s + pk * (s + 4) + T2 * H2 * s}
+        hbm = {"workload": "routing+dispatch T=65536 E=128 k=8 H=2048 bf16, identity experts, cache flushed"}
+        for name in ("route", "dispatch", "combine"):
+            us = float(np.median([hip.ms(a, b) for a, b in ev[name]])) * 1e3
+            gbs = hbm_bytes[name] / (us / 1e6) / 1e9
+            hbm[name] = {"us": us, "bytes": hbm_bytes[name], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+
+    traffic = traffic_for("experts_gate_up", "mixtral")
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; random-init expert weights N(0,1)/sqrt(fan_in))",
+        "config": {"workload": "Mixtral-shaped MoE layer", "T": T, "H": H, "I": I, "E": E, "top_k": k,
+                   "renormalize": renorm, "token_dtype": w.dtype, "logits_dtype": w.logits_dtype},
+        "roofline": {"bound": "mfma", "kernel": "experts_gate_up", "achieved": gu_tflops,
+                     "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                     "frac": gu_tflops / MFMA_PEAK_TFLOPS[w.dtype], "traffic": traffic,
+                     "algorithmic_per_launch": gu_flops, "avg_launch_ms": gu_ms},
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "hbm_stages": hbm,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * rudnn_moe.h -- local mixture-of-experts forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the local MoE sequence of the ruDNN user guide (docs.rs, ruDNN 0.1.72):
+ *   section 3 "MoE workflow":   logits -> softmax/top-k -> compact dispatch -> SwiGLU experts
+ *                                -> weighted combine, each step also callable on its own;
+ *   section 4 "Routing contract", section 5 "Expert weights and dispatch",
+ *   section 6 "Calling MoE"     (the staged call forms, shapes and error rules).
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers (memory of the device the stream belongs to),
+ *     row-major and contiguous.  The caller owns every buffer, workspace included; the
+ *     library never allocates, frees or keeps a pointer after returning.
+ *   - Calls only enqueue work on `stream` (NULL = the null stream).  Nothing is synchronised
+ *     and nothing is copied to the host: results are valid once the stream reaches them,
+ *     like a readback that waits for the device (section 6).
+ *   - Inputs are read-only.  Outputs must not overlap any input or each other
+ *     (RUDNN_MOE_ERR_ARGUMENT otherwise).
+ *   - Every argument is validated on the host before anything is enqueued.  A status other
+ *     than RUDNN_MOE_OK means nothing was enqueued and no output was touched, except for
+ *     RUDNN_MOE_ERR_RUNTIME (the HIP runtime refused a launch after earlier launches of the
+ *     same call were enqueued).
+ *   - T = 0 (no tokens) is a successful no-op.
+ *   - No global state: calls are reentrant and may run concurrently on different streams
+ *     with different buffers.  (The optional timing hook at the end is per host thread.)
+ */
+#ifndef RUDNN_MOE_H
+#define RUDNN_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Floating-point storage types (section 4: unquantised F32, F16 or BF16). */
+typedef enum {
+    RUDNN_MOE_F32 = 0,
+    RUDNN_MOE_F16 = 1,
+    RUDNN_MOE_BF16 = 2
+} rudnn_moe_dtype;
+
+/* Result of every entry point; the counterpart of the guide's MoeError (sections 3 and 6). */
+typedef enum {
+    RUDNN_MOE_OK = 0,
+    RUDNN_MOE_ERR_SHAPE = 1,       /* a size < 1 where one is required; E/H/I disagree */
+    RUDNN_MOE_ERR_DTYPE = 2,       /* not F32/F16/BF16; tokens and expert weights differ */
+    RUDNN_MOE_ERR_ARGUMENT = 3,    /* top_k outside [1, E]; NULL pointer; overlapping buffers */
+    RUDNN_MOE_ERR_DEVICE = 4,      /* a pointer is not device memory of the stream's device */
+    RUDNN_MOE_ERR_UNSUPPORTED = 5, /* beyond the kernels' limits: E > 1024, top_k > 64,
+                                      T*top_k >= 2^31, rows*max(H,I) >= 2^31 elements */
+    RUDNN_MOE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the size query returns */
+    RUDNN_MOE_ERR_RUNTIME = 7      /* HIP reported an error for a launch */
+} rudnn_moe_status;
+
+/* RoutingOptions of section 4: 1 <= top_k <= E; renormalize != 0 rescales the k selected
+ * probabilities of a row to sum to one before the cast to the logits dtype. */
+typedef struct {
+    int64_t top_k;
+    int32_t renormalize;
+} rudnn_moe_routing_options;
+
+/* Borrowed view of the expert weights (SwiGluExperts::new of section 3; shapes and dtype
+ * rules of section 5): bias-free SwiGLU experts
+ *     y = down_e . ( silu(gate_e . x) * (up_e . x) ),   silu(z) = z / (1 + exp(-z)),
+ * gate and up [E, I, H], down [E, H, I] (rows are output features; the contraction axis is
+ * contiguous).  All three tensors and the tokens share one float dtype.  The view may be
+ * reused for any number of batches; the weights must stay alive until the stream has
+ * consumed every call that used them. */
+typedef struct {
+    const void* gate;
+    const void* up;
+    const void* down;
+    int64_t num_experts;   /* E */
+    int64_t hidden;        /* H */
+    int64_t intermediate;  /* I */
+    rudnn_moe_dtype dtype;
+} rudnn_moe_experts;
+
+/*
+ * route -- section 4 "Routing contract" (RoutingPlan, expert_indices(), weights()).
+ * For each row t of logits [T, E]: p = softmax over all E experts, computed in FP32; the k
+ * largest p are selected, equal p favouring the lower expert id, and listed by descending
+ * p (equal p: ascending id).  weights[t, j] = p of the j-th selected expert, divided by the
+ * sum of the k selected p when opt.renormalize, then cast (round to nearest even) to the
+ * logits dtype.  A row holding a NaN, a +inf, or nothing but -inf gets weights NaN and
+ * indices 0..k-1.
+ *   logits          [T, E]  logits_dtype (F32/F16/BF16)
+ *   expert_indices  [T, k]  uint32, written
+ *   weights         [T, k]  logits_dtype, written
+ * Errors: SHAPE (T < 0, E < 1), ARGUMENT (top_k outside [1, E], NULL, overlap),
+ * DTYPE, UNSUPPORTED (E > 1024 or top_k > 64), DEVICE, RUNTIME.
+ */
+rudnn_moe_status rudnn_moe_route(const void* logits, rudnn_moe_dtype logits_dtype, int64_t T, int64_t E,
+                                 rudnn_moe_routing_options opt, uint32_t* expert_indices, void* weights,
+                                 hipStream_t stream);
+
+/* Bytes of device workspace rudnn_moe_dispatch needs for T tokens, top_k, E experts. */
+size_t rudnn_moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E);
+
+/*
+ * dispatch -- section 5 "Expert weights and dispatch" (RoutingPlan::dispatch).
+ * Capacity-free grouping of the T*k (token, slot) pairs by expert; no token is dropped.
+ *   expert_indices  [T, k] uint32 (as written by rudnn_moe_route)
+ *   input           [T, H] dtype
+ *   dispatched      [T*k, H] dtype, written: rows [expert_offsets[e], expert_offsets[e+1])
+ *                   hold the tokens routed to expert e
+ *   expert_offsets  [E+1] int32, written: exclusive prefix sum of the per-expert counts;
+ *                   expert_offsets[E] = number of pairs with an index < E (T*k normally)
+ *   token_map       [T, k] int32, written: the dispatched row holding copy j of token t
+ *                   (the stored map that restores token order); -1 for an index >= E
+ * Inside one expert this implementation orders rows by (t, j); the guide leaves that order
+ * open, so callers must rely only on token_map.  Indices >= E are a caller error that is
+ * contained: such a pair is not copied and combine yields a NaN row for its token.
+ * workspace: at least rudnn_moe_dispatch_workspace_size(T, top_k, E) bytes, 256-B aligned.
+ * Errors: SHAPE, ARGUMENT, DTYPE, UNSUPPORTED (E > 1024, T*k >= 2^31), WORKSPACE, DEVICE,
+ * RUNTIME.
+ */
+rudnn_moe_status rudnn_moe_dispatch(const uint32_t* expert_indices, int64_t T, int64_t top_k, int64_t E,
+                                    const void* input, rudnn_moe_dtype dtype, int64_t H, void* dispatched,
+                                    int32_t* expert_offsets, int32_t* token_map, void* workspace,
+                                    size_t workspace_size, hipStream_t stream);
+
+/* Bytes of device workspace rudnn_moe_experts_forward needs for `rows` dispatched rows
+ * (the hidden activation [rows, I] plus the tile schedule). */
+size_t rudnn_moe_experts_workspace_size(const rudnn_moe_experts* ex, int64_t rows);
+
+/*
+ * experts_forward -- sections 3 and 5 (SwiGluExperts::forward_dispatched).
+ * For every expert e and every row r in [expert_offsets[e], expert_offsets[e+1]):
+ *   h = dtype( silu(gate_e . x_r) * (up_e . x_r) )    (FP32 accumulation, one rounding)
+ *   expert_output[r] = dtype( down_e . h )             (FP32 accumulation, one rounding)
+ *   dispatched      [rows, H] dtype;   expert_offsets [E+1] int32 (device, as written by
+ *                   rudnn_moe_dispatch; never read on the host); rows = T*k
+ *   expert_output   [rows, H] dtype, written for rows < expert_offsets[E]
+ * BF16/F16 run on the matrix cores (MFMA) with FP32 accumulators; F32 runs in FP32 FMA.
+ * workspace: at least rudnn_moe_experts_workspace_size(ex, rows) bytes, 256-B aligned.
+ * Errors: SHAPE, DTYPE, ARGUMENT, UNSUPPORTED, WORKSPACE, DEVICE, RUNTIME.
+ */
+rudnn_moe_status rudnn_moe_experts_forward(const rudnn_moe_experts* ex, const void* dispatched,
+                                           const int32_t* expert_offsets, int64_t rows, void* expert_output,
+                                           void* workspace, size_t workspace_size, hipStream_t stream);
+
+/*
+ * combine -- sections 3 and 6 (DispatchedTokens::combine).
+ *   output[t] = dtype( sum_{j=0..k-1} weights[t, j] * expert_output[token_map[t, j]] )
+ * accumulated in FP32 with j ascending.  A token with a map entry outside [0, T*k) (dispatch
+ * writes -1 for an expert id >= E) gets a NaN row; no row outside expert_output is read.
+ *   expert_output [T*k, H] dtype;  token_map [T, k] int32;  weights [T, k] weights_dtype
+ *   output        [T, H] dtype, written
+ * Errors: SHAPE, DTYPE, ARGUMENT, UNSUPPORTED (top_k > 64, T*k >= 2^31), DEVICE, RUNTIME.
+ */
+rudnn_moe_status rudnn_moe_combine(const void* expert_output, rudnn_moe_dtype dtype, const int32_t* token_map,
+                                   const void* weights, rudnn_moe_dtype weights_dtype, int64_t T, int64_t top_k,
+                                   int64_t H, void* output, hipStream_t stream);
+
+/* Bytes of device workspace rudnn_moe_forward needs. */
+size_t rudnn_moe_forward_workspace_size(const rudnn_moe_experts* ex, int64_t T, int64_t top_k,
+                                        rudnn_moe_dtype logits_dtype);
+
+/*
+ * forward -- section 6 (SwiGluExperts::forward(input, logits, options)): the whole local
+ * sequence route -> dispatch -> experts -> combine on one stream, bit-identical to calling
+ * the four stages in turn.  The gate projection producing the logits is the caller's
+ * (section 5).
+ *   input [T, H] ex->dtype;  logits [T, E] logits_dtype;  output [T, H] ex->dtype, written
+ * workspace: at least rudnn_moe_forward_workspace_size(ex, T, opt.top_k, logits_dtype) bytes.
+ */
+rudnn_moe_status rudnn_moe_forward(const rudnn_moe_experts* ex, const void* input, const void* logits,
+                                   rudnn_moe_dtype logits_dtype, int64_t T, rudnn_moe_routing_options opt,
+                                   void* output, void* workspace, size_t workspace_size, hipStream_t stream);
+
+/* Static, human-readable name of a status. */
+const char* rudnn_moe_status_string(rudnn_moe_status s);
+
+/*
+ * Optional timing hook (measurement only; not part of the method).  The library's kernels,
+ * as launched by the entry points above:
+ */
+typedef enum {
+    RUDNN_MOE_KERNEL_ROUTE = 0,
+    RUDNN_MOE_KERNEL_DISPATCH_COUNT = 1,
+    RUDNN_MOE_KERNEL_DISPATCH_SCAN = 2,
+    RUDNN_MOE_KERNEL_DISPATCH_RANK = 3,
+    RUDNN_MOE_KERNEL_DISPATCH_COPY = 4,
+    RUDNN_MOE_KERNEL_EXPERTS_PLAN = 5,
+    RUDNN_MOE_KERNEL_EXPERTS_GATE_UP = 6,
+    RUDNN_MOE_KERNEL_EXPERTS_DOWN = 7,
+    RUDNN_MOE_KERNEL_COMBINE = 8,
+    RUDNN_MOE_KERNEL_COUNT = 9
+} rudnn_moe_kernel;
+
+/* For the calling host thread: record `before` on the launch stream immediately before the
+ * next launch of `kernel` and `after` immediately after it, then forget the pair (one-shot).
+ * Passing NULL events clears a pending pair.  Events are created and destroyed by the
+ * caller.  Errors: ARGUMENT (unknown kernel). */
+rudnn_moe_status rudnn_moe_time_next_launch(rudnn_moe_kernel kernel, hipEvent_t before, hipEvent_t after);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RUDNN_MOE_H */

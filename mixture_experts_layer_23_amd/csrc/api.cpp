@@ -1,0 +1,308 @@
+// api.cpp -- the C ABI of rudnn_moe.h: host-side validation, workspace layout, launches.
+//
+// Every check runs on the host before the first launch (the counterpart of the guide's
+// Result<_, MoeError>, ruDNN user guide sections 3 and 6); pure argument checks come first and
+// make no HIP call, so they can be exercised without a GPU.
+#include <mutex>
+
+#include "internal.hpp"
+
+using namespace rudnn;
+
+namespace {
+
+thread_local hipEvent_t g_timing[RUDNN_MOE_KERNEL_COUNT][2] = {};
+
+bool valid_dtype(rudnn_moe_dtype d) { return d == RUDNN_MOE_F32 || d == RUDNN_MOE_F16 || d == RUDNN_MOE_BF16; }
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+
+bool overlap(Range a, Range b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Each output against every input and every other output.
+bool any_overlap(std::initializer_list<Range> outs, std::initializer_list<Range> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Range& i : ins)
+            if (overlap(*o, i)) return true;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(*o, *o2)) return true;
+    }
+    return false;
+}
+
+rudnn_moe_status check_device(hipStream_t s, std::initializer_list<const void*> ptrs) {
+    int dev = -1;
+    if (s) {
+        if (hipStreamGetDevice(s, &dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return RUDNN_MOE_ERR_DEVICE;
+        }
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return RUDNN_MOE_ERR_DEVICE;
+    }
+    for (const void* p : ptrs) {
+        hipPointerAttribute_t a;
+        if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+            (void)hipGetLastError();
+            return RUDNN_MOE_ERR_DEVICE;
+        }
+        if ((a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) || a.device != dev)
+            return RUDNN_MOE_ERR_DEVICE;
+    }
+    return RUDNN_MOE_OK;
+}
+
+rudnn_moe_status runtime(hipError_t e) { return e == hipSuccess ? RUDNN_MOE_OK : RUDNN_MOE_ERR_RUNTIME; }
+
+constexpr int64_t INT32_LIMIT = (int64_t)1 << 31;
+
+rudnn_moe_status check_route_args(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E,
+                                  rudnn_moe_routing_options opt, const uint32_t* idx, const void* w) {
+    if (T < 0 || E < 1) return RUDNN_MOE_ERR_SHAPE;
+    if (opt.top_k < 1 || opt.top_k > E) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!valid_dtype(ldt)) return RUDNN_MOE_ERR_DTYPE;
+    if (E > MAX_EXPERTS || opt.top_k > MAX_TOP_K || T * opt.top_k >= INT32_LIMIT || T * E >= ((int64_t)1 << 40))
+        return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (T == 0) return RUDNN_MOE_OK;
+    if (!logits || !idx || !w) return RUDNN_MOE_ERR_ARGUMENT;
+    const size_t ls = dtype_size(ldt), pk = (size_t)(T * opt.top_k);
+    if (any_overlap({{idx, pk * 4}, {w, pk * ls}}, {{logits, (size_t)(T * E) * ls}})) return RUDNN_MOE_ERR_ARGUMENT;
+    return RUDNN_MOE_OK;
+}
+
+rudnn_moe_status check_experts_view(const rudnn_moe_experts* ex) {
+    if (!ex) return RUDNN_MOE_ERR_ARGUMENT;
+    if (ex->num_experts < 1 || ex->hidden < 1 || ex->intermediate < 1) return RUDNN_MOE_ERR_SHAPE;
+    if (!valid_dtype(ex->dtype)) return RUDNN_MOE_ERR_DTYPE;
+    if (!ex->gate || !ex->up || !ex->down) return RUDNN_MOE_ERR_ARGUMENT;
+    if (ex->num_experts > MAX_EXPERTS) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (ex->dtype != RUDNN_MOE_F32) {
+        // 16-byte vector loads of the contraction axis: H and I multiples of 8, aligned bases
+        if (ex->hidden % 8 || ex->intermediate % 8) return RUDNN_MOE_ERR_UNSUPPORTED;
+        if ((uintptr_t)ex->gate % 16 || (uintptr_t)ex->up % 16 || (uintptr_t)ex->down % 16)
+            return RUDNN_MOE_ERR_UNSUPPORTED;
+    }
+    const int64_t wsz = ex->num_experts * ex->hidden * ex->intermediate;
+    if (ex->hidden >= INT32_LIMIT || ex->intermediate >= INT32_LIMIT || wsz >= ((int64_t)1 << 40))
+        return RUDNN_MOE_ERR_UNSUPPORTED;
+    return RUDNN_MOE_OK;
+}
+
+rudnn_moe_status check_experts_rows(const rudnn_moe_experts* ex, int64_t rows) {
+    if (rows < 0) return RUDNN_MOE_ERR_SHAPE;
+    const int64_t wide = ex->hidden > ex->intermediate ? ex->hidden : ex->intermediate;
+    if (rows >= INT32_LIMIT || rows * wide >= INT32_LIMIT * 64) return RUDNN_MOE_ERR_UNSUPPORTED;
+    return RUDNN_MOE_OK;
+}
+
+}  // namespace
+
+namespace rudnn {
+
+void timing_before(rudnn_moe_kernel k, hipStream_t s) {
+    if (g_timing[k][0]) hipEventRecord(g_timing[k][0], s);
+}
+
+void timing_after(rudnn_moe_kernel k, hipStream_t s) {
+    if (g_timing[k][1]) hipEventRecord(g_timing[k][1], s);
+    g_timing[k][0] = g_timing[k][1] = nullptr;
+}
+
+}  // namespace rudnn
+
+extern "C" {
+
+const char* rudnn_moe_status_string(rudnn_moe_status s) {
+    switch (s) {
+    case RUDNN_MOE_OK: return "ok";
+    case RUDNN_MOE_ERR_SHAPE: return "invalid shape";
+    case RUDNN_MOE_ERR_DTYPE: return "invalid or mismatched dtype";
+    case RUDNN_MOE_ERR_ARGUMENT: return "invalid argument (top_k, null pointer or overlapping buffers)";
+    case RUDNN_MOE_ERR_DEVICE: return "pointer is not device memory of the stream's device";
+    case RUDNN_MOE_ERR_UNSUPPORTED: return "outside the kernels' supported limits";
+    case RUDNN_MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case RUDNN_MOE_ERR_RUNTIME: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+rudnn_moe_status rudnn_moe_time_next_launch(rudnn_moe_kernel kernel, hipEvent_t before, hipEvent_t after) {
+    if ((int)kernel < 0 || (int)kernel >= RUDNN_MOE_KERNEL_COUNT) return RUDNN_MOE_ERR_ARGUMENT;
+    g_timing[kernel][0] = before;
+    g_timing[kernel][1] = after;
+    return RUDNN_MOE_OK;
+}
+
+rudnn_moe_status rudnn_moe_route(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E,
+                                 rudnn_moe_routing_options opt, uint32_t* idx, void* w, hipStream_t stream) {
+    rudnn_moe_status st = check_route_args(logits, ldt, T, E, opt, idx, w);
+    if (st != RUDNN_MOE_OK || T == 0) return st;
+    if ((st = check_device(stream, {logits, idx, w})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_route(logits, ldt, T, E, opt.top_k, opt.renormalize != 0, idx, w, stream));
+}
+
+size_t rudnn_moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E) {
+    if (T < 0 || top_k < 1 || E < 1) return 0;
+    return align_up(sizeof(int32_t) * (size_t)(dispatch_chunks(T * top_k) * E));
+}
+
+rudnn_moe_status rudnn_moe_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input,
+                                    rudnn_moe_dtype dt, int64_t H, void* dispatched, int32_t* offsets,
+                                    int32_t* token_map, void* workspace, size_t workspace_size, hipStream_t stream) {
+    if (T < 0 || E < 1 || H < 1) return RUDNN_MOE_ERR_SHAPE;
+    if (k < 1 || k > E) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!valid_dtype(dt)) return RUDNN_MOE_ERR_DTYPE;
+    if (E > MAX_EXPERTS || k > MAX_TOP_K || T * k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (!offsets) return RUDNN_MOE_ERR_ARGUMENT;
+    const size_t es = dtype_size(dt), pk = (size_t)(T * k), rb = (size_t)H * es;
+    const size_t need = rudnn_moe_dispatch_workspace_size(T, k, E);
+    if (T > 0) {
+        if (!idx || !input || !dispatched || !token_map) return RUDNN_MOE_ERR_ARGUMENT;
+        if (!workspace || workspace_size < need) return RUDNN_MOE_ERR_WORKSPACE;
+    }
+    if (any_overlap({{dispatched, pk * rb}, {offsets, 4 * (size_t)(E + 1)}, {token_map, pk * 4}, {workspace, need}},
+                    {{idx, pk * 4}, {input, (size_t)T * rb}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    rudnn_moe_status st;
+    if (T == 0) {
+        // no pairs: all offsets are zero
+        if ((st = check_device(stream, {offsets})) != RUDNN_MOE_OK) return st;
+        return runtime(launch_fill_i32(offsets, E + 1, 0, stream));
+    }
+    if ((st = check_device(stream, {idx, input, dispatched, offsets, token_map, workspace})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_dispatch(idx, T, k, E, input, rb, dispatched, offsets, token_map, (int32_t*)workspace,
+                                   stream));
+}
+
+size_t rudnn_moe_experts_workspace_size(const rudnn_moe_experts* ex, int64_t rows) {
+    if (!ex || rows < 0 || ex->num_experts < 1 || ex->intermediate < 1 || !valid_dtype(ex->dtype)) return 0;
+    return experts_workspace_bytes(ex->num_experts, ex->hidden, ex->intermediate, ex->dtype, rows);
+}
+
+rudnn_moe_status rudnn_moe_experts_forward(const rudnn_moe_experts* ex, const void* dispatched, const int32_t* offsets,
+                                           int64_t rows, void* out, void* workspace, size_t workspace_size,
+                                           hipStream_t stream) {
+    rudnn_moe_status st = check_experts_view(ex);
+    if (st != RUDNN_MOE_OK) return st;
+    if ((st = check_experts_rows(ex, rows)) != RUDNN_MOE_OK) return st;
+    if (rows == 0) return RUDNN_MOE_OK;
+    if (!dispatched || !offsets || !out) return RUDNN_MOE_ERR_ARGUMENT;
+    if (ex->dtype != RUDNN_MOE_F32 && ((uintptr_t)dispatched % 16 || (uintptr_t)out % 16))
+        return RUDNN_MOE_ERR_UNSUPPORTED;
+    const size_t need = rudnn_moe_experts_workspace_size(ex, rows);
+    if (!workspace || workspace_size < need) return RUDNN_MOE_ERR_WORKSPACE;
+    const size_t es = dtype_size(ex->dtype);
+    const size_t wsz = (size_t)(ex->num_experts * ex->hidden * ex->intermediate) * es;
+    const size_t xb = (size_t)rows * ex->hidden * es;
+    if (any_overlap({{out, xb}, {workspace, need}},
+                    {{dispatched, xb}, {offsets, 4 * (size_t)(ex->num_experts + 1)}, {ex->gate, wsz}, {ex->up, wsz},
+                     {ex->down, wsz}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    if ((st = check_device(stream, {dispatched, offsets, out, workspace, ex->gate, ex->up, ex->down})) != RUDNN_MOE_OK)
+        return st;
+    return runtime(launch_experts(ex, dispatched, offsets, rows, out, workspace, stream));
+}
+
+rudnn_moe_status rudnn_moe_combine(const void* y, rudnn_moe_dtype dt, const int32_t* token_map, const void* w,
+                                   rudnn_moe_dtype wdt, int64_t T, int64_t k, int64_t H, void* out,
+                                   hipStream_t stream) {
+    if (T < 0 || H < 1) return RUDNN_MOE_ERR_SHAPE;
+    if (k < 1) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!valid_dtype(dt) || !valid_dtype(wdt)) return RUDNN_MOE_ERR_DTYPE;
+    if (k > MAX_TOP_K || T * k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (T == 0) return RUDNN_MOE_OK;
+    if (!y || !token_map || !w || !out) return RUDNN_MOE_ERR_ARGUMENT;
+    const size_t es = dtype_size(dt), pk = (size_t)(T * k);
+    if (any_overlap({{out, (size_t)T * H * es}},
+                    {{y, pk * H * es}, {token_map, pk * 4}, {w, pk * dtype_size(wdt)}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    rudnn_moe_status st;
+    if ((st = check_device(stream, {y, token_map, w, out})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_combine(y, dt, token_map, w, wdt, T, k, H, out, stream));
+}
+
+namespace {
+struct ForwardLayout {
+    size_t idx, w, offsets, map, dws, disp, ews, y, total;
+};
+
+ForwardLayout forward_layout(const rudnn_moe_experts* ex, int64_t T, int64_t k, rudnn_moe_dtype ldt) {
+    ForwardLayout L;
+    const size_t es = dtype_size(ex->dtype), pk = (size_t)(T * k);
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        size_t at = off;
+        off += align_up(n);
+        return at;
+    };
+    L.idx = take(pk * 4);
+    L.w = take(pk * dtype_size(ldt));
+    L.offsets = take(4 * (size_t)(ex->num_experts + 1));
+    L.map = take(pk * 4);
+    L.dws = take(rudnn_moe_dispatch_workspace_size(T, k, ex->num_experts));
+    L.disp = take(pk * ex->hidden * es);
+    L.ews = take(experts_workspace_bytes(ex->num_experts, ex->hidden, ex->intermediate, ex->dtype, (int64_t)pk));
+    L.y = take(pk * ex->hidden * es);
+    L.total = off;
+    return L;
+}
+}  // namespace
+
+size_t rudnn_moe_forward_workspace_size(const rudnn_moe_experts* ex, int64_t T, int64_t top_k,
+                                        rudnn_moe_dtype logits_dtype) {
+    if (!ex || T < 0 || top_k < 1 || ex->num_experts < 1 || ex->hidden < 1 || ex->intermediate < 1 ||
+        !valid_dtype(ex->dtype) || !valid_dtype(logits_dtype))
+        return 0;
+    return forward_layout(ex, T, top_k, logits_dtype).total;
+}
+
+rudnn_moe_status rudnn_moe_forward(const rudnn_moe_experts* ex, const void* input, const void* logits,
+                                   rudnn_moe_dtype ldt, int64_t T, rudnn_moe_routing_options opt, void* output,
+                                   void* workspace, size_t workspace_size, hipStream_t stream) {
+    rudnn_moe_status st = check_experts_view(ex);
+    if (st != RUDNN_MOE_OK) return st;
+    if (T < 0) return RUDNN_MOE_ERR_SHAPE;
+    if (opt.top_k < 1 || opt.top_k > ex->num_experts) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!valid_dtype(ldt)) return RUDNN_MOE_ERR_DTYPE;
+    if (opt.top_k > MAX_TOP_K || T * opt.top_k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if ((st = check_experts_rows(ex, T * opt.top_k)) != RUDNN_MOE_OK) return st;
+    if (T == 0) return RUDNN_MOE_OK;
+    if (!input || !logits || !output) return RUDNN_MOE_ERR_ARGUMENT;
+    if (ex->dtype != RUDNN_MOE_F32 && ((uintptr_t)input % 16 || (uintptr_t)output % 16))
+        return RUDNN_MOE_ERR_UNSUPPORTED;
+    const ForwardLayout L = forward_layout(ex, T, opt.top_k, ldt);
+    if (!workspace || workspace_size < L.total) return RUDNN_MOE_ERR_WORKSPACE;
+    const size_t es = dtype_size(ex->dtype);
+    const size_t wsz = (size_t)(ex->num_experts * ex->hidden * ex->intermediate) * es;
+    const size_t xb = (size_t)T * ex->hidden * es;
+    if (any_overlap({{output, xb}, {workspace, L.total}},
+                    {{input, xb}, {logits, (size_t)(T * ex->num_experts) * dtype_size(ldt)}, {ex->gate, wsz},
+                     {ex->up, wsz}, {ex->down, wsz}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    if ((st = check_device(stream, {input, logits, output, workspace, ex->gate, ex->up, ex->down})) != RUDNN_MOE_OK)
+        return st;
+    unsigned char* ws = (unsigned char*)workspace;
+    uint32_t* idx = (uint32_t*)(ws + L.idx);
+    void* w = ws + L.w;
+    int32_t* offsets = (int32_t*)(ws + L.offsets);
+    int32_t* map = (int32_t*)(ws + L.map);
+    void* disp = ws + L.disp;
+    void* y = ws + L.y;
+    const int64_t E = ex->num_experts, k = opt.top_k, H = ex->hidden;
+    hipError_t e = launch_route(logits, ldt, T, E, k, opt.renormalize != 0, idx, w, stream);
+    if (e == hipSuccess)
+        e = launch_dispatch(idx, T, k, E, input, (size_t)H * es, disp, offsets, map, (int32_t*)(ws + L.dws), stream);
+    if (e == hipSuccess) e = launch_experts(ex, disp, offsets, T * k, y, ws + L.ews, stream);
+    if (e == hipSuccess) e = launch_combine(y, ex->dtype, map, w, ldt, T, k, H, output, stream);
+    return runtime(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// dispatch.hip -- capacity-free grouping of tokens by expert (ruDNN user guide, section 5
+// "Expert weights and dispatch").
+//
+// The T*k (token, slot) pairs, flattened as a = t*k + j, are cut into chunks of
+// DISPATCH_CHUNK pairs.  Four kernels:
+//   count  one block per chunk: LDS histogram of the chunk's expert ids, stored as
+//          chunk_counts[c, e] (every entry written, so nothing needs clearing first);
+//   scan   one block: per expert, the exclusive sum of its counts over the chunks (in place,
+//          turning counts into per-chunk bases), then the exclusive sum over experts ->
+//          expert_offsets[E+1];
+//   rank   one block per chunk: the stable rank of each pair among the chunk's pairs of the
+//          same expert (wavefront ballots for lanes with equal ids, LDS counters across the
+//          block's waves and rounds); token_map[a] = offsets[e] + base[c, e] + rank.  Rows of
+//          an expert therefore follow (t, j) order, and the result does not depend on
+//          scheduling (no global atomics);
+//   copy   one wavefront per token: the token row is read from HBM once, in 16-byte vectors,
+//          and written to its k dispatched rows.
+// HBM traffic: T*k*4 (ids, twice) + T*H*s (tokens, once) + T*k*H*s (rows) + T*k*4 (map).
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace rudnn {
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const uint32_t* __restrict__ idx, int64_t pairs, int E,
+                                                             int32_t* __restrict__ chunk_counts) {
+    extern __shared__ int hist[];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+    __syncthreads();
+    const int64_t a0 = (int64_t)blockIdx.x * DISPATCH_CHUNK;
+    const int64_t a1 = min(pairs, a0 + DISPATCH_CHUNK);
+    for (int64_t a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
+        const uint32_t e = idx[a];
+        if (e < (uint32_t)E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunks, int E,
+                                                            int32_t* __restrict__ offsets) {
+    __shared__ int scratch[17];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int c = 0; c < nchunks; ++c) {
+            const int n = chunk_counts[(int64_t)c * E + e];
+            chunk_counts[(int64_t)c * E + e] = run;
+            run += n;
+        }
+    }
+    int total;
+    const int excl = block_exclusive_scan(e < E ? run : 0, scratch, &total);
+    if (e < E) offsets[e] = excl;
+    if (e == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(const uint32_t* __restrict__ idx, int64_t pairs, int E,
+                                                            const int32_t* __restrict__ chunk_base,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ token_map) {
+    extern __shared__ int sm[];
+    int* run = sm;       // [E]    pairs of expert e already ranked in earlier rounds
+    int* wcnt = sm + E;  // [4][E] pairs of expert e held by wave w in this round
+    for (int i = threadIdx.x; i < 5 * E; i += blockDim.x) sm[i] = 0;
+    __syncthreads();
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int64_t a0 = (int64_t)blockIdx.x * DISPATCH_CHUNK;
+    const int64_t a1 = min(pairs, a0 + DISPATCH_CHUNK);
+    const int32_t* base = chunk_base + (int64_t)blockIdx.x * E;
+    for (int64_t r0 = a0; r0 < a1; r0 += blockDim.x) {
+        const int64_t a = r0 + threadIdx.x;
+        const bool in = a < a1;
+        const uint32_t e = in ? idx[a] : 0xffffffffu;
+        const bool valid = in && e < (uint32_t)E;
+        // Group the wave's lanes by expert id: one iteration per distinct id.
+        uint64_t rem = __ballot(valid);
+        int rank = 0, group = 0;
+        while (rem != 0) {
+            const int leader = __builtin_ctzll(rem);
+            const uint32_t le = (uint32_t)readlane((int)e, leader);
+            const uint64_t peers = __ballot(valid && e == le);
+            if (valid && e == le) {
+                rank = __popcll(peers & lt_mask);
+                if (lane == leader) group = __popcll(peers);
+            }
+            rem &= ~peers;
+        }
+        if (group) wcnt[wave * E + e] = group;
+        __syncthreads();
+        if (valid) {
+            int r = run[e] + rank;
+            for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
+            token_map[a] = offsets[e] + base[e] + r;
+        } else if (in) {
+            token_map[a] = -1;
+        }
+        __syncthreads();
+        if (group) {
+            atomicAdd(&run[e], group);
+            wcnt[wave * E + e] = 0;
+        }
+        __syncthreads();
+    }
+}
+
+// One wavefront per token; V is the copy unit (16-byte vector when the row allows it).
+template <typename V, int UNROLL>
+__global__ __launch_bounds__(256) void dispatch_copy_kernel(const V* __restrict__ x, int64_t T, int k, int64_t row_units,
+                                                            const int32_t* __restrict__ token_map,
+                                                            V* __restrict__ out) {
+    const int lane = lane_id();
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int my_row = lane < k ? token_map[t * k + lane] : -1;
+    const V* src = x + t * row_units;
+    for (int64_t u0 = 0; u0 < row_units; u0 += 64 * UNROLL) {
+        V buf[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t i = u0 + u * 64 + lane;
+            if (i < row_units) buf[u] = src[i];
+        }
+        for (int j = 0; j < k; ++j) {
+            const int dst = readlane(my_row, j);
+            if (dst < 0) continue;
+            V* d = out + (int64_t)dst * row_units;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t i = u0 + u * 64 + lane;
+                if (i < row_units) d[i] = buf[u];
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+    if (n > 0) fill_i32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input, size_t row_bytes,
+                           void* dispatched, int32_t* offsets, int32_t* token_map, int32_t* chunk_counts,
+                           hipStream_t s) {
+    const int64_t pairs = T * k;
+    const int nchunks = (int)dispatch_chunks(pairs);
+    const int Ei = (int)E;
+    timing_before(RUDNN_MOE_KERNEL_DISPATCH_COUNT, s);
+    dispatch_count_kernel<<<nchunks, 256, E * sizeof(int), s>>>(idx, pairs, Ei, chunk_counts);
+    timing_after(RUDNN_MOE_KERNEL_DISPATCH_COUNT, s);
+    timing_before(RUDNN_MOE_KERNEL_DISPATCH_SCAN, s);
+    dispatch_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, nchunks, Ei, offsets);
+    timing_after(RUDNN_MOE_KERNEL_DISPATCH_SCAN, s);
+    timing_before(RUDNN_MOE_KERNEL_DISPATCH_RANK, s);
+    dispatch_rank_kernel<<<nchunks, 256, 5 * E * sizeof(int), s>>>(idx, pairs, Ei, chunk_counts, offsets, token_map);
+    timing_after(RUDNN_MOE_KERNEL_DISPATCH_RANK, s);
+    const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+    const int ki = (int)k;
+    timing_before(RUDNN_MOE_KERNEL_DISPATCH_COPY, s);
+    if (row_bytes % 16 == 0 && ((uintptr_t)input % 16) == 0 && ((uintptr_t)dispatched % 16) == 0)
+        dispatch_copy_kernel<uint4, 4><<<grid, block, 0, s>>>((const uint4*)input, T, ki, (int64_t)(row_bytes / 16),
+                                                              token_map, (uint4*)dispatched);
+    else if (row_bytes % 4 == 0 && ((uintptr_t)input % 4) == 0 && ((uintptr_t)dispatched % 4) == 0)
+        dispatch_copy_kernel<uint32_t, 4><<<grid, block, 0, s>>>((const uint32_t*)input, T, ki,
+                                                                 (int64_t)(row_bytes / 4), token_map,
+                                                                 (uint32_t*)dispatched);
+    else
+        dispatch_copy_kernel<uint16_t, 4><<<grid, block, 0, s>>>((const uint16_t*)input, T, ki,
+                                                                 (int64_t)(row_bytes / 2), token_map,
+                                                                 (uint16_t*)dispatched);
+    timing_after(RUDNN_MOE_KERNEL_DISPATCH_COPY, s);
+    return hipGetLastError();
+}
+
+}  // namespace rudnn

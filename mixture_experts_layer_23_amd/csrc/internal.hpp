@@ -1,0 +1,49 @@
+// internal.hpp -- host-side contract between the C-ABI layer (api.cpp) and the kernel files.
+// Launchers only enqueue; argument validation happens in api.cpp before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rudnn_moe.h"
+
+namespace rudnn {
+
+// Dispatch works on chunks of DISPATCH_CHUNK consecutive (token, slot) pairs; one block of the
+// count and rank kernels owns one chunk.  Workspace: [nchunks, E] int32 per-chunk counts that
+// the scan kernel turns into per-chunk bases in place.
+constexpr int64_t DISPATCH_CHUNK = 4096;
+inline int64_t dispatch_chunks(int64_t pairs) { return (pairs + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK; }
+
+// Kernel limits (documented in rudnn_moe.h as RUDNN_MOE_ERR_UNSUPPORTED).
+constexpr int64_t MAX_EXPERTS = 1024;
+constexpr int64_t MAX_TOP_K = 64;
+
+inline size_t align_up(size_t n, size_t a = 256) { return (n + a - 1) / a * a; }
+inline size_t dtype_size(rudnn_moe_dtype d) { return d == RUDNN_MOE_F32 ? 4 : 2; }
+
+// Per-thread one-shot timing hook (rudnn_moe_time_next_launch).
+void timing_before(rudnn_moe_kernel k, hipStream_t s);
+void timing_after(rudnn_moe_kernel k, hipStream_t s);
+
+// ---- launchers (each returns hipGetLastError() after its launches) ----
+hipError_t launch_route(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E, int64_t k, bool renorm,
+                        uint32_t* idx, void* w, hipStream_t s);
+
+hipError_t launch_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input, size_t row_bytes,
+                           void* dispatched, int32_t* offsets, int32_t* token_map, int32_t* chunk_counts,
+                           hipStream_t s);
+
+// n int32 values set to v (a kernel, so that the call stays capturable in a HIP graph).
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+hipError_t launch_combine(const void* y, rudnn_moe_dtype dt, const int32_t* token_map, const void* w,
+                          rudnn_moe_dtype wdt, int64_t T, int64_t k, int64_t H, void* out, hipStream_t s);
+
+// Expert GEMMs.  Workspace layout is owned by experts.hip.
+size_t experts_workspace_bytes(int64_t E, int64_t H, int64_t I, rudnn_moe_dtype dt, int64_t rows);
+hipError_t launch_experts(const rudnn_moe_experts* ex, const void* dispatched, const int32_t* offsets, int64_t rows,
+                          void* out, void* workspace, hipStream_t s);
+
+}  // namespace rudnn

@@ -1,0 +1,247 @@
+"""Thin ctypes binding of ``librudnn_moe.so`` (C ABI: include/rudnn_moe.h).
+
+Argument marshalling only: every step of the MoE path runs in the library's HIP kernels, on
+torch's current stream of the tensors' device.  Output and workspace buffers are allocated
+with torch (PyTorch is plumbing here: device memory and streams).  There is no fallback: if
+the library is missing, or a call returns an error status, this module raises.
+
+The functions follow the ruDNN user guide's MoE API (sections 3-6): ``route``,
+``dispatch``, ``experts_forward`` (``SwiGluExperts.forward_dispatched``), ``combine`` and
+``forward`` (``SwiGluExperts.forward``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librudnn_moe.so")
+
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+STATUS = {0: "ok", 1: "shape", 2: "dtype", 3: "argument", 4: "device", 5: "unsupported", 6: "workspace",
+          7: "runtime"}
+
+KERNELS = ("route", "dispatch_count", "dispatch_scan", "dispatch_rank", "dispatch_copy", "experts_plan",
+           "experts_gate_up", "experts_down", "combine")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _lib.rudnn_moe_status_string(status).decode() if _lib is not None else STATUS.get(status, "?")
+        super().__init__(f"{fn}: {msg} (status {status})")
+
+
+class RoutingOptions(ctypes.Structure):
+    _fields_ = [("top_k", ctypes.c_int64), ("renormalize", ctypes.c_int32)]
+
+
+class ExpertsView(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("num_experts", ctypes.c_int64), ("hidden", ctypes.c_int64), ("intermediate", ctypes.c_int64),
+                ("dtype", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        # torch was imported first, so the library binds to torch's HIP runtime (same soname);
+        # a second runtime in the process would not know torch's streams and allocations.
+        runtimes = _loaded_hip_runtimes()
+        if len(runtimes) > 1:
+            raise RuntimeError(f"more than one HIP runtime loaded: {runtimes}")
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        EXP = ctypes.POINTER(ExpertsView)
+        L.rudnn_moe_route.argtypes = [P, I32, I64, I64, RoutingOptions, P, P, P]
+        L.rudnn_moe_dispatch_workspace_size.argtypes = [I64, I64, I64]
+        L.rudnn_moe_dispatch_workspace_size.restype = SZ
+        L.rudnn_moe_dispatch.argtypes = [P, I64, I64, I64, P, I32, I64, P, P, P, P, SZ, P]
+        L.rudnn_moe_experts_workspace_size.argtypes = [EXP, I64]
+        L.rudnn_moe_experts_workspace_size.restype = SZ
+        L.rudnn_moe_experts_forward.argtypes = [EXP, P, P, I64, P, P, SZ, P]
+        L.rudnn_moe_combine.argtypes = [P, I32, P, P, I32, I64, I64, I64, P, P]
+        L.rudnn_moe_forward_workspace_size.argtypes = [EXP, I64, I64, I32]
+        L.rudnn_moe_forward_workspace_size.restype = SZ
+        L.rudnn_moe_forward.argtypes = [EXP, P, P, I32, I64, RoutingOptions, P, P, SZ, P]
+        L.rudnn_moe_status_string.argtypes = [I32]
+        L.rudnn_moe_status_string.restype = ctypes.c_char_p
+        L.rudnn_moe_time_next_launch.argtypes = [I32, P, P]
+        for f in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
+                  "rudnn_moe_forward", "rudnn_moe_time_next_launch"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _loaded_hip_runtimes():
+    import re
+    try:
+        maps = open("/proc/self/maps").read()
+    except OSError:
+        return []
+    return sorted({os.path.realpath(p) for p in re.findall(r"(/\S*libamdhip64\.so\S*)", maps)})
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _contig(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def time_next_launch(kernel: str, before: int, after: int) -> None:
+    """Record the raw ``hipEvent_t`` handles ``before``/``after`` on the launch stream around the
+    next launch of ``kernel`` by this host thread (measurement only)."""
+    _check("rudnn_moe_time_next_launch", lib().rudnn_moe_time_next_launch(KERNELS.index(kernel), before, after))
+
+
+class SwiGluExperts:
+    """Bias-free SwiGLU expert weights: gate/up [E, I, H], down [E, H, I], one dtype and device
+    (user guide section 5).  Reusable across batches (section 6)."""
+
+    def __init__(self, gate: torch.Tensor, up: torch.Tensor, down: torch.Tensor):
+        if gate.dim() != 3 or up.shape != gate.shape or down.dim() != 3:
+            raise ValueError("gate and up must be [E, I, H] and down [E, H, I]")
+        E, I, H = gate.shape
+        if tuple(down.shape) != (E, H, I):
+            raise ValueError("down must be [E, H, I]")
+        if not (gate.dtype == up.dtype == down.dtype) or not (gate.device == up.device == down.device):
+            raise ValueError("gate, up and down must share dtype and device")
+        self.gate, self.up, self.down = (_contig(t, n) for t, n in ((gate, "gate"), (up, "up"), (down, "down")))
+        self.E, self.I, self.H = E, I, H
+        self.view = ExpertsView(gate.data_ptr(), up.data_ptr(), down.data_ptr(), E, H, I, _dt(gate))
+
+    @property
+    def dtype(self):
+        return self.gate.dtype
+
+    @property
+    def device(self):
+        return self.gate.device
+
+    def forward(self, input: torch.Tensor, logits: torch.Tensor, top_k: int, renormalize: bool, out=None,
+                workspace=None) -> torch.Tensor:
+        return forward(self, input, logits, top_k, renormalize, out=out, workspace=workspace)
+
+    def forward_dispatched(self, d: "Dispatched", out=None, workspace=None) -> torch.Tensor:
+        return experts_forward(self, d.dispatched, d.expert_offsets, out=out, workspace=workspace)
+
+
+def route(logits: torch.Tensor, top_k: int, renormalize: bool):
+    """Returns ``(expert_indices [T, k] int32 holding the uint32 ids, weights [T, k] logits dtype)``."""
+    logits = _contig(logits, "logits")
+    T, E = logits.shape
+    idx = torch.empty(T, top_k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, top_k, dtype=logits.dtype, device=logits.device)
+    _check("rudnn_moe_route", lib().rudnn_moe_route(_ptr(logits), _dt(logits), T, E, RoutingOptions(top_k, int(renormalize)),
+                                                    _ptr(idx), _ptr(w), _stream(logits)))
+    return idx, w
+
+
+@dataclass
+class Dispatched:
+    dispatched: torch.Tensor      # [T*k, H]
+    expert_offsets: torch.Tensor  # [E+1] int32
+    token_map: torch.Tensor       # [T, k] int32
+
+
+def dispatch(expert_indices: torch.Tensor, input: torch.Tensor, num_experts: int, out: Dispatched | None = None,
+             workspace=None) -> Dispatched:
+    expert_indices = _contig(expert_indices, "expert_indices")
+    input = _contig(input, "input")
+    T, k = expert_indices.shape
+    H = input.shape[1]
+    dev = input.device
+    if out is None:
+        out = Dispatched(torch.empty(T * k, H, dtype=input.dtype, device=dev),
+                         torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
+                         torch.empty(T, k, dtype=torch.int32, device=dev))
+    need = lib().rudnn_moe_dispatch_workspace_size(T, k, num_experts)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("rudnn_moe_dispatch", lib().rudnn_moe_dispatch(
+        _ptr(expert_indices), T, k, num_experts, _ptr(input), _dt(input), H, _ptr(out.dispatched),
+        _ptr(out.expert_offsets), _ptr(out.token_map), _ptr(workspace), workspace.numel(), _stream(input)))
+    return out
+
+
+def experts_workspace_size(experts: SwiGluExperts, rows: int) -> int:
+    return lib().rudnn_moe_experts_workspace_size(ctypes.byref(experts.view), rows)
+
+
+def experts_forward(experts: SwiGluExperts, dispatched: torch.Tensor, expert_offsets: torch.Tensor, out=None,
+                    workspace=None) -> torch.Tensor:
+    dispatched = _contig(dispatched, "dispatched")
+    rows = dispatched.shape[0]
+    if out is None:
+        out = torch.empty_like(dispatched)
+    if workspace is None:
+        workspace = torch.empty(max(experts_workspace_size(experts, rows), 1), dtype=torch.uint8,
+                                device=dispatched.device)
+    _check("rudnn_moe_experts_forward", lib().rudnn_moe_experts_forward(
+        ctypes.byref(experts.view), _ptr(dispatched), _ptr(expert_offsets), rows, _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream(dispatched)))
+    return out
+
+
+def combine(expert_output: torch.Tensor, token_map: torch.Tensor, weights: torch.Tensor, out=None) -> torch.Tensor:
+    expert_output = _contig(expert_output, "expert_output")
+    T, k = token_map.shape
+    H = expert_output.shape[1]
+    if out is None:
+        out = torch.empty(T, H, dtype=expert_output.dtype, device=expert_output.device)
+    _check("rudnn_moe_combine", lib().rudnn_moe_combine(
+        _ptr(expert_output), _dt(expert_output), _ptr(_contig(token_map, "token_map")), _ptr(_contig(weights, "weights")),
+        _dt(weights), T, k, H, _ptr(out), _stream(expert_output)))
+    return out
+
+
+def forward_workspace_size(experts: SwiGluExperts, T: int, top_k: int, logits_dtype: torch.dtype) -> int:
+    return lib().rudnn_moe_forward_workspace_size(ctypes.byref(experts.view), T, top_k, _DT[logits_dtype])
+
+
+def forward(experts: SwiGluExperts, input: torch.Tensor, logits: torch.Tensor, top_k: int, renormalize: bool,
+            out=None, workspace=None) -> torch.Tensor:
+    """The whole local forward route -> dispatch -> experts -> combine (user guide section 6)."""
+    input = _contig(input, "input")
+    logits = _contig(logits, "logits")
+    T = input.shape[0]
+    if out is None:
+        out = torch.empty_like(input)
+    if workspace is None:
+        workspace = torch.empty(max(forward_workspace_size(experts, T, top_k, logits.dtype), 1), dtype=torch.uint8,
+                                device=input.device)
+    _check("rudnn_moe_forward", lib().rudnn_moe_forward(
+        ctypes.byref(experts.view), _ptr(input), _ptr(logits), _dt(logits), T, RoutingOptions(top_k, int(renormalize)),
+        _ptr(out), _ptr(workspace), workspace.numel(), _stream(input)))
+    return out

@@ -1,0 +1,338 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle, on the same seeded
+inputs.  Indices, dispatch counts and maps are compared bit for bit; floating-point outputs
+within the stated tolerances (FP32: 1e-4 relative + 1e-5; BF16/F16: 2e-2 relative with a
+floor of 2e-2 times the RMS of the reference, see ``assert_close``); NaN positions exactly.
+
+Small cases run the whole oracle; the full-size workloads compare sampled tokens, which the
+oracle computes one by one (each token's output depends only on its own row)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_23_amd import moe
+from mixture_experts_layer_23_amd.inputs import DTYPES, WORKLOADS, Workload, make_experts, make_logits, make_tokens
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+
+
+def assert_close(got: torch.Tensor, ref: torch.Tensor, dt: str, what: str = ""):
+    g = got.detach().double().cpu()
+    r = ref.detach().double().cpu()
+    assert g.shape == r.shape, what
+    gn, rn = torch.isnan(g), torch.isnan(r)
+    assert torch.equal(gn, rn), f"{what}: NaN positions differ ({int((gn != rn).sum())} elements)"
+    inf = torch.isinf(r)
+    assert torch.equal(g[inf], r[inf]), f"{what}: infinities differ"
+    fin = torch.isfinite(r)
+    if not fin.any():
+        return
+    d = (g - r).abs()[fin]
+    ra = r.abs()[fin]
+    if dt == "f32":
+        bound = 1e-4 * ra + 1e-5
+    else:
+        rms = r[fin].pow(2).mean().sqrt()
+        bound = 2e-2 * ra + 2e-2 * rms
+    bad = d > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())}/{d.numel()} elements out of tolerance; "
+                           f"max abs err {d.max():.3g}, max rel {(d / ra.clamp_min(1e-30)).max():.3g}")
+
+
+def gpu_route(logits, k, renorm):
+    idx, w = moe.route(logits.to(DEV), k, renorm)
+    return idx.cpu().numpy().astype(np.int64), w.cpu()
+
+
+def nan_rows_of(special):
+    return np.concatenate([special["nan"], special["posinf"], special["all_neginf"]]) if special else np.zeros(0, int)
+
+
+# ------------------------------------------------------------------------------------------
+# route
+# ------------------------------------------------------------------------------------------
+
+ROUTE_CASES = [(n, r) for n in ("tiny", "route_dispatch", "decode", "mixtral", "skewed") for r in (True, False)]
+
+
+@pytest.mark.parametrize("name,renorm", ROUTE_CASES, ids=[f"{n}-renorm{int(r)}" for n, r in ROUTE_CASES])
+def test_route_parity_full_size(name, renorm):
+    w = WORKLOADS[name]
+    say("route", name, "renorm", renorm, "T", w.T, "E", w.E, "k", w.top_k)
+    logits, special = make_logits(w)
+    idx, wt = gpu_route(logits, w.top_k, renorm)
+    ridx, rwt, _ = oracle.route(logits, w.top_k, renorm)
+    assert np.array_equal(idx, ridx.astype(np.int64)), f"{int((idx != ridx).sum())} indices differ"
+    assert_close(wt, rwt, w.logits_dtype, "weights")
+    for t in nan_rows_of(special):
+        assert idx[t].tolist() == list(range(w.top_k)) and torch.isnan(wt[t]).all()
+
+
+ROUTE_EDGE = [
+    # (T, E, k, dtype)
+    (1, 1, 1, "f32"), (5, 3, 3, "bf16"), (333, 64, 64, "f16"), (97, 65, 7, "bf16"), (70, 1000, 64, "f32"),
+    (129, 1024, 64, "bf16"), (1000, 1024, 1, "f16"), (257, 200, 16, "f32"), (64, 8, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("T,E,k,dt", ROUTE_EDGE)
+@pytest.mark.parametrize("renorm", [True, False])
+def test_route_edge_shapes(T, E, k, dt, renorm):
+    say("route-edge", T, E, k, dt, renorm)
+    special = (1, 1, 1, 1, 1, 1, 1) if (T >= 7 and E > k) else (0,) * 7
+    w = Workload("edge", T, 16, None, E, k, dt, dt, (renorm,), 1.0, 700 + T + E + k, special=special)
+    logits, _ = make_logits(w)
+    idx, wt = gpu_route(logits, k, renorm)
+    ridx, rwt, _ = oracle.route(logits, k, renorm)
+    assert np.array_equal(idx, ridx.astype(np.int64))
+    assert_close(wt, rwt, dt, "weights")
+
+
+def test_route_hand_cases():
+    import json, os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))["route"]
+    for c in cases:
+        logits = torch.tensor([[float(v) for v in r] for r in c["logits"]], dtype=torch.float64).to(DTYPES[c["dtype"]])
+        for renorm in (False, True):
+            idx, wt = gpu_route(logits, c["top_k"], renorm)
+            assert idx.tolist() == c["indices"], c["name"]
+            exp = np.array([[float(v) for v in r] for r in c["weights"][str(renorm).lower()]])
+            got = wt.double().numpy()
+            assert np.array_equal(np.isnan(exp), np.isnan(got)), c["name"]
+            fin = ~np.isnan(exp)
+            assert np.all(np.abs(got[fin] - exp[fin]) <= max(c["tol"], 2e-7)), c["name"]
+
+
+# ------------------------------------------------------------------------------------------
+# dispatch and combine
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["route_dispatch", "skewed", "mixtral", "decode", "tiny"])
+def test_dispatch_parity_full_size(name):
+    w = WORKLOADS[name]
+    say("dispatch", name, "T", w.T, "H", w.H, "E", w.E, "k", w.top_k)
+    logits, _ = make_logits(w)
+    ridx, _, _ = oracle.route(logits, w.top_k, True)
+    x = make_tokens(w, DEV)
+    d = moe.dispatch(torch.from_numpy(ridx.astype(np.int32)).to(DEV), x, w.E)
+    torch.cuda.synchronize()
+    rdisp, roffs, rmap, _ = oracle.dispatch(ridx, x.cpu(), w.E)
+    assert np.array_equal(d.expert_offsets.cpu().numpy(), roffs)
+    tmap = d.token_map.cpu().numpy()
+    # the implementation's documented order is (t, j) inside an expert: the oracle's order
+    assert np.array_equal(tmap, rmap)
+    # and independently of that order: a bijection whose rows hold their tokens bit for bit
+    n = w.T * w.top_k
+    assert np.array_equal(np.sort(tmap.ravel()), np.arange(n))
+    e = ridx.astype(np.int64)
+    assert np.all((roffs[e] <= tmap) & (tmap < roffs[e + 1]))
+    ib = torch.int32 if x.dtype == torch.float32 else torch.int16
+    assert torch.equal(d.dispatched.cpu().view(ib), rdisp.view(ib))
+
+
+def test_dispatch_invalid_indices_are_contained():
+    say("dispatch-invalid")
+    w = WORKLOADS["route_dispatch"].with_T(300).replace(H=64, special=(0,) * 7)
+    logits, _ = make_logits(w)
+    ridx, rw, _ = oracle.route(logits, w.top_k, True)
+    bad = ridx.copy()
+    bad[[3, 77, 299], [0, 5, 7]] = [w.E, 10**6, 2**32 - 1]
+    x = make_tokens(w, DEV)
+    d = moe.dispatch(torch.from_numpy(bad.view(np.int32)).to(DEV), x, w.E)
+    rdisp, roffs, rmap, _ = oracle.dispatch(bad, x.cpu(), w.E)
+    assert np.array_equal(d.expert_offsets.cpu().numpy(), roffs)
+    assert np.array_equal(d.token_map.cpu().numpy(), rmap)
+    valid = rmap.ravel() >= 0
+    got = d.dispatched.cpu()[: int(roffs[-1])]
+    assert torch.equal(got.view(torch.int16), rdisp[: int(roffs[-1])].view(torch.int16))
+    out = moe.combine(d.dispatched, d.token_map, rw.to(DEV))
+    ref = oracle.combine(rdisp, rmap, rw)
+    assert_close(out, ref, "bf16", "combine")
+    assert torch.isnan(out[[3, 77, 299]].cpu()).all() and valid.sum() == w.T * w.top_k - 3
+
+
+@pytest.mark.parametrize("name,renorm", [("route_dispatch", True), ("route_dispatch", False), ("skewed", False)])
+def test_route_dispatch_combine_roundtrip_full_size(name, renorm):
+    """Identity experts: combine(dispatch(x)) = x * sum_j w[t, j] (route+dispatch workload)."""
+    w = WORKLOADS[name]
+    say("roundtrip", name, renorm)
+    logits, special = make_logits(w)
+    x = make_tokens(w, DEV)
+    lg = logits.to(DEV)
+    idx, wt = moe.route(lg, w.top_k, renorm)
+    d = moe.dispatch(idx, x, w.E)
+    out = moe.combine(d.dispatched, d.token_map, wt)
+    ref = oracle.forward(x.cpu(), logits, w.top_k, renorm)
+    assert_close(out, ref, w.dtype, "roundtrip")
+    nan_rows = nan_rows_of(special)
+    if len(nan_rows):
+        assert torch.isnan(out[torch.from_numpy(nan_rows).to(DEV)]).all()
+
+
+def test_combine_exact_inverse_with_one_expert():
+    say("combine-inverse")
+    w = WORKLOADS["route_dispatch"].with_T(4096).replace(top_k=1, special=(0,) * 7)
+    logits, _ = make_logits(w)
+    x = make_tokens(w, DEV)
+    idx, wt = moe.route(logits.to(DEV), 1, True)
+    assert torch.all(wt == 1)
+    d = moe.dispatch(idx, x, w.E)
+    out = moe.combine(d.dispatched, d.token_map, wt)
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("dt,wdt,H,k", [("bf16", "bf16", 2048, 8), ("f16", "f32", 200, 3), ("f32", "bf16", 100, 2),
+                                        ("bf16", "f16", 64, 12)])
+def test_combine_parity(dt, wdt, H, k):
+    say("combine", dt, wdt, H, k)
+    T = 517
+    w = Workload("c", T, H, None, 32, k, dt, wdt, (True,), None, 900 + H + k)
+    logits, _ = make_logits(w)
+    ridx, rw, _ = oracle.route(logits, k, True)
+    _, _, rmap, _ = oracle.dispatch(ridx, torch.zeros(T, 1), 32, copy_rows=False)
+    y = make_tokens(w.replace(T=T * k), DEV)  # stands for the expert outputs
+    out = moe.combine(y, torch.from_numpy(rmap).to(DEV), rw.to(DEV))
+    ref = oracle.combine(y.cpu(), rmap, rw)
+    assert_close(out, ref, dt, "combine")
+
+
+# ------------------------------------------------------------------------------------------
+# experts and the full forward
+# ------------------------------------------------------------------------------------------
+
+SMALL_LAYERS = {
+    # spans several 256-row tiles with ragged tails, several n-tiles, both GEMMs
+    "bf16_multi_tile": Workload("bf16_multi_tile", 700, 512, 384, 8, 2, "bf16", "bf16", (True,), None, 201),
+    # skewed load with empty experts, fp16, no renormalisation
+    "f16_skewed": Workload("f16_skewed", 600, 256, 192, 32, 4, "f16", "f16", (False,), 1.2, 202),
+    # shapes that are not tile multiples (H, I multiples of 8 only)
+    "bf16_ragged_dims": Workload("bf16_ragged_dims", 77, 200, 136, 6, 3, "bf16", "bf16", (True,), None, 203),
+    # fp32 with dimensions that are not multiples of anything
+    "f32_odd": Workload("f32_odd", 45, 100, 52, 5, 2, "f32", "f32", (True,), None, 204),
+    "tiny": WORKLOADS["tiny"],
+    # a single expert: a dense SwiGLU
+    "one_expert": Workload("one_expert", 300, 256, 512, 1, 1, "bf16", "bf16", (True,), None, 205),
+    # top_k = E
+    "topk_all": Workload("topk_all", 130, 128, 64, 4, 4, "f16", "f16", (False,), None, 206),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_LAYERS))
+def test_experts_parity_small(name):
+    w = SMALL_LAYERS[name]
+    say("experts", name)
+    logits, _ = make_logits(w)
+    ridx, _, _ = oracle.route(logits, w.top_k, w.renormalize[0])
+    x = make_tokens(w, DEV)
+    gate, up, down = make_experts(w, DEV)
+    rdisp, roffs, rmap, _ = oracle.dispatch(ridx, x.cpu(), w.E)
+    ex = moe.SwiGluExperts(gate, up, down)
+    y = moe.experts_forward(ex, rdisp.to(DEV), torch.from_numpy(roffs).to(DEV))
+    ry = oracle.experts_forward(rdisp, roffs, gate.cpu(), up.cpu(), down.cpu())
+    assert_close(y, ry, w.dtype, "expert output")
+
+
+@pytest.mark.parametrize("name", list(SMALL_LAYERS))
+def test_forward_parity_small(name):
+    w = SMALL_LAYERS[name]
+    say("forward", name)
+    logits, special = make_logits(w)
+    x = make_tokens(w, DEV)
+    gate, up, down = make_experts(w, DEV)
+    ex = moe.SwiGluExperts(gate, up, down)
+    renorm = w.renormalize[0]
+    out = ex.forward(x, logits.to(DEV), w.top_k, renorm)
+    ref = oracle.forward(x.cpu(), logits, w.top_k, renorm, gate.cpu(), up.cpu(), down.cpu())
+    assert_close(out, ref, w.dtype, "forward")
+    # staged form == forward, bit for bit, and repeatable
+    idx, wt = moe.route(logits.to(DEV), w.top_k, renorm)
+    d = moe.dispatch(idx, x, w.E)
+    y = ex.forward_dispatched(d)
+    staged = moe.combine(y, d.token_map, wt)
+    ib = torch.int32 if w.dtype == "f32" else torch.int16
+    assert torch.equal(staged.view(ib), out.view(ib))
+    again = ex.forward(x, logits.to(DEV), w.top_k, renorm)
+    assert torch.equal(again.view(ib), out.view(ib))
+    for t in nan_rows_of(special):
+        assert torch.isnan(out[int(t)]).all()
+
+
+def sampled_oracle_forward(x, logits, rows, k, renorm, gate, up, down):
+    """The oracle's forward on the given tokens only: route, each selected expert on the
+    token's row (only the experts used are copied to the host), combine."""
+    xs, ls = x[rows].cpu(), logits[rows].cpu()
+    ridx, rw, _ = oracle.route(ls, k, renorm)
+    used = np.unique(ridx)
+    remap = {int(e): i for i, e in enumerate(used)}
+    sel = torch.from_numpy(used.astype(np.int64)).to(gate.device)
+    g, u, dn = gate[sel].cpu(), up[sel].cpu(), down[sel].cpu()
+    n = len(rows)
+    order = np.argsort(ridx.ravel(), kind="stable")  # group rows by expert
+    xr = xs.repeat_interleave(k, 0)[torch.from_numpy(order)]
+    eor = np.array([remap[int(e)] for e in ridx.ravel()[order]], np.int32)
+    yr = oracle.expert_rows(xr, eor, g, u, dn)
+    y = torch.empty_like(yr)
+    y[torch.from_numpy(order)] = yr
+    tmap = np.arange(n * k, dtype=np.int32).reshape(n, k)
+    return oracle.combine(y, tmap, rw)
+
+
+@pytest.mark.parametrize("name,nsample", [("decode", 16), ("skewed", 64), ("mixtral", 24)])
+def test_forward_parity_full_size_sampled(name, nsample):
+    w = WORKLOADS[name]
+    say("forward-full", name, "T", w.T, "H", w.H, "I", w.I, "E", w.E, "k", w.top_k, "sample", nsample)
+    logits, _ = make_logits(w)
+    x = make_tokens(w, DEV)
+    gate, up, down = make_experts(w, DEV)
+    ex = moe.SwiGluExperts(gate, up, down)
+    renorm = w.renormalize[0]
+    out = ex.forward(x, logits.to(DEV), w.top_k, renorm)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    rows = np.sort(rng.choice(w.T, size=min(nsample, w.T), replace=False))
+    # the hottest and the coldest tokens' experts are covered by taking first/last rows too
+    rows = np.unique(np.concatenate([rows, [0, w.T - 1]]))
+    say("oracle on", len(rows), "tokens")
+    ref = sampled_oracle_forward(x, logits, rows, w.top_k, renorm, gate, up, down)
+    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, w.dtype, "forward (sampled)")
+    # every output row is finite (no NaN rows in these workloads) and no row was left unwritten
+    assert torch.isfinite(out).all()
+
+
+def test_empty_and_degenerate_batches():
+    say("degenerate")
+    w = SMALL_LAYERS["bf16_multi_tile"]
+    gate, up, down = make_experts(w, DEV)
+    ex = moe.SwiGluExperts(gate, up, down)
+    x = torch.empty(0, w.H, dtype=torch.bfloat16, device=DEV)
+    lg = torch.empty(0, w.E, dtype=torch.bfloat16, device=DEV)
+    assert ex.forward(x, lg, 2, True).shape == (0, w.H)
+    idx, wt = moe.route(lg, 2, True)
+    assert idx.shape == (0, 2)
+    d = moe.dispatch(idx, x, w.E)
+    assert d.expert_offsets.cpu().tolist() == [0] * (w.E + 1)
+    # every token to one expert (others empty), T = 1, and T not a multiple of anything
+    for T, hot in ((1, 0), (513, 5)):
+        x = make_tokens(w.replace(T=T), DEV)
+        lg = torch.full((T, w.E), -30.0, dtype=torch.bfloat16)
+        lg[:, hot] = 5.0
+        lg[:, (hot + 1) % w.E] = 4.0
+        out = ex.forward(x, lg.to(DEV), 2, True)
+        ref = oracle.forward(x.cpu(), lg, 2, True, gate.cpu(), up.cpu(), down.cpu())
+        assert_close(out, ref, "bf16", f"T={T}")
