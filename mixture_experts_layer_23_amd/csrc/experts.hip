@@ -9,11 +9,13 @@
 //            tiles per expert and their exclusive prefix (no host round trip, no sync);
 //   gate_up  grouped GEMM, N = I, fused epilogue silu(g) * u (two accumulator sets per tile);
 //   down     grouped GEMM, N = H, K = I.
-// BF16/F16: v_mfma_f32_32x32x16_{bf16,f16} with FP32 accumulators; 512-thread blocks of eight
-// wavefronts, output tile 256 rows x 256 accumulator columns (gate_up: 128 of gate + 128 of up),
-// K staged 64 at a time through LDS (row pitch 144 B against bank conflicts), double-buffered:
-// the global loads of step k+1 are in flight while the MFMAs consume step k.
-// F32: the same schedule with an FP32 FMA tile (64 x 64) -- there is no reduced-precision step.
+// BF16/F16: v_mfma_f32_32x32x16_{bf16,f16} with FP32 accumulators.  A block of eight wavefronts
+// (4 along M x 2 along N) owns a 256-row tile of 256 accumulator columns (gate_up: 128 of gate +
+// 128 of up).  K is staged 64 at a time: tokens and weight rows go straight from global memory
+// into LDS with global_load_lds_dwordx4 (no register staging), in an XOR-swizzled layout that
+// keeps the MFMA operand reads free of bank conflicts.  Two LDS stages: the copies of step k+1
+// are issued under the MFMAs of step k; one barrier per step.
+// F32: a plain FP32 FMA tile (64 x 64) on the same tile plan -- no reduced-precision step.
 //
 // Tile order.  Tiles of expert e are enumerated in groups of GROUP_N n-tiles, all m-tiles of a
 // group together, so tiles that run side by side share both their weight columns and their
@@ -21,6 +23,9 @@
 // tile (start of XCD i % 8's share) + i / 8, so each XCD walks a contiguous, equal share of
 // the tile list and its 4 MB L2 sees the reuse.  The grid is sized for the worst case
 // (floor(rows / BM) + min(E, rows) m-tiles); blocks beyond the real count exit at once.
+#include <mutex>
+#include <type_traits>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -30,7 +35,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int GROUP_N = 8;
+#ifndef RUDNN_DMA_SPREAD
+#define RUDNN_DMA_SPREAD 2
+#endif
+#ifndef RUDNN_XCD_REMAP
+#define RUDNN_XCD_REMAP 1
+#endif
+#ifndef RUDNN_GROUP_N
+#define RUDNN_GROUP_N 4
+#endif
+constexpr int GROUP_N = RUDNN_GROUP_N;  // n-tiles scheduled together (see "Tile order")
 
 // ---------------------------------------------------------------------------------------
 // plan
@@ -71,9 +85,9 @@ __device__ __forceinline__ bool find_tile(const Plan& plan, int E, int N, int* s
     __syncthreads();
     const int NT = (N + BN - 1) / BN;
     const int64_t total = (int64_t)s_mt[E] * NT;
-    const int xcd = blockIdx.x & 7;
-    const int64_t slot = blockIdx.x >> 3;
-    const int64_t q = total >> 3, r = total & 7;
+    const int xcd = RUDNN_XCD_REMAP ? (blockIdx.x & 7) : 0;
+    const int64_t slot = RUDNN_XCD_REMAP ? (blockIdx.x >> 3) : blockIdx.x;
+    const int64_t q = RUDNN_XCD_REMAP ? (total >> 3) : total, r = RUDNN_XCD_REMAP ? (total & 7) : 0;
     const int64_t count = q + (xcd < r ? 1 : 0);
     if (slot >= count) return false;
     const int64_t L = xcd * q + min((int64_t)xcd, r) + slot;
@@ -123,78 +137,140 @@ struct Mfma<f16> {
     }
 };
 
-constexpr int MF_BM = 256;             // rows per tile
-constexpr int MF_BK = 64;              // K elements per LDS stage
-constexpr int MF_PITCH = MF_BK + 8;    // LDS row pitch in elements (144 B)
-constexpr int MF_THREADS = 512;        // 8 wavefronts: 4 along M x 2 along N
-constexpr int MF_WM = 4, MF_WN = 2;
+// Tile shapes: block rows BM, output columns BN per weight set, WM x WN wavefronts, K elements
+// per LDS stage BK (32 or 64), STAGES LDS buffers.  gate_up stages 2*BN weight rows (gate then
+// up) per tile.
+#ifndef RUDNN_GATE_UP_TILE
+#define RUDNN_GATE_UP_TILE 256, 128, 4, 2, 64, 2
+#endif
+#ifndef RUDNN_DOWN_TILE
+#define RUDNN_DOWN_TILE 256, 256, 4, 2, 64, 2
+#endif
 
-// DUAL: B0 = gate, B1 = up, BN = 128 columns of each; else B0 only, BN = 256.
-template <typename T, bool DUAL>
-__global__ __launch_bounds__(MF_THREADS) void grouped_gemm_mfma(const T* __restrict__ A, const T* __restrict__ B0,
-                                                                const T* __restrict__ B1, T* __restrict__ C, int K,
-                                                                int N, int E, Plan plan) {
-    constexpr int BM = MF_BM;
-    constexpr int BN = DUAL ? 128 : 256;    // output columns per tile
-    constexpr int NB = DUAL ? 2 * BN : BN;  // B rows staged per tile
-    constexpr int WTM = BM / MF_WM;         // 64
-    constexpr int WTN = BN / MF_WN;         // 64 (DUAL) or 128
-    constexpr int FM = WTM / 32, FN = WTN / 32;
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, int OCC_ = 1>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
+    static constexpr int OCC = OCC_;  // wavefronts per SIMD the register budget is sized for
+    static constexpr int THREADS = WM * WN * 64;
+    static constexpr int ROWB = BK * 2;     // bytes of one staged row (16-bit elements)
+    static constexpr int CPR = ROWB / 16;   // 16-byte chunks per staged row
+    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+};
+typedef TileCfg<RUDNN_GATE_UP_TILE> GateUpCfg;
+typedef TileCfg<RUDNN_DOWN_TILE> DownCfg;
+
+// Staged rows hold CPR 16-byte chunks; chunk c of row r is stored at c ^ swz(r).  MFMA operand
+// reads take one chunk from each of 32 consecutive rows.  With 128-byte rows the swizzle gives
+// any 8 consecutive aligned rows, and the even and the odd rows of any 16, eight different
+// chunk slots; with 64-byte rows the four rows of any 16 that share an LDS bank offset get
+// four different slots.  Either way the reads spread over all LDS banks.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    return CPR == 8 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Staging.  A tile step copies BM rows of tokens and NB = NSETS * BN weight rows, BK elements
+// each, straight from global memory into swizzled LDS (global_load_lds_dwordx4: lane i of a
+// wave writes 16 bytes at the wave's LDS base + 16 i, so one wave instruction fills 1 KiB =
+// 1024 / ROWB rows).  The copies of one step are numbered as slots (token groups first, then
+// weight groups) and dealt to the wavefronts round-robin, so each wave owns SLOTS copies.
+// A row past the end of its matrix re-reads the last row (such rows are never stored); in the
+// last step of a K that is not a multiple of BK, chunks at k >= K are zeroed instead of copied.
+// Offsets from a tile's base pointers are 32-bit: a tile spans at most a few MB of a matrix.
+struct StageSrc {
+    const unsigned char* a;   // token rows of the tile
+    const unsigned char* b0;  // weight rows (gate, or down)
+    const unsigned char* b1;  // up weight rows (gate_up only)
+    int ld_bytes, last_a, last_b, K, esize;
+};
+
+template <typename Cfg, int NSETS, int NWAVES, bool TAIL>
+__device__ __forceinline__ void stage_slot(int slot, unsigned char* st, const StageSrc& src, int k0, int wave,
+                                           int lane) {
+    constexpr int CPR = Cfg::CPR, RPG = 64 / CPR;  // rows per 1 KiB wave copy
+    constexpr int GA = Cfg::BM / RPG, GB = Cfg::BN / RPG;  // groups per region
+    static_assert(GA % NWAVES == 0 && GB % NWAVES == 0, "each region splits evenly over the wavefronts");
+    const int gi = wave + slot * NWAVES;  // global group index over A, B0, B1
+    // the region depends on the slot only (a constant once the slot loop is unrolled)
+    const unsigned char* base;
+    int g, last;
+    if (slot < GA / NWAVES) {
+        base = src.a, g = gi, last = src.last_a;
+    } else if (NSETS == 1 || slot < (GA + GB) / NWAVES) {
+        base = src.b0, g = gi - GA, last = src.last_b;
+    } else {
+        base = src.b1, g = gi - GA - GB, last = src.last_b;
+    }
+    const int r = g * RPG + lane / CPR;
+    const int kk = k0 + ((lane % CPR) ^ swz<CPR>(r)) * 8;
+    const int rr = r < last ? r : last;
+    unsigned char* dst = st + gi * 1024;
+    if (!TAIL || kk < src.K)
+        __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(rr * src.ld_bytes + kk * src.esize)),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    else
+        *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+}
+
+// Grouped GEMM on MFMA: for the tile's expert e, C[r, n] = sum_k A[r, k] B_e[n, k] over the
+// tile's rows; DUAL computes gate and up together and stores silu(gate) * up.
+template <typename T, bool DUAL, typename Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(const T* __restrict__ A,
+                                                                            const T* __restrict__ B0,
+                                                                            const T* __restrict__ B1,
+                                                                            T* __restrict__ C, int K, int N, int E,
+                                                                            Plan plan) {
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, STAGES = Cfg::STAGES;
+    constexpr int BK = Cfg::BK, ROWB = Cfg::ROWB, CPR = Cfg::CPR;
+    constexpr int NWAVES = WM * WN;
     constexpr int NSETS = DUAL ? 2 : 1;
-    constexpr int A_CHUNKS = BM * (MF_BK / 8) / MF_THREADS;  // 16-byte chunks per thread
-    constexpr int B_CHUNKS = NB * (MF_BK / 8) / MF_THREADS;
+    constexpr int NB = NSETS * BN;          // weight rows staged per tile
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int KS = BK / 16;             // MFMA steps per staged tile
+    constexpr int A_BYTES = BM * ROWB, STAGE_BYTES = (BM + NB) * ROWB;
+    constexpr int SLOTS = (BM + NB) * ROWB / 1024 / NWAVES;  // copies per wave per stage
+    static_assert((BM + NB) * ROWB % (1024 * NWAVES) == 0, "copies must split evenly over the wavefronts");
+    static_assert(BM * ROWB % 1024 == 0 && BN * ROWB % 1024 == 0, "regions are whole 1 KiB copies");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 MFMA blocks");
     typedef typename Mfma<T>::frag frag;
 
-    extern __shared__ __align__(16) unsigned char smem_raw[];
+    extern __shared__ __align__(1024) unsigned char smem_raw[];
     int* s_mt = reinterpret_cast<int*>(smem_raw);
     Tile tile;
     if (!find_tile<BM, BN>(plan, E, N, s_mt, tile)) return;
     __syncthreads();  // s_mt shares space with the stages
-    T* sA = reinterpret_cast<T*>(smem_raw);
-    T* sB = sA + 2 * BM * MF_PITCH;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave % MF_WM, wn = wave / MF_WM;
-    const int e = tile.e, nrows = tile.nrows, n0 = tile.n0;
-    const T* Ab = A + (int64_t)tile.row0 * K;
-    const T* B0e = B0 + (int64_t)e * N * K;
-    const T* B1e = DUAL ? B1 + (int64_t)e * N * K : nullptr;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
+    const int wm = wave % WM, wn = wave / WM;
+    const int nrows = tile.nrows, n0 = tile.n0;
+    StageSrc src;
+    src.a = reinterpret_cast<const unsigned char*>(A + (int64_t)tile.row0 * K);
+    src.b0 = reinterpret_cast<const unsigned char*>(B0 + ((int64_t)tile.e * N + n0) * K);
+    src.b1 = DUAL ? reinterpret_cast<const unsigned char*>(B1 + ((int64_t)tile.e * N + n0) * K) : nullptr;
+    src.ld_bytes = K * (int)sizeof(T);
+    src.last_a = nrows - 1;
+    src.last_b = N - 1 - n0;
+    src.K = K;
+    src.esize = (int)sizeof(T);
+    const int KT = (K + BK - 1) / BK;
+    const bool ragged_k = (K % BK) != 0;
 
-    uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-    auto load = [&](int k0) {
+    // all copies of step kt (the tail form zeroes chunks past K)
+    auto issue_all = [&](int kt) __attribute__((always_inline)) {
+        unsigned char* st = smem_raw + (kt % STAGES) * STAGE_BYTES;
+        if (ragged_k && kt == KT - 1) {
 #pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            const int q = tid + i * MF_THREADS, row = q >> 3, c = q & 7;
-            const int kk = k0 + c * 8;
-            ra[i] = (row < nrows && kk < K) ? *reinterpret_cast<const uint4*>(Ab + (int64_t)row * K + kk)
-                                            : make_uint4(0, 0, 0, 0);
-        }
+            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, NWAVES, true>(q, st, src, kt * BK, wave, lane);
+        } else {
 #pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i) {
-            const int q = tid + i * MF_THREADS, row = q >> 3, c = q & 7;
-            const int kk = k0 + c * 8;
-            const T* src = B0e;
-            int n = n0 + row;
-            if (DUAL && row >= BN) {
-                src = B1e;
-                n -= BN;
-            }
-            rb[i] = (n < N && kk < K) ? *reinterpret_cast<const uint4*>(src + (int64_t)n * K + kk)
-                                      : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store = [&](int stage) {
-        T* a = sA + stage * BM * MF_PITCH;
-        T* b = sB + stage * NB * MF_PITCH;
-#pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            const int q = tid + i * MF_THREADS, row = q >> 3, c = q & 7;
-            *reinterpret_cast<uint4*>(a + row * MF_PITCH + c * 8) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i) {
-            const int q = tid + i * MF_THREADS, row = q >> 3, c = q & 7;
-            *reinterpret_cast<uint4*>(b + row * MF_PITCH + c * 8) = rb[i];
+            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, NWAVES, false>(q, st, src, kt * BK, wave, lane);
         }
     };
 
@@ -208,44 +284,89 @@ __global__ __launch_bounds__(MF_THREADS) void grouped_gemm_mfma(const T* __restr
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[s][i][j][v] = 0.f;
 
-    // Rows of this wavefront that hold real tokens: skip the MFMAs of empty 32-row blocks.
+    // Rows of this wavefront that hold real tokens (a wavefront without any skips its MFMAs).
     const int wave_rows = min(max(nrows - wm * WTM, 0), WTM);
     const int fr = lane & 31, fh = lane >> 5;
+    int lane_off[KS];  // byte offset of this lane's 16-byte operand chunk in a 32-row block
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) lane_off[ks] = fr * ROWB + (((ks * 2 + fh) ^ swz<CPR>(fr)) * 16);
 
-    const int KT = (K + MF_BK - 1) / MF_BK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load((kt + 1) * MF_BK);
-        if (wave_rows > 0) {
-            const T* a = sA + cur * BM * MF_PITCH + (wm * WTM + fr) * MF_PITCH;
-            const T* b = sB + cur * NB * MF_PITCH + (wn * WTN + fr) * MF_PITCH;
+    // The MFMAs of one staged step.  Operand fragments of MFMA step ks+1 are read from LDS while
+    // the MFMAs of step ks run; with ISSUE, the copies of step kt_next are spread over the MFMA
+    // steps.  A scheduling fence after each MFMA step keeps at most two fragment sets live.
+    auto step = [&](int kt, auto with_mfma, auto with_issue, int kt_next) __attribute__((always_inline)) {
+        const unsigned char* st = smem_raw + (kt % STAGES) * STAGE_BYTES;
+        unsigned char* st_next = smem_raw + (kt_next % STAGES) * STAGE_BYTES;
+        const unsigned char* a = st + (wm * WTM) * ROWB;
+        const unsigned char* b = st + A_BYTES + (wn * WTN) * ROWB;
+        frag fa[2][FM], fb[2][NSETS][FN];
+        auto fetch = [&](int ks, int buf) __attribute__((always_inline)) {
 #pragma unroll
-            for (int ks = 0; ks < MF_BK / 16; ++ks) {
-                const int off = (ks * 2 + fh) * 8;
-                frag fa[FM], fb[NSETS][FN];
+            for (int i = 0; i < FM; ++i)
+                fa[buf][i] = *reinterpret_cast<const frag*>(a + i * 32 * ROWB + lane_off[ks]);
 #pragma unroll
-                for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const frag*>(a + i * 32 * MF_PITCH + off);
+            for (int s = 0; s < NSETS; ++s)
 #pragma unroll
-                for (int s = 0; s < NSETS; ++s)
+                for (int j = 0; j < FN; ++j)
+                    fb[buf][s][j] = *reinterpret_cast<const frag*>(b + (s * BN + j * 32) * ROWB + lane_off[ks]);
+        };
+        if constexpr (decltype(with_mfma)::value) fetch(0, 0);
 #pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        fb[s][j] = *reinterpret_cast<const frag*>(b + (s * BN + j * 32) * MF_PITCH + off);
+        for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (decltype(with_issue)::value) {
+                // copies for the next step go out early: spread over the first DMA_SPREAD MFMA steps
+                constexpr int SP = RUDNN_DMA_SPREAD < KS ? RUDNN_DMA_SPREAD : KS;
+                if (ks < SP) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i) {
-                    if (i * 32 >= wave_rows) continue;
+                    for (int q = ks * SLOTS / SP; q < (ks + 1) * SLOTS / SP; ++q)
+                        stage_slot<Cfg, NSETS, NWAVES, false>(q, st_next, src, kt_next * BK, wave, lane);
+                }
+            }
+            if constexpr (decltype(with_mfma)::value) {
+                if (ks + 1 < KS) fetch(ks + 1, (ks + 1) & 1);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int s = 0; s < NSETS; ++s)
 #pragma unroll
-                        for (int j = 0; j < FN; ++j) acc[s][i][j] = Mfma<T>::run(fa[i], fb[s][j], acc[s][i][j]);
-                }
+                        for (int j = 0; j < FN; ++j)
+                            acc[s][i][j] = Mfma<T>::run(fa[ks & 1][i], fb[ks & 1][s][j], acc[s][i][j]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (kt + 1 < KT) store(cur ^ 1);
-        __syncthreads();
-    }
+    };
+
+    // The K loop; a wavefront without rows only helps stage the tiles.  Three straight-line
+    // loops, so the accumulators stay in place: the steady state (copies of step kt+STAGES-1
+    // under the MFMAs of step kt), the step that issues a ragged last K tile, and the drain.
+    auto kloop = [&](auto with_mfma) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < KT) issue_all(s);
+        const int steady = KT - (STAGES - 1) - (ragged_k ? 1 : 0);
+        int kt = 0;
+        for (; kt < steady; ++kt) {
+            wait_vmcnt<(STAGES - 2) * SLOTS>();  // this wavefront's copies of step kt have landed
+            __syncthreads();  // everyone's copies of step kt landed; everyone is done with step kt-1
+            step(kt, with_mfma, std::true_type{}, kt + STAGES - 1);
+        }
+        if (ragged_k && KT >= STAGES) {  // kt == KT - STAGES: stage the ragged last tile
+            wait_vmcnt<(STAGES - 2) * SLOTS>();
+            __syncthreads();
+            issue_all(KT - 1);
+            step(kt, with_mfma, std::false_type{}, kt);
+            ++kt;
+        }
+        for (; kt < KT; ++kt) {
+            wait_vmcnt<0>();
+            __syncthreads();
+            step(kt, with_mfma, std::false_type{}, kt);
+        }
+    };
+    if (wave_rows > 0)
+        kloop(std::true_type{});
+    else
+        kloop(std::false_type{});
 
     // Epilogue.  32x32 MFMA output: lane l holds column l % 32 and rows
     // 8 * (v / 4) + 4 * (l / 32) + v % 4 for v = 0..15.
@@ -348,8 +469,9 @@ size_t experts_workspace_bytes(int64_t E, int64_t H, int64_t I, rudnn_moe_dtype 
     return align_up((size_t)rows * I * dtype_size(dt)) + align_up(sizeof(int32_t) * (3 * E + 1));
 }
 
-static size_t mfma_smem_bytes(bool dual, size_t es, int64_t E) {
-    const size_t stages = 2 * (size_t)(MF_BM + (dual ? 256 : 256)) * MF_PITCH * es;
+template <typename Cfg, bool DUAL>
+static size_t mfma_smem_bytes(int64_t E) {
+    const size_t stages = (size_t)Cfg::STAGES * (Cfg::BM + (DUAL ? 2 : 1) * Cfg::BN) * Cfg::ROWB;
     const size_t mt = sizeof(int) * (size_t)(E + 1);
     return stages > mt ? stages : mt;
 }
@@ -358,18 +480,19 @@ template <typename T>
 static void launch_mfma(const rudnn_moe_experts* ex, const void* disp, int64_t rows, void* out, void* h, Plan plan,
                         hipStream_t s) {
     const int E = (int)ex->num_experts, H = (int)ex->hidden, I = (int)ex->intermediate;
-    const int64_t mt = max_mtiles(rows, E, MF_BM);
+    const int64_t mt = max_mtiles(rows, E, GateUpCfg::BM);
     auto grid_for = [&](int N, int BN) {
         const int64_t tiles = mt * ((N + BN - 1) / BN);
         return (unsigned)((tiles + 7) / 8 * 8);
     };
-    const size_t es = sizeof(T);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
-    grouped_gemm_mfma<T, true><<<grid_for(I, 128), MF_THREADS, mfma_smem_bytes(true, es, E), s>>>(
+    grouped_gemm_mfma<T, true, GateUpCfg><<<grid_for(I, GateUpCfg::BN), GateUpCfg::THREADS,
+                                            mfma_smem_bytes<GateUpCfg, true>(E), s>>>(
         (const T*)disp, (const T*)ex->gate, (const T*)ex->up, (T*)h, H, I, E, plan);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
-    grouped_gemm_mfma<T, false><<<grid_for(H, 256), MF_THREADS, mfma_smem_bytes(false, es, E), s>>>(
+    grouped_gemm_mfma<T, false, DownCfg><<<grid_for(H, DownCfg::BN), DownCfg::THREADS,
+                                           mfma_smem_bytes<DownCfg, false>(E), s>>>(
         (const T*)h, (const T*)ex->down, nullptr, (T*)out, I, H, E, plan);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
 }
@@ -389,7 +512,19 @@ static void launch_f32(const rudnn_moe_experts* ex, const void* disp, int64_t ro
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
 }
 
-static bool smem_configured = false;
+// Dynamic LDS above 64 KiB per block has to be allowed per kernel (once per process).
+static std::once_flag g_smem_once;
+static void allow_large_lds() {
+    const int lds = 160 * 1024;
+    (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<bf16, true, GateUpCfg>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<bf16, false, DownCfg>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<f16, true, GateUpCfg>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<f16, false, DownCfg>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+}
 
 hipError_t launch_experts(const rudnn_moe_experts* ex, const void* disp, const int32_t* offsets, int64_t rows,
                           void* out, void* workspace, hipStream_t s) {
@@ -399,19 +534,9 @@ hipError_t launch_experts(const rudnn_moe_experts* ex, const void* disp, const i
     void* h = ws;
     int32_t* ints = (int32_t*)(ws + align_up((size_t)rows * I * es));
     Plan plan{ints, ints + E, ints + 2 * E};
-    if (!smem_configured) {
-        // LDS beyond 64 KiB per block must be requested explicitly.
-        hipFuncSetAttribute((const void*)grouped_gemm_mfma<bf16, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-        hipFuncSetAttribute((const void*)grouped_gemm_mfma<bf16, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-        hipFuncSetAttribute((const void*)grouped_gemm_mfma<f16, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-        hipFuncSetAttribute((const void*)grouped_gemm_mfma<f16, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-        smem_configured = true;
-    }
-    const int BM = ex->dtype == RUDNN_MOE_F32 ? F_BM : MF_BM;
+    std::call_once(g_smem_once, allow_large_lds);
+    static_assert(GateUpCfg::BM == DownCfg::BM, "both expert GEMMs share one tile plan");
+    const int BM = ex->dtype == RUDNN_MOE_F32 ? F_BM : GateUpCfg::BM;
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_PLAN, s);
     experts_plan_kernel<<<1, 1024, 0, s>>>(offsets, (int)E, (int)rows, BM, plan);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_PLAN, s);
