@@ -86,8 +86,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8,
-                    help="tokens of the layer the CPU oracle runs for the baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (sized from an 8-token probe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-stages", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -202,17 +202,21 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import oracle
-        n = args.cpu_sample_tokens
-        log("cpu baseline:", n, "tokens through the oracle")
         g_c, u_c, d_c = gate.cpu(), up.cpu(), down.cpu()
-        xs, ls = x[:n].cpu(), logits_cpu[:n]
+        x_c = x.cpu()
+        probe = 8
         t0 = time.perf_counter()
-        oracle.forward(xs, ls, k, renorm, g_c, u_c, d_c)
+        oracle.forward(x_c[:probe], logits_cpu[:probe], k, renorm, g_c, u_c, d_c)
+        per_token = (time.perf_counter() - t0) / probe
+        n = int(min(T, max(probe, args.cpu_seconds / per_token)))
+        log(f"cpu baseline: {n} tokens through the oracle (probe: {per_token * 1e3:.1f} ms/token)")
+        t0 = time.perf_counter()
+        oracle.forward(x_c[:n], logits_cpu[:n], k, renorm, g_c, u_c, d_c)
         dt = time.perf_counter() - t0
         cpu = {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"first {n} of the {T} tokens of the Mixtral-shaped layer, whole forward "
                          f"(route, dispatch, SwiGLU experts, combine) in the fp64 oracle; {dt:.1f} s"}
-        del g_c, u_c, d_c
+        del g_c, u_c, d_c, x_c
 
     # ---------------- HBM-bound stages on the routing+dispatch workload ----------------
     hbm = None
