@@ -8,6 +8,7 @@ namespace rudnn {
 
 typedef __bf16 bf16;
 typedef _Float16 f16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a 16-byte copy unit
 
 // Storage <-> fp32.  Narrowing rounds to nearest even (v_cvt_pk_bf16_f32 / v_cvt_f16_f32).
 __device__ __forceinline__ float to_f32(float v) { return v; }

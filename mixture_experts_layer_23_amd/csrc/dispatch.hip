@@ -1,20 +1,21 @@
 // dispatch.hip -- capacity-free grouping of tokens by expert (ruDNN user guide, section 5
 // "Expert weights and dispatch").
 //
-// The T*k (token, slot) pairs, flattened as a = t*k + j, are cut into chunks of
-// DISPATCH_CHUNK pairs.  Four kernels:
+// The T*k (token, slot) pairs, flattened as a = t*k + j, are cut into chunks of `chunk` pairs
+// (256..4096, see dispatch_chunk).  Four kernels:
 //   count  one block per chunk: LDS histogram of the chunk's expert ids, stored as
 //          chunk_counts[c, e] (every entry written, so nothing needs clearing first);
 //   scan   one block: per expert, the exclusive sum of its counts over the chunks (in place,
-//          turning counts into per-chunk bases), then the exclusive sum over experts ->
-//          expert_offsets[E+1];
+//          turning counts into per-chunk bases; the chunks are split over 1024 / E thread
+//          groups), then the exclusive sum over experts -> expert_offsets[E+1];
 //   rank   one block per chunk: the stable rank of each pair among the chunk's pairs of the
 //          same expert (wavefront ballots for lanes with equal ids, LDS counters across the
 //          block's waves and rounds); token_map[a] = offsets[e] + base[c, e] + rank.  Rows of
 //          an expert therefore follow (t, j) order, and the result does not depend on
 //          scheduling (no global atomics);
-//   copy   one wavefront per token: the token row is read from HBM once, in 16-byte vectors,
-//          and written to its k dispatched rows.
+//   copy   one wavefront per (token, 2 KiB piece of the row): the piece is read from HBM once
+//          in 16-byte vectors and written to the token's k dispatched rows (plain stores
+//          measured faster here than non-temporal ones).
 // HBM traffic: T*k*4 (ids, twice) + T*H*s (tokens, once) + T*k*H*s (rows) + T*k*4 (map).
 #include "device.hpp"
 #include "internal.hpp"
@@ -22,12 +23,12 @@
 namespace rudnn {
 
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const uint32_t* __restrict__ idx, int64_t pairs, int E,
-                                                             int32_t* __restrict__ chunk_counts) {
+                                                             int chunk, int32_t* __restrict__ chunk_counts) {
     extern __shared__ int hist[];
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
     __syncthreads();
-    const int64_t a0 = (int64_t)blockIdx.x * DISPATCH_CHUNK;
-    const int64_t a1 = min(pairs, a0 + DISPATCH_CHUNK);
+    const int64_t a0 = (int64_t)blockIdx.x * chunk;
+    const int64_t a1 = min(pairs, a0 + chunk);
     for (int64_t a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
         const uint32_t e = idx[a];
         if (e < (uint32_t)E) atomicAdd(&hist[e], 1);
@@ -39,23 +40,45 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const uint32_t* __r
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunks, int E,
                                                             int32_t* __restrict__ offsets) {
     __shared__ int scratch[17];
-    const int e = threadIdx.x;
-    int run = 0;
-    if (e < E) {
-        for (int c = 0; c < nchunks; ++c) {
+    __shared__ int part[1024];  // [group][expert] chunk-range totals, then their prefix
+    const int groups = max(1, min(1024 / E, nchunks));
+    const int per = (nchunks + groups - 1) / groups;
+    const int t = threadIdx.x, e = t % E, grp = t / E;
+    const bool active = grp < groups;
+    const int c0 = min(nchunks, grp * per), c1 = min(nchunks, c0 + per);
+    int sum = 0;
+    if (active) {
+#pragma unroll 8
+        for (int c = c0; c < c1; ++c) sum += chunk_counts[(int64_t)c * E + e];
+    }
+    if (active) part[grp * E + e] = sum;
+    __syncthreads();
+    int total = 0;
+    if (t < E) {  // exclusive prefix over the groups of expert t
+        for (int g = 0; g < groups; ++g) {
+            const int v = part[g * E + t];
+            part[g * E + t] = total;
+            total += v;
+        }
+    }
+    __syncthreads();
+    if (active) {  // per-chunk bases inside the expert, in place
+        int run = part[grp * E + e];
+#pragma unroll 8
+        for (int c = c0; c < c1; ++c) {
             const int n = chunk_counts[(int64_t)c * E + e];
             chunk_counts[(int64_t)c * E + e] = run;
             run += n;
         }
     }
-    int total;
-    const int excl = block_exclusive_scan(e < E ? run : 0, scratch, &total);
-    if (e < E) offsets[e] = excl;
-    if (e == 0) offsets[E] = total;
+    int grand;
+    const int excl = block_exclusive_scan(t < E ? total : 0, scratch, &grand);
+    if (t < E) offsets[t] = excl;
+    if (t == 0) offsets[E] = grand;
 }
 
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(const uint32_t* __restrict__ idx, int64_t pairs, int E,
-                                                            const int32_t* __restrict__ chunk_base,
+                                                            int chunk, const int32_t* __restrict__ chunk_base,
                                                             const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ token_map) {
     extern __shared__ int sm[];
@@ -65,8 +88,8 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const uint32_t* __re
     __syncthreads();
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int64_t a0 = (int64_t)blockIdx.x * DISPATCH_CHUNK;
-    const int64_t a1 = min(pairs, a0 + DISPATCH_CHUNK);
+    const int64_t a0 = (int64_t)blockIdx.x * chunk;
+    const int64_t a1 = min(pairs, a0 + chunk);
     const int32_t* base = chunk_base + (int64_t)blockIdx.x * E;
     for (int64_t r0 = a0; r0 < a1; r0 += blockDim.x) {
         const int64_t a = r0 + threadIdx.x;
@@ -104,31 +127,40 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const uint32_t* __re
     }
 }
 
-// One wavefront per token; V is the copy unit (16-byte vector when the row allows it).
-template <typename V, int UNROLL>
+// One wavefront per (token, piece of 64 * RUDNN_COPY_UNROLL copy units); V is the copy unit (a
+// 16-byte vector when the row allows it).
+#ifndef RUDNN_COPY_UNROLL
+#define RUDNN_COPY_UNROLL 2
+#endif
+#ifndef RUDNN_COPY_NT
+#define RUDNN_COPY_NT 0
+#endif
+template <typename V>
 __global__ __launch_bounds__(256) void dispatch_copy_kernel(const V* __restrict__ x, int64_t T, int k, int64_t row_units,
-                                                            const int32_t* __restrict__ token_map,
+                                                            int pieces, const int32_t* __restrict__ token_map,
                                                             V* __restrict__ out) {
+    constexpr int U = RUDNN_COPY_UNROLL;  // 64-unit pieces per wavefront
     const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t t = w / pieces;
     if (t >= T) return;
+    const int64_t i0 = (w - t * pieces) * 64 * U + lane;
     const int my_row = lane < k ? token_map[t * k + lane] : -1;
-    const V* src = x + t * row_units;
-    for (int64_t u0 = 0; u0 < row_units; u0 += 64 * UNROLL) {
-        V buf[UNROLL];
+    V v[U];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int64_t i = u0 + u * 64 + lane;
-            if (i < row_units) buf[u] = src[i];
-        }
-        for (int j = 0; j < k; ++j) {
-            const int dst = readlane(my_row, j);
-            if (dst < 0) continue;
-            V* d = out + (int64_t)dst * row_units;
+    for (int u = 0; u < U; ++u)
+        if (i0 + u * 64 < row_units) v[u] = x[t * row_units + i0 + u * 64];
+    for (int j = 0; j < k; ++j) {
+        const int dst = readlane(my_row, j);
+        if (dst < 0) continue;
+        V* d = out + (int64_t)dst * row_units;
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int64_t i = u0 + u * 64 + lane;
-                if (i < row_units) d[i] = buf[u];
+        for (int u = 0; u < U; ++u) {
+            if (i0 + u * 64 < row_units) {
+                if (RUDNN_COPY_NT)
+                    __builtin_nontemporal_store(v[u], d + i0 + u * 64);
+                else
+                    d[i0 + u * 64] = v[u];
             }
         }
     }
@@ -148,31 +180,35 @@ hipError_t launch_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E,
                            void* dispatched, int32_t* offsets, int32_t* token_map, int32_t* chunk_counts,
                            hipStream_t s) {
     const int64_t pairs = T * k;
+    const int chunk = (int)dispatch_chunk(pairs);
     const int nchunks = (int)dispatch_chunks(pairs);
     const int Ei = (int)E;
     timing_before(RUDNN_MOE_KERNEL_DISPATCH_COUNT, s);
-    dispatch_count_kernel<<<nchunks, 256, E * sizeof(int), s>>>(idx, pairs, Ei, chunk_counts);
+    dispatch_count_kernel<<<nchunks, 256, E * sizeof(int), s>>>(idx, pairs, Ei, chunk, chunk_counts);
     timing_after(RUDNN_MOE_KERNEL_DISPATCH_COUNT, s);
     timing_before(RUDNN_MOE_KERNEL_DISPATCH_SCAN, s);
     dispatch_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, nchunks, Ei, offsets);
     timing_after(RUDNN_MOE_KERNEL_DISPATCH_SCAN, s);
     timing_before(RUDNN_MOE_KERNEL_DISPATCH_RANK, s);
-    dispatch_rank_kernel<<<nchunks, 256, 5 * E * sizeof(int), s>>>(idx, pairs, Ei, chunk_counts, offsets, token_map);
+    dispatch_rank_kernel<<<nchunks, 256, 5 * E * sizeof(int), s>>>(idx, pairs, Ei, chunk, chunk_counts, offsets,
+                                                                    token_map);
     timing_after(RUDNN_MOE_KERNEL_DISPATCH_RANK, s);
-    const dim3 grid((unsigned)((T + 3) / 4)), block(256);
     const int ki = (int)k;
+    auto copy = [&](auto unit) {
+        typedef decltype(unit) V;
+        const int64_t units = (int64_t)(row_bytes / sizeof(V));
+        const int pieces = (int)((units + 64 * RUDNN_COPY_UNROLL - 1) / (64 * RUDNN_COPY_UNROLL));
+        const int64_t waves = T * pieces;
+        dispatch_copy_kernel<V><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>((const V*)input, T, ki, units, pieces,
+                                                                          token_map, (V*)dispatched);
+    };
     timing_before(RUDNN_MOE_KERNEL_DISPATCH_COPY, s);
     if (row_bytes % 16 == 0 && ((uintptr_t)input % 16) == 0 && ((uintptr_t)dispatched % 16) == 0)
-        dispatch_copy_kernel<uint4, 4><<<grid, block, 0, s>>>((const uint4*)input, T, ki, (int64_t)(row_bytes / 16),
-                                                              token_map, (uint4*)dispatched);
+        copy(u32x4{});
     else if (row_bytes % 4 == 0 && ((uintptr_t)input % 4) == 0 && ((uintptr_t)dispatched % 4) == 0)
-        dispatch_copy_kernel<uint32_t, 4><<<grid, block, 0, s>>>((const uint32_t*)input, T, ki,
-                                                                 (int64_t)(row_bytes / 4), token_map,
-                                                                 (uint32_t*)dispatched);
+        copy(uint32_t{});
     else
-        dispatch_copy_kernel<uint16_t, 4><<<grid, block, 0, s>>>((const uint16_t*)input, T, ki,
-                                                                 (int64_t)(row_bytes / 2), token_map,
-                                                                 (uint16_t*)dispatched);
+        copy(uint16_t{});
     timing_after(RUDNN_MOE_KERNEL_DISPATCH_COPY, s);
     return hipGetLastError();
 }

@@ -10,11 +10,23 @@
 
 namespace rudnn {
 
-// Dispatch works on chunks of DISPATCH_CHUNK consecutive (token, slot) pairs; one block of the
-// count and rank kernels owns one chunk.  Workspace: [nchunks, E] int32 per-chunk counts that
-// the scan kernel turns into per-chunk bases in place.
-constexpr int64_t DISPATCH_CHUNK = 4096;
-inline int64_t dispatch_chunks(int64_t pairs) { return (pairs + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK; }
+// Dispatch works on chunks of consecutive (token, slot) pairs; one block of the count and rank
+// kernels owns one chunk.  The chunk is 256..4096 pairs (a multiple of the 256-thread block),
+// about pairs / 512: enough blocks for the count and rank kernels, few enough chunks for the
+// one-block scan.  Workspace: [nchunks, E] int32 per-chunk counts that the scan kernel turns
+// into per-chunk bases in place.
+#ifndef RUDNN_DISPATCH_CHUNKS
+#define RUDNN_DISPATCH_CHUNKS 512
+#endif
+inline int64_t dispatch_chunk(int64_t pairs) {
+    int64_t c = 256;
+    while (c < 4096 && c * RUDNN_DISPATCH_CHUNKS < pairs) c *= 2;
+    return c;
+}
+inline int64_t dispatch_chunks(int64_t pairs) {
+    const int64_t c = dispatch_chunk(pairs);
+    return (pairs + c - 1) / c;
+}
 
 // Kernel limits (documented in rudnn_moe.h as RUDNN_MOE_ERR_UNSUPPORTED).
 constexpr int64_t MAX_EXPERTS = 1024;
