@@ -19,10 +19,10 @@
 //
 // Tile order.  Tiles of expert e are enumerated in groups of GROUP_N n-tiles, all m-tiles of a
 // group together, so tiles that run side by side share both their weight columns and their
-// token rows.  Workgroup i runs on XCD i % 8 (round-robin); block i therefore takes logical
-// tile (start of XCD i % 8's share) + i / 8, so each XCD walks a contiguous, equal share of
-// the tile list and its 4 MB L2 sees the reuse.  The grid is sized for the worst case
-// (floor(rows / BM) + min(E, rows) m-tiles); blocks beyond the real count exit at once.
+// token rows; block i takes tile i.  (Dealing contiguous shares of the list to the 8 XCDs,
+// RUDNN_XCD_REMAP, measured slower on the Mixtral-shaped layer and is off.)  The grid is
+// sized for the worst case (floor(rows / BM) + min(E, rows) m-tiles); blocks beyond the real
+// count exit at once.
 #include <mutex>
 #include <type_traits>
 
@@ -39,7 +39,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define RUDNN_DMA_SPREAD 2
 #endif
 #ifndef RUDNN_XCD_REMAP
-#define RUDNN_XCD_REMAP 1
+#define RUDNN_XCD_REMAP 0
 #endif
 #ifndef RUDNN_GROUP_N
 #define RUDNN_GROUP_N 4

@@ -241,6 +241,10 @@ SMALL_LAYERS = {
     "one_expert": Workload("one_expert", 300, 256, 512, 1, 1, "bf16", "bf16", (True,), None, 205),
     # top_k = E
     "topk_all": Workload("topk_all", 130, 128, 64, 4, 4, "f16", "f16", (False,), None, 206),
+    # few rows per expert and a long K (64 steps of 64)
+    "long_k": Workload("long_k", 64, 4096, 2048, 4, 2, "bf16", "bf16", (True,), None, 207),
+    # a long K that is not a multiple of the 64-element step, fp16
+    "long_ragged_k": Workload("long_ragged_k", 40, 4104, 1032, 3, 1, "f16", "f16", (True,), None, 208),
 }
 
 
