@@ -41,6 +41,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #ifndef RUDNN_XCD_REMAP
 #define RUDNN_XCD_REMAP 0
 #endif
+#ifndef RUDNN_COPY_WAVES
+#define RUDNN_COPY_WAVES 8
+#endif
+#ifndef RUDNN_COPY_HALF
+#define RUDNN_COPY_HALF 0
+#endif
+#ifndef RUDNN_SETPRIO
+#define RUDNN_SETPRIO 0
+#endif
 #ifndef RUDNN_GROUP_N
 #define RUDNN_GROUP_N 4
 #endif
@@ -206,6 +215,11 @@ __device__ __forceinline__ void stage_slot(int slot, unsigned char* st, const St
     } else {
         base = src.b1, g = gi - GA - GB, last = src.last_b;
     }
+    // A group of token rows wholly past the tile's last row is not copied: those LDS rows only
+    // feed output rows that are never stored (each output row depends on its own token row).
+    // Only with two stages, whose steps wait for every copy (vmcnt 0): with deeper pipelines
+    // the per-step copy counts that the waits assume must not vary.
+    if (Cfg::STAGES == 2 && slot < GA / NWAVES && g * RPG > last) return;
     const int r = g * RPG + lane / CPR;
     const int kk = k0 + ((lane % CPR) ^ swz<CPR>(r)) * 8;
     const int rr = r < last ? r : last;
@@ -234,8 +248,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int KS = BK / 16;             // MFMA steps per staged tile
     constexpr int A_BYTES = BM * ROWB, STAGE_BYTES = (BM + NB) * ROWB;
-    constexpr int SLOTS = (BM + NB) * ROWB / 1024 / NWAVES;  // copies per wave per stage
-    static_assert((BM + NB) * ROWB % (1024 * NWAVES) == 0, "copies must split evenly over the wavefronts");
+    constexpr int CW = RUDNN_COPY_WAVES;                      // wavefronts that issue the copies
+    constexpr int SLOTS = (BM + NB) * ROWB / 1024 / CW;       // copies per copying wave per stage
+    static_assert((BM + NB) * ROWB % (1024 * CW) == 0, "copies must split evenly over the wavefronts");
     static_assert(BM * ROWB % 1024 == 0 && BN * ROWB % 1024 == 0, "regions are whole 1 KiB copies");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 MFMA blocks");
     typedef typename Mfma<T>::frag frag;
@@ -248,7 +263,12 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
-    const int wm = wave % WM, wn = wave / WM;
+    // Wavefronts go to the four SIMDs of the CU round-robin (wave w on SIMD w % 4).  Neighbouring
+    // waves share a row band, so a tile with few rows still spreads its MFMAs over several SIMDs
+    // instead of stacking them on one (rows <= 64: two SIMDs, rows <= 128: all four).
+    const int wm = wave / WN, wn = wave % WN;
+    const bool copier = RUDNN_COPY_HALF ? (wave >= NWAVES - CW) : (wave < CW);
+    const int cwave = RUDNN_COPY_HALF ? wave - (NWAVES - CW) : wave;
     const int nrows = tile.nrows, n0 = tile.n0;
     StageSrc src;
     src.a = reinterpret_cast<const unsigned char*>(A + (int64_t)tile.row0 * K);
@@ -265,12 +285,13 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     // all copies of step kt (the tail form zeroes chunks past K)
     auto issue_all = [&](int kt) __attribute__((always_inline)) {
         unsigned char* st = smem_raw + (kt % STAGES) * STAGE_BYTES;
+        if (!copier) return;
         if (ragged_k && kt == KT - 1) {
 #pragma unroll
-            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, NWAVES, true>(q, st, src, kt * BK, wave, lane);
+            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, CW, true>(q, st, src, kt * BK, cwave, lane);
         } else {
 #pragma unroll
-            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, NWAVES, false>(q, st, src, kt * BK, wave, lane);
+            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, CW, false>(q, st, src, kt * BK, cwave, lane);
         }
     };
 
@@ -316,10 +337,12 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
             if constexpr (decltype(with_issue)::value) {
                 // copies for the next step go out early: spread over the first DMA_SPREAD MFMA steps
                 constexpr int SP = RUDNN_DMA_SPREAD < KS ? RUDNN_DMA_SPREAD : KS;
-                if (ks < SP) {
+                if (ks < SP && copier) {
+                    if (RUDNN_SETPRIO) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
                     for (int q = ks * SLOTS / SP; q < (ks + 1) * SLOTS / SP; ++q)
-                        stage_slot<Cfg, NSETS, NWAVES, false>(q, st_next, src, kt_next * BK, wave, lane);
+                        stage_slot<Cfg, NSETS, CW, false>(q, st_next, src, kt_next * BK, cwave, lane);
+                    if (RUDNN_SETPRIO) __builtin_amdgcn_s_setprio(0);
                 }
             }
             if constexpr (decltype(with_mfma)::value) {
@@ -330,7 +353,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
                     for (int s = 0; s < NSETS; ++s)
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
-                            acc[s][i][j] = Mfma<T>::run(fa[ks & 1][i], fb[ks & 1][s][j], acc[s][i][j]);
+                            acc[s][i][j] = Mfma<T>::run(fb[ks & 1][s][j], fa[ks & 1][i], acc[s][i][j]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -368,27 +391,46 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     else
         kloop(std::false_type{});
 
-    // Epilogue.  32x32 MFMA output: lane l holds column l % 32 and rows
-    // 8 * (v / 4) + 4 * (l / 32) + v % 4 for v = 0..15.
-    T* Cb = C + (int64_t)tile.row0 * N + n0;
+    // Epilogue.  The MFMAs take the weight fragment as their first operand, so each 32 x 32
+    // accumulator block is the transposed output: lane l holds token row l % 32 and output
+    // columns 8 * (v / 4) + 4 * (l / 32) + v % 4 for v = 0..15, i.e. four runs of four adjacent
+    // columns.  Each run goes to LDS as one 8-byte write into a row-major [BM][BN] tile (rows
+    // padded by 16 bytes), which is then stored to global memory in 16-byte pieces, whole rows per
+    // wavefront instruction.  N is a multiple of 8, so a piece lies wholly inside or outside it.
+    constexpr int PITCH = BN * (int)sizeof(T) + 16;  // bytes per staged output row
+    constexpr int CHUNKS = BN * (int)sizeof(T) / 16;  // 16-byte pieces per row
+    static_assert(BM * PITCH <= 160 * 1024, "output tile exceeds the LDS");
+    __syncthreads();  // every wavefront is done with the stages
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        const int row = wm * WTM + i * 32 + fr;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int col = wn * WTN + j * 32 + fr;
-            if (n0 + col >= N) continue;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
-                if (row >= nrows) continue;
-                float val;
-                if (DUAL)
-                    val = silu_f(acc[0][i][j][v]) * acc[NSETS - 1][i][j][v];
-                else
-                    val = acc[0][i][j][v];
-                Cb[(int64_t)row * N + col] = from_f32<T>(val);
+            for (int q = 0; q < 4; ++q) {
+                const int col = wn * WTN + j * 32 + 8 * q + 4 * fh;
+                T out[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int v = 4 * q + u;
+                    const float val = DUAL ? silu_f(acc[0][i][j][v]) * acc[NSETS - 1][i][j][v] : acc[0][i][j][v];
+                    out[u] = from_f32<T>(val);
+                }
+                uint2 packed;
+                __builtin_memcpy(&packed, out, sizeof(packed));
+                *reinterpret_cast<uint2*>(smem_raw + row * PITCH + col * (int)sizeof(T)) = packed;
             }
         }
+    }
+    __syncthreads();
+    T* Cb = C + (int64_t)tile.row0 * N + n0;
+    const int ncols = min(BN, N - n0);
+#pragma unroll 4
+    for (int p = tid; p < BM * CHUNKS; p += Cfg::THREADS) {
+        const int row = p / CHUNKS, ch = p % CHUNKS;
+        if (row < nrows && ch * 8 < ncols)
+            *reinterpret_cast<uint4*>(Cb + (int64_t)row * N + ch * 8) =
+                *reinterpret_cast<const uint4*>(smem_raw + row * PITCH + ch * 16);
     }
 }
 
@@ -472,8 +514,10 @@ size_t experts_workspace_bytes(int64_t E, int64_t H, int64_t I, rudnn_moe_dtype 
 template <typename Cfg, bool DUAL>
 static size_t mfma_smem_bytes(int64_t E) {
     const size_t stages = (size_t)Cfg::STAGES * (Cfg::BM + (DUAL ? 2 : 1) * Cfg::BN) * Cfg::ROWB;
+    const size_t out_tile = (size_t)Cfg::BM * (Cfg::BN * 2 + 16);  // staged 16-bit output rows
     const size_t mt = sizeof(int) * (size_t)(E + 1);
-    return stages > mt ? stages : mt;
+    size_t bytes = stages > mt ? stages : mt;
+    return bytes > out_tile ? bytes : out_tile;
 }
 
 template <typename T>
@@ -516,6 +560,7 @@ static void launch_f32(const rudnn_moe_experts* ex, const void* disp, int64_t ro
 static std::once_flag g_smem_once;
 static void allow_large_lds() {
     const int lds = 160 * 1024;
+
     (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<bf16, true, GateUpCfg>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<bf16, false, DownCfg>,
