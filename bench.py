@@ -185,6 +185,7 @@ def main():
         "experts_gate_up": {"us": stage_ms["experts_gate_up"] * 1e3, "flops": gu_flops},
         "experts_down": {"us": stage_ms["experts_down"] * 1e3, "flops": dn_flops},
         "experts_plan": {"us": stage_ms["experts_plan"] * 1e3},
+        "experts_split_reduce": {"us": (stage_ms["experts_gate_up_reduce"] + stage_ms["experts_down_reduce"]) * 1e3},
         "combine": {"us": stage_ms["combine"] * 1e3, "bytes": T * k * H * s + T * k * (s + 4) + T * H * s},
     }
     for v in stages.values():
@@ -194,7 +195,7 @@ def main():
         if "flops" in v:
             v["TFLOPps"] = v["flops"] / (v["us"] / 1e6) / 1e12
             v["mfma_frac"] = v["TFLOPps"] / MFMA_PEAK_TFLOPS[w.dtype]
-    experts_us = stages["experts_gate_up"]["us"] + stages["experts_down"]["us"] + stages["experts_plan"]["us"]
+    experts_us = sum(stages[n]["us"] for n in ("experts_gate_up", "experts_down", "experts_plan", "experts_split_reduce"))
     stages["experts_total"] = {"us": experts_us, "TFLOPps": (gu_flops + dn_flops) / (experts_us / 1e6) / 1e12}
     stages["experts_total"]["mfma_frac"] = stages["experts_total"]["TFLOPps"] / MFMA_PEAK_TFLOPS[w.dtype]
 

@@ -190,7 +190,9 @@ typedef enum {
     RUDNN_MOE_KERNEL_EXPERTS_GATE_UP = 6,
     RUDNN_MOE_KERNEL_EXPERTS_DOWN = 7,
     RUDNN_MOE_KERNEL_COMBINE = 8,
-    RUDNN_MOE_KERNEL_COUNT = 9
+    RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE = 9, /* sums the K-split partials of gate_up tail tiles */
+    RUDNN_MOE_KERNEL_EXPERTS_DOWN_REDUCE = 10,   /* the same for down */
+    RUDNN_MOE_KERNEL_COUNT = 11
 } rudnn_moe_kernel;
 
 /* For the calling host thread: record `before` on the launch stream immediately before the

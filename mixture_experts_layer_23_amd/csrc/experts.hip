@@ -19,10 +19,16 @@
 //
 // Tile order.  Tiles of expert e are enumerated in groups of GROUP_N n-tiles, all m-tiles of a
 // group together, so tiles that run side by side share both their weight columns and their
-// token rows; block i takes tile i.  (Dealing contiguous shares of the list to the 8 XCDs,
-// RUDNN_XCD_REMAP, measured slower on the Mixtral-shaped layer and is off.)  The grid is
-// sized for the worst case (floor(rows / BM) + min(E, rows) m-tiles); blocks beyond the real
+// token rows; block i takes tile i.  (Dealing contiguous shares of the list to the 8 XCDs
+// measured slower on the Mixtral-shaped layer.)  The grid is sized for the worst case
+// (floor(rows / BM) + min(E, rows) m-tiles, plus the split units below); blocks beyond the real
 // count exit at once.
+//
+// Tail split.  Tiles run one per CU in rounds; when the tile count leaves a last, partial round
+// of R tiles, each of those R tiles is cut along K into S segments (S = CUs / R, at most
+// SPLIT_SLOTS / R, each at least SPLIT_MIN_STEPS K steps), so the last round fills the machine.
+// A segment stores its FP32 partial sums; a small reduce kernel then adds the S partials of each
+// split tile in segment order (deterministic) and applies the epilogue.
 #include <mutex>
 #include <type_traits>
 
@@ -38,8 +44,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #ifndef RUDNN_DMA_SPREAD
 #define RUDNN_DMA_SPREAD 2
 #endif
-#ifndef RUDNN_XCD_REMAP
-#define RUDNN_XCD_REMAP 0
+#ifndef RUDNN_SPLIT_MIN_STEPS
+#define RUDNN_SPLIT_MIN_STEPS 8
 #endif
 #ifndef RUDNN_COPY_WAVES
 #define RUDNN_COPY_WAVES 8
@@ -54,6 +60,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define RUDNN_GROUP_N 4
 #endif
 constexpr int GROUP_N = RUDNN_GROUP_N;  // n-tiles scheduled together (see "Tile order")
+constexpr int SPLIT_SLOTS = 256;        // partial-sum slots of the tail split (see "Tail split")
 
 // ---------------------------------------------------------------------------------------
 // plan
@@ -87,19 +94,16 @@ struct Tile {
     int e, row0, nrows, n0;
 };
 
-// Maps this block to a tile; false if the block has no tile.  `s_mt` is __shared__ int[E+1].
-template <int BM, int BN>
-__device__ __forceinline__ bool find_tile(const Plan& plan, int E, int N, int* s_mt, Tile& t) {
+// Loads the tile plan into LDS (`s_mt` is __shared__ int[E+1]) and returns the tile count.
+__device__ __forceinline__ int64_t load_plan(const Plan& plan, int E, int NT, int* s_mt) {
     for (int i = threadIdx.x; i <= E; i += blockDim.x) s_mt[i] = plan.mt_begin[i];
     __syncthreads();
-    const int NT = (N + BN - 1) / BN;
-    const int64_t total = (int64_t)s_mt[E] * NT;
-    const int xcd = RUDNN_XCD_REMAP ? (blockIdx.x & 7) : 0;
-    const int64_t slot = RUDNN_XCD_REMAP ? (blockIdx.x >> 3) : blockIdx.x;
-    const int64_t q = RUDNN_XCD_REMAP ? (total >> 3) : total, r = RUDNN_XCD_REMAP ? (total & 7) : 0;
-    const int64_t count = q + (xcd < r ? 1 : 0);
-    if (slot >= count) return false;
-    const int64_t L = xcd * q + min((int64_t)xcd, r) + slot;
+    return (int64_t)s_mt[E] * NT;
+}
+
+// Tile L of the list (see "Tile order").
+template <int BM, int BN>
+__device__ __forceinline__ void decode_tile(const Plan& plan, const int* s_mt, int E, int NT, int64_t L, Tile& t) {
     const int64_t M = L / NT;  // the expert owns m-tile rows [s_mt[e], s_mt[e+1])
     int lo = 0, hi = E - 1;    // largest e with s_mt[e] <= M
     while (lo < hi) {
@@ -121,6 +125,63 @@ __device__ __forceinline__ bool find_tile(const Plan& plan, int E, int N, int* s
     t.row0 = plan.row_begin[e] + mt * BM;
     t.nrows = min(BM, plan.row_count[e] - mt * BM);
     t.n0 = nt * BN;
+}
+
+// The tail split (see "Tail split"): the last R tiles of the list are cut into S segments each.
+struct Split {
+    int64_t full;  // tiles run whole
+    int R, S;      // split tiles, segments per split tile (R = 0, S = 1: no split)
+};
+
+__device__ __forceinline__ Split split_plan(int64_t tiles, int KT, int cus) {
+    Split sp;
+    int64_t R = tiles >= cus ? tiles % cus : tiles;
+    int S = R > 0 ? (int)min((int64_t)cus / R, (int64_t)SPLIT_SLOTS / R) : 1;
+    S = min(S, KT / RUDNN_SPLIT_MIN_STEPS);
+    if (S < 2) S = 1, R = 0;
+    sp.full = tiles - R;
+    sp.R = (int)R;
+    sp.S = S;
+    return sp;
+}
+
+// This block's work: a whole tile (slot -1) or segment `seg` of a split tile, which leaves its
+// partial sums in partial slot `slot`.  False if the block has no work.
+struct Unit {
+    int kb, ke;  // K steps [kb, ke)
+    int slot;    // partial slot, -1 for a whole tile
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ bool find_unit(const Plan& plan, int E, int N, int KT, int cus, int* s_mt, Tile& t,
+                                          Unit& u) {
+    const int NT = (N + BN - 1) / BN;
+    const int64_t tiles = load_plan(plan, E, NT, s_mt);
+    const Split sp = split_plan(tiles, KT, cus);
+    const int64_t U = blockIdx.x;
+    int64_t L;
+    if (U < sp.full) {
+        L = U, u.kb = 0, u.ke = KT, u.slot = -1;
+    } else {
+        const int64_t v = U - sp.full;
+        if (v >= (int64_t)sp.R * sp.S) return false;
+        const int seg = (int)(v % sp.S);
+        L = sp.full + v / sp.S;
+        u.kb = (int)((int64_t)seg * KT / sp.S);
+        u.ke = (int)((int64_t)(seg + 1) * KT / sp.S);
+        u.slot = (int)v;
+    }
+    decode_tile<BM, BN>(plan, s_mt, E, NT, L, t);
+    return true;
+}
+
+// Whole tiles only (the FP32 path).
+template <int BM, int BN>
+__device__ __forceinline__ bool find_tile(const Plan& plan, int E, int N, int* s_mt, Tile& t) {
+    const int NT = (N + BN - 1) / BN;
+    const int64_t tiles = load_plan(plan, E, NT, s_mt);
+    if ((int64_t)blockIdx.x >= tiles) return false;
+    decode_tile<BM, BN>(plan, s_mt, E, NT, blockIdx.x, t);
     return true;
 }
 
@@ -238,7 +299,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
                                                                             const T* __restrict__ B0,
                                                                             const T* __restrict__ B1,
                                                                             T* __restrict__ C, int K, int N, int E,
-                                                                            Plan plan) {
+                                                                            Plan plan, int cus,
+                                                                            float* __restrict__ partials) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, STAGES = Cfg::STAGES;
     constexpr int BK = Cfg::BK, ROWB = Cfg::ROWB, CPR = Cfg::CPR;
     constexpr int NWAVES = WM * WN;
@@ -257,8 +319,10 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
 
     extern __shared__ __align__(1024) unsigned char smem_raw[];
     int* s_mt = reinterpret_cast<int*>(smem_raw);
+    const int KT = (K + BK - 1) / BK;
     Tile tile;
-    if (!find_tile<BM, BN>(plan, E, N, s_mt, tile)) return;
+    Unit unit;
+    if (!find_unit<BM, BN>(plan, E, N, KT, cus, s_mt, tile, unit)) return;
     __syncthreads();  // s_mt shares space with the stages
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -279,7 +343,6 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     src.last_b = N - 1 - n0;
     src.K = K;
     src.esize = (int)sizeof(T);
-    const int KT = (K + BK - 1) / BK;
     const bool ragged_k = (K % BK) != 0;
 
     // all copies of step kt (the tail form zeroes chunks past K)
@@ -359,28 +422,31 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
         }
     };
 
-    // The K loop; a wavefront without rows only helps stage the tiles.  Three straight-line
-    // loops, so the accumulators stay in place: the steady state (copies of step kt+STAGES-1
-    // under the MFMAs of step kt), the step that issues a ragged last K tile, and the drain.
+    // The K loop over this unit's steps [kb, ke); a wavefront without rows only helps stage the
+    // tiles.  Three straight-line loops, so the accumulators stay in place: the steady state
+    // (copies of step kt+STAGES-1 under the MFMAs of step kt), the step that issues a ragged last
+    // K tile, and the drain.
+    const int kb = unit.kb, ke = unit.ke;
+    const bool last_ragged = ragged_k && ke == KT;
     auto kloop = [&](auto with_mfma) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
-            if (s < KT) issue_all(s);
-        const int steady = KT - (STAGES - 1) - (ragged_k ? 1 : 0);
-        int kt = 0;
+            if (kb + s < ke) issue_all(kb + s);
+        const int steady = ke - (STAGES - 1) - (last_ragged ? 1 : 0);
+        int kt = kb;
         for (; kt < steady; ++kt) {
             wait_vmcnt<(STAGES - 2) * SLOTS>();  // this wavefront's copies of step kt have landed
             __syncthreads();  // everyone's copies of step kt landed; everyone is done with step kt-1
             step(kt, with_mfma, std::true_type{}, kt + STAGES - 1);
         }
-        if (ragged_k && KT >= STAGES) {  // kt == KT - STAGES: stage the ragged last tile
+        if (last_ragged && ke - kb >= STAGES) {  // kt == ke - STAGES: stage the ragged last tile
             wait_vmcnt<(STAGES - 2) * SLOTS>();
             __syncthreads();
-            issue_all(KT - 1);
+            issue_all(ke - 1);
             step(kt, with_mfma, std::false_type{}, kt);
             ++kt;
         }
-        for (; kt < KT; ++kt) {
+        for (; kt < ke; ++kt) {
             wait_vmcnt<0>();
             __syncthreads();
             step(kt, with_mfma, std::false_type{}, kt);
@@ -397,6 +463,29 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     // columns.  Each run goes to LDS as one 8-byte write into a row-major [BM][BN] tile (rows
     // padded by 16 bytes), which is then stored to global memory in 16-byte pieces, whole rows per
     // wavefront instruction.  N is a multiple of 8, so a piece lies wholly inside or outside it.
+    if (unit.slot >= 0) {
+        // a segment of a split tile: FP32 partial sums, [slot][BM][NSETS * BN], rows past the
+        // tile and columns past N left unwritten (the reduce kernel never reads them)
+        float* P = partials + (int64_t)unit.slot * BM * NB;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WTM + i * 32 + fr;
+            if (row >= nrows) continue;
+#pragma unroll
+            for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = wn * WTN + j * 32 + 8 * q + 4 * fh;
+                        if (n0 + col >= N) continue;
+                        float4 v4 = make_float4(acc[s][i][j][4 * q], acc[s][i][j][4 * q + 1], acc[s][i][j][4 * q + 2],
+                                                acc[s][i][j][4 * q + 3]);
+                        *reinterpret_cast<float4*>(P + (int64_t)row * NB + s * BN + col) = v4;
+                    }
+        }
+        return;
+    }
     constexpr int PITCH = BN * (int)sizeof(T) + 16;  // bytes per staged output row
     constexpr int CHUNKS = BN * (int)sizeof(T) / 16;  // 16-byte pieces per row
     static_assert(BM * PITCH <= 160 * 1024, "output tile exceeds the LDS");
@@ -431,6 +520,44 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
         if (row < nrows && ch * 8 < ncols)
             *reinterpret_cast<uint4*>(Cb + (int64_t)row * N + ch * 8) =
                 *reinterpret_cast<const uint4*>(smem_raw + row * PITCH + ch * 16);
+    }
+}
+
+// Adds the S partials of every split tile in segment order and applies the epilogue (silu(g) * u
+// for gate_up); one thread per 8 output columns of a row.
+template <typename T, bool DUAL, typename Cfg>
+__global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ partials, T* __restrict__ C, int K,
+                                                     int N, int E, Plan plan, int cus) {
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, NSETS = DUAL ? 2 : 1, NB = NSETS * BN;
+    __shared__ int s_mt[MAX_EXPERTS + 1];
+    const int NT = (N + BN - 1) / BN;
+    const int KT = (K + Cfg::BK - 1) / Cfg::BK;
+    const Split sp = split_plan(load_plan(plan, E, NT, s_mt), KT, cus);
+    const int64_t items = (int64_t)sp.R * BM * (BN / 8);
+    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (int64_t)gridDim.x * blockDim.x) {
+        const int c8 = (int)(it % (BN / 8));
+        const int row = (int)(it / (BN / 8) % BM);
+        const int r = (int)(it / ((int64_t)BM * (BN / 8)));
+        Tile t;
+        decode_tile<BM, BN>(plan, s_mt, E, NT, sp.full + r, t);
+        const int col = c8 * 8;
+        if (row >= t.nrows || t.n0 + col >= N) continue;
+        float g[8] = {}, u[8] = {};
+        for (int seg = 0; seg < sp.S; ++seg) {
+            const float* P = partials + ((int64_t)(r * sp.S + seg) * BM + row) * NB + col;
+            const float4 a0 = *reinterpret_cast<const float4*>(P), a1 = *reinterpret_cast<const float4*>(P + 4);
+            g[0] += a0.x, g[1] += a0.y, g[2] += a0.z, g[3] += a0.w, g[4] += a1.x, g[5] += a1.y, g[6] += a1.z, g[7] += a1.w;
+            if (DUAL) {
+                const float4 b0 = *reinterpret_cast<const float4*>(P + BN), b1 = *reinterpret_cast<const float4*>(P + BN + 4);
+                u[0] += b0.x, u[1] += b0.y, u[2] += b0.z, u[3] += b0.w, u[4] += b1.x, u[5] += b1.y, u[6] += b1.z, u[7] += b1.w;
+            }
+        }
+        T out[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) out[q] = from_f32<T>(DUAL ? silu_f(g[q]) * u[q] : g[q]);
+        uint4 packed;
+        __builtin_memcpy(&packed, out, sizeof(packed));
+        *reinterpret_cast<uint4*>(C + (int64_t)(t.row0 + row) * N + t.n0 + col) = packed;
     }
 }
 
@@ -506,9 +633,29 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
 // ---------------------------------------------------------------------------------------
 static int64_t max_mtiles(int64_t rows, int64_t E, int BM) { return rows / BM + (E < rows ? E : rows); }
 
+// Partial-sum slots of the tail split: SPLIT_SLOTS x BM x 256 FP32 (both GEMMs stage 256
+// accumulator columns per tile).
+static size_t split_partials_bytes(rudnn_moe_dtype dt) {
+    static_assert(GateUpCfg::BN * 2 == 256 && DownCfg::BN == 256, "partial slots hold 256 columns");
+    return dt == RUDNN_MOE_F32 ? 0 : (size_t)SPLIT_SLOTS * GateUpCfg::BM * 256 * sizeof(float);
+}
+
 size_t experts_workspace_bytes(int64_t E, int64_t H, int64_t I, rudnn_moe_dtype dt, int64_t rows) {
     (void)H;
-    return align_up((size_t)rows * I * dtype_size(dt)) + align_up(sizeof(int32_t) * (3 * E + 1));
+    return align_up((size_t)rows * I * dtype_size(dt)) + align_up(sizeof(int32_t) * (3 * E + 1)) +
+           split_partials_bytes(dt);
+}
+
+// Compute units of the current device (the size of one round of tiles).
+static int device_cus() {
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev < 64) cache[dev] = cus;
+    return cus;
 }
 
 template <typename Cfg, bool DUAL>
@@ -522,23 +669,31 @@ static size_t mfma_smem_bytes(int64_t E) {
 
 template <typename T>
 static void launch_mfma(const rudnn_moe_experts* ex, const void* disp, int64_t rows, void* out, void* h, Plan plan,
-                        hipStream_t s) {
+                        float* partials, hipStream_t s) {
     const int E = (int)ex->num_experts, H = (int)ex->hidden, I = (int)ex->intermediate;
     const int64_t mt = max_mtiles(rows, E, GateUpCfg::BM);
+    const int cus = device_cus();
+    // every tile, plus at most SPLIT_SLOTS segments of split tiles
     auto grid_for = [&](int N, int BN) {
-        const int64_t tiles = mt * ((N + BN - 1) / BN);
-        return (unsigned)((tiles + 7) / 8 * 8);
+        const int64_t units = mt * ((N + BN - 1) / BN) + SPLIT_SLOTS;
+        return (unsigned)((units + 7) / 8 * 8);
     };
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
     grouped_gemm_mfma<T, true, GateUpCfg><<<grid_for(I, GateUpCfg::BN), GateUpCfg::THREADS,
                                             mfma_smem_bytes<GateUpCfg, true>(E), s>>>(
-        (const T*)disp, (const T*)ex->gate, (const T*)ex->up, (T*)h, H, I, E, plan);
+        (const T*)disp, (const T*)ex->gate, (const T*)ex->up, (T*)h, H, I, E, plan, cus, partials);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
+    timing_before(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE, s);
+    splitk_reduce<T, true, GateUpCfg><<<256, 256, 0, s>>>(partials, (T*)h, H, I, E, plan, cus);
+    timing_after(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
     grouped_gemm_mfma<T, false, DownCfg><<<grid_for(H, DownCfg::BN), DownCfg::THREADS,
                                            mfma_smem_bytes<DownCfg, false>(E), s>>>(
-        (const T*)h, (const T*)ex->down, nullptr, (T*)out, I, H, E, plan);
+        (const T*)h, (const T*)ex->down, nullptr, (T*)out, I, H, E, plan, cus, partials);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
+    timing_before(RUDNN_MOE_KERNEL_EXPERTS_DOWN_REDUCE, s);
+    splitk_reduce<T, false, DownCfg><<<256, 256, 0, s>>>(partials, (T*)out, I, H, E, plan, cus);
+    timing_after(RUDNN_MOE_KERNEL_EXPERTS_DOWN_REDUCE, s);
 }
 
 static void launch_f32(const rudnn_moe_experts* ex, const void* disp, int64_t rows, void* out, void* h, Plan plan,
@@ -585,10 +740,11 @@ hipError_t launch_experts(const rudnn_moe_experts* ex, const void* disp, const i
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_PLAN, s);
     experts_plan_kernel<<<1, 1024, 0, s>>>(offsets, (int)E, (int)rows, BM, plan);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_PLAN, s);
+    float* partials = (float*)(ws + align_up((size_t)rows * I * es) + align_up(sizeof(int32_t) * (3 * E + 1)));
     switch (ex->dtype) {
     case RUDNN_MOE_F32: launch_f32(ex, disp, rows, out, h, plan, s); break;
-    case RUDNN_MOE_F16: launch_mfma<f16>(ex, disp, rows, out, h, plan, s); break;
-    default: launch_mfma<bf16>(ex, disp, rows, out, h, plan, s); break;
+    case RUDNN_MOE_F16: launch_mfma<f16>(ex, disp, rows, out, h, plan, partials, s); break;
+    default: launch_mfma<bf16>(ex, disp, rows, out, h, plan, partials, s); break;
     }
     return hipGetLastError();
 }

@@ -25,7 +25,7 @@ STATUS = {0: "ok", 1: "shape", 2: "dtype", 3: "argument", 4: "device", 5: "unsup
           7: "runtime"}
 
 KERNELS = ("route", "dispatch_count", "dispatch_scan", "dispatch_rank", "dispatch_copy", "experts_plan",
-           "experts_gate_up", "experts_down", "combine")
+           "experts_gate_up", "experts_down", "combine", "experts_gate_up_reduce", "experts_down_reduce")
 
 
 class MoeError(RuntimeError):

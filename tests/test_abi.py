@@ -153,6 +153,6 @@ def test_forward_validation(L):
 
 
 def test_timing_hook_validation(L):
-    assert L.rudnn_moe_time_next_launch(9, None, None) == ARGUMENT
+    assert L.rudnn_moe_time_next_launch(11, None, None) == ARGUMENT
     assert L.rudnn_moe_time_next_launch(-1, None, None) == ARGUMENT
     assert L.rudnn_moe_time_next_launch(0, None, None) == OK
