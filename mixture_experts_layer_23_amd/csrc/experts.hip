@@ -524,33 +524,38 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
 }
 
 // Adds the S partials of every split tile in segment order and applies the epilogue (silu(g) * u
-// for gate_up); one thread per 8 output columns of a row.
+// for gate_up).  A block takes a slab of 2048 / BN rows of one split tile (the tile is decoded
+// once per slab); a thread takes 8 output columns of one row.
 template <typename T, bool DUAL, typename Cfg>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ partials, T* __restrict__ C, int K,
                                                      int N, int E, Plan plan, int cus) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, NSETS = DUAL ? 2 : 1, NB = NSETS * BN;
+    constexpr int CPRW = BN / 8, SLAB = 256 / CPRW;  // 8-column chunks per row, rows per slab
+    static_assert(BM % SLAB == 0, "slabs tile the rows");
     __shared__ int s_mt[MAX_EXPERTS + 1];
     const int NT = (N + BN - 1) / BN;
     const int KT = (K + Cfg::BK - 1) / Cfg::BK;
     const Split sp = split_plan(load_plan(plan, E, NT, s_mt), KT, cus);
-    const int64_t items = (int64_t)sp.R * BM * (BN / 8);
-    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (int64_t)gridDim.x * blockDim.x) {
-        const int c8 = (int)(it % (BN / 8));
-        const int row = (int)(it / (BN / 8) % BM);
-        const int r = (int)(it / ((int64_t)BM * (BN / 8)));
+    const int slabs = sp.R * (BM / SLAB);
+    for (int b = blockIdx.x; b < slabs; b += gridDim.x) {
+        const int r = b / (BM / SLAB);
         Tile t;
         decode_tile<BM, BN>(plan, s_mt, E, NT, sp.full + r, t);
-        const int col = c8 * 8;
+        const int row = (b % (BM / SLAB)) * SLAB + threadIdx.x / CPRW;
+        const int col = (threadIdx.x % CPRW) * 8;
         if (row >= t.nrows || t.n0 + col >= N) continue;
+        const float* P = partials + ((int64_t)r * sp.S * BM + row) * NB + col;
+        const int64_t seg_stride = (int64_t)BM * NB;
         float g[8] = {}, u[8] = {};
+        auto add = [&](const float* q, float* acc) __attribute__((always_inline)) {
+            const float4 x0 = *reinterpret_cast<const float4*>(q), x1 = *reinterpret_cast<const float4*>(q + 4);
+            acc[0] += x0.x, acc[1] += x0.y, acc[2] += x0.z, acc[3] += x0.w;
+            acc[4] += x1.x, acc[5] += x1.y, acc[6] += x1.z, acc[7] += x1.w;
+        };
+#pragma unroll 4
         for (int seg = 0; seg < sp.S; ++seg) {
-            const float* P = partials + ((int64_t)(r * sp.S + seg) * BM + row) * NB + col;
-            const float4 a0 = *reinterpret_cast<const float4*>(P), a1 = *reinterpret_cast<const float4*>(P + 4);
-            g[0] += a0.x, g[1] += a0.y, g[2] += a0.z, g[3] += a0.w, g[4] += a1.x, g[5] += a1.y, g[6] += a1.z, g[7] += a1.w;
-            if (DUAL) {
-                const float4 b0 = *reinterpret_cast<const float4*>(P + BN), b1 = *reinterpret_cast<const float4*>(P + BN + 4);
-                u[0] += b0.x, u[1] += b0.y, u[2] += b0.z, u[3] += b0.w, u[4] += b1.x, u[5] += b1.y, u[6] += b1.z, u[7] += b1.w;
-            }
+            add(P + seg * seg_stride, g);
+            if (DUAL) add(P + seg * seg_stride + BN, u);
         }
         T out[8];
 #pragma unroll
@@ -684,7 +689,7 @@ static void launch_mfma(const rudnn_moe_experts* ex, const void* disp, int64_t r
         (const T*)disp, (const T*)ex->gate, (const T*)ex->up, (T*)h, H, I, E, plan, cus, partials);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE, s);
-    splitk_reduce<T, true, GateUpCfg><<<256, 256, 0, s>>>(partials, (T*)h, H, I, E, plan, cus);
+    splitk_reduce<T, true, GateUpCfg><<<1024, 256, 0, s>>>(partials, (T*)h, H, I, E, plan, cus);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
     grouped_gemm_mfma<T, false, DownCfg><<<grid_for(H, DownCfg::BN), DownCfg::THREADS,
@@ -692,7 +697,7 @@ static void launch_mfma(const rudnn_moe_experts* ex, const void* disp, int64_t r
         (const T*)h, (const T*)ex->down, nullptr, (T*)out, I, H, E, plan, cus, partials);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_DOWN_REDUCE, s);
-    splitk_reduce<T, false, DownCfg><<<256, 256, 0, s>>>(partials, (T*)out, I, H, E, plan, cus);
+    splitk_reduce<T, false, DownCfg><<<1024, 256, 0, s>>>(partials, (T*)out, I, H, E, plan, cus);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_DOWN_REDUCE, s);
 }
 
