@@ -10,8 +10,8 @@
 //   gate_up  grouped GEMM, N = I, fused epilogue silu(g) * u (two accumulator sets per tile);
 //   down     grouped GEMM, N = H, K = I.
 // BF16/F16: v_mfma_f32_32x32x16_{bf16,f16} with FP32 accumulators.  A block of eight wavefronts
-// (4 along M x 2 along N) owns a 256-row tile of 256 accumulator columns (gate_up: 128 of gate +
-// 128 of up).  K is staged 64 at a time: tokens and weight rows go straight from global memory
+// (4 along M x 2 along N, two per SIMD) owns a 256-row tile: gate_up 192 columns of gate + 192 of
+// up (384 accumulator columns, 192 registers per lane), down 256 columns.  K is staged 64 at a time: tokens and weight rows go straight from global memory
 // into LDS with global_load_lds_dwordx4 (no register staging), in an XOR-swizzled layout that
 // keeps the MFMA operand reads free of bank conflicts.  Two LDS stages: the copies of step k+1
 // are issued under the MFMAs of step k; one barrier per step.
@@ -46,15 +46,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #endif
 #ifndef RUDNN_SPLIT_MIN_STEPS
 #define RUDNN_SPLIT_MIN_STEPS 8
-#endif
-#ifndef RUDNN_COPY_WAVES
-#define RUDNN_COPY_WAVES 8
-#endif
-#ifndef RUDNN_COPY_HALF
-#define RUDNN_COPY_HALF 0
-#endif
-#ifndef RUDNN_SETPRIO
-#define RUDNN_SETPRIO 0
 #endif
 #ifndef RUDNN_GROUP_N
 #define RUDNN_GROUP_N 4
@@ -211,7 +202,7 @@ struct Mfma<f16> {
 // per LDS stage BK (32 or 64), STAGES LDS buffers.  gate_up stages 2*BN weight rows (gate then
 // up) per tile.
 #ifndef RUDNN_GATE_UP_TILE
-#define RUDNN_GATE_UP_TILE 256, 128, 4, 2, 64, 2
+#define RUDNN_GATE_UP_TILE 256, 192, 4, 2, 64, 2
 #endif
 #ifndef RUDNN_DOWN_TILE
 #define RUDNN_DOWN_TILE 256, 256, 4, 2, 64, 2
@@ -310,9 +301,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int KS = BK / 16;             // MFMA steps per staged tile
     constexpr int A_BYTES = BM * ROWB, STAGE_BYTES = (BM + NB) * ROWB;
-    constexpr int CW = RUDNN_COPY_WAVES;                      // wavefronts that issue the copies
-    constexpr int SLOTS = (BM + NB) * ROWB / 1024 / CW;       // copies per copying wave per stage
-    static_assert((BM + NB) * ROWB % (1024 * CW) == 0, "copies must split evenly over the wavefronts");
+    constexpr int SLOTS = (BM + NB) * ROWB / 1024 / NWAVES;  // copies per wave per stage
+    static_assert((BM + NB) * ROWB % (1024 * NWAVES) == 0, "copies must split evenly over the wavefronts");
     static_assert(BM * ROWB % 1024 == 0 && BN * ROWB % 1024 == 0, "regions are whole 1 KiB copies");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 MFMA blocks");
     typedef typename Mfma<T>::frag frag;
@@ -331,8 +321,6 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     // waves share a row band, so a tile with few rows still spreads its MFMAs over several SIMDs
     // instead of stacking them on one (rows <= 64: two SIMDs, rows <= 128: all four).
     const int wm = wave / WN, wn = wave % WN;
-    const bool copier = RUDNN_COPY_HALF ? (wave >= NWAVES - CW) : (wave < CW);
-    const int cwave = RUDNN_COPY_HALF ? wave - (NWAVES - CW) : wave;
     const int nrows = tile.nrows, n0 = tile.n0;
     StageSrc src;
     src.a = reinterpret_cast<const unsigned char*>(A + (int64_t)tile.row0 * K);
@@ -348,13 +336,12 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     // all copies of step kt (the tail form zeroes chunks past K)
     auto issue_all = [&](int kt) __attribute__((always_inline)) {
         unsigned char* st = smem_raw + (kt % STAGES) * STAGE_BYTES;
-        if (!copier) return;
         if (ragged_k && kt == KT - 1) {
 #pragma unroll
-            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, CW, true>(q, st, src, kt * BK, cwave, lane);
+            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, NWAVES, true>(q, st, src, kt * BK, wave, lane);
         } else {
 #pragma unroll
-            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, CW, false>(q, st, src, kt * BK, cwave, lane);
+            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, NWAVES, false>(q, st, src, kt * BK, wave, lane);
         }
     };
 
@@ -400,12 +387,10 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
             if constexpr (decltype(with_issue)::value) {
                 // copies for the next step go out early: spread over the first DMA_SPREAD MFMA steps
                 constexpr int SP = RUDNN_DMA_SPREAD < KS ? RUDNN_DMA_SPREAD : KS;
-                if (ks < SP && copier) {
-                    if (RUDNN_SETPRIO) __builtin_amdgcn_s_setprio(3);
+                if (ks < SP) {
 #pragma unroll
                     for (int q = ks * SLOTS / SP; q < (ks + 1) * SLOTS / SP; ++q)
-                        stage_slot<Cfg, NSETS, CW, false>(q, st_next, src, kt_next * BK, cwave, lane);
-                    if (RUDNN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+                        stage_slot<Cfg, NSETS, NWAVES, false>(q, st_next, src, kt_next * BK, wave, lane);
                 }
             }
             if constexpr (decltype(with_mfma)::value) {
@@ -488,38 +473,47 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     }
     constexpr int PITCH = BN * (int)sizeof(T) + 16;  // bytes per staged output row
     constexpr int CHUNKS = BN * (int)sizeof(T) / 16;  // 16-byte pieces per row
-    static_assert(BM * PITCH <= 160 * 1024, "output tile exceeds the LDS");
-    __syncthreads();  // every wavefront is done with the stages
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int row = wm * WTM + i * 32 + fr;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int col = wn * WTN + j * 32 + 8 * q + 4 * fh;
-                T out[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int v = 4 * q + u;
-                    const float val = DUAL ? silu_f(acc[0][i][j][v]) * acc[NSETS - 1][i][j][v] : acc[0][i][j][v];
-                    out[u] = from_f32<T>(val);
-                }
-                uint2 packed;
-                __builtin_memcpy(&packed, out, sizeof(packed));
-                *reinterpret_cast<uint2*>(smem_raw + row * PITCH + col * (int)sizeof(T)) = packed;
-            }
-        }
-    }
-    __syncthreads();
+    constexpr int LDS_MAX = 160 * 1024;
+    constexpr int PASSES = (BM * PITCH + LDS_MAX - 1) / LDS_MAX;  // row bands staged one at a time
+    constexpr int PROWS = BM / PASSES;                            // rows per band
+    static_assert(WM % PASSES == 0 && PROWS * PITCH <= LDS_MAX, "output bands follow the wavefront rows");
     T* Cb = C + (int64_t)tile.row0 * N + n0;
     const int ncols = min(BN, N - n0);
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+        __syncthreads();  // the stages (or the previous band) are no longer read
+        if (wm / (WM / PASSES) == pass) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int row = wm * WTM + i * 32 + fr - pass * PROWS;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = wn * WTN + j * 32 + 8 * q + 4 * fh;
+                        T out[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int v = 4 * q + u;
+                            const float val =
+                                DUAL ? silu_f(acc[0][i][j][v]) * acc[NSETS - 1][i][j][v] : acc[0][i][j][v];
+                            out[u] = from_f32<T>(val);
+                        }
+                        uint2 packed;
+                        __builtin_memcpy(&packed, out, sizeof(packed));
+                        *reinterpret_cast<uint2*>(smem_raw + row * PITCH + col * (int)sizeof(T)) = packed;
+                    }
+                }
+            }
+        }
+        __syncthreads();
 #pragma unroll 4
-    for (int p = tid; p < BM * CHUNKS; p += Cfg::THREADS) {
-        const int row = p / CHUNKS, ch = p % CHUNKS;
-        if (row < nrows && ch * 8 < ncols)
-            *reinterpret_cast<uint4*>(Cb + (int64_t)row * N + ch * 8) =
-                *reinterpret_cast<const uint4*>(smem_raw + row * PITCH + ch * 16);
+        for (int p = tid; p < PROWS * CHUNKS; p += Cfg::THREADS) {
+            const int r = p / CHUNKS, ch = p % CHUNKS, row = pass * PROWS + r;
+            if (row < nrows && ch * 8 < ncols)
+                *reinterpret_cast<uint4*>(Cb + (int64_t)row * N + ch * 8) =
+                    *reinterpret_cast<const uint4*>(smem_raw + r * PITCH + ch * 16);
+        }
     }
 }
 
@@ -531,19 +525,19 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
                                                      int N, int E, Plan plan, int cus) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, NSETS = DUAL ? 2 : 1, NB = NSETS * BN;
     constexpr int CPRW = BN / 8, SLAB = 256 / CPRW;  // 8-column chunks per row, rows per slab
-    static_assert(BM % SLAB == 0, "slabs tile the rows");
+    constexpr int SLABS = (BM + SLAB - 1) / SLAB;     // slabs per tile
     __shared__ int s_mt[MAX_EXPERTS + 1];
     const int NT = (N + BN - 1) / BN;
     const int KT = (K + Cfg::BK - 1) / Cfg::BK;
     const Split sp = split_plan(load_plan(plan, E, NT, s_mt), KT, cus);
-    const int slabs = sp.R * (BM / SLAB);
+    const int slabs = sp.R * SLABS;
     for (int b = blockIdx.x; b < slabs; b += gridDim.x) {
-        const int r = b / (BM / SLAB);
+        const int r = b / SLABS;
         Tile t;
         decode_tile<BM, BN>(plan, s_mt, E, NT, sp.full + r, t);
-        const int row = (b % (BM / SLAB)) * SLAB + threadIdx.x / CPRW;
+        const int row = (b % SLABS) * SLAB + threadIdx.x / CPRW;
         const int col = (threadIdx.x % CPRW) * 8;
-        if (row >= t.nrows || t.n0 + col >= N) continue;
+        if (threadIdx.x >= SLAB * CPRW || row >= min(t.nrows, BM) || t.n0 + col >= N) continue;
         const float* P = partials + ((int64_t)r * sp.S * BM + row) * NB + col;
         const int64_t seg_stride = (int64_t)BM * NB;
         float g[8] = {}, u[8] = {};
@@ -638,11 +632,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
 // ---------------------------------------------------------------------------------------
 static int64_t max_mtiles(int64_t rows, int64_t E, int BM) { return rows / BM + (E < rows ? E : rows); }
 
-// Partial-sum slots of the tail split: SPLIT_SLOTS x BM x 256 FP32 (both GEMMs stage 256
-// accumulator columns per tile).
+// Partial-sum slots of the tail split: SPLIT_SLOTS x BM x (accumulator columns of the wider
+// tile) FP32.
 static size_t split_partials_bytes(rudnn_moe_dtype dt) {
-    static_assert(GateUpCfg::BN * 2 == 256 && DownCfg::BN == 256, "partial slots hold 256 columns");
-    return dt == RUDNN_MOE_F32 ? 0 : (size_t)SPLIT_SLOTS * GateUpCfg::BM * 256 * sizeof(float);
+    constexpr size_t NB = 2 * GateUpCfg::BN > DownCfg::BN ? 2 * GateUpCfg::BN : DownCfg::BN;  // widest tile
+    return dt == RUDNN_MOE_F32 ? 0 : (size_t)SPLIT_SLOTS * GateUpCfg::BM * NB * sizeof(float);
 }
 
 size_t experts_workspace_bytes(int64_t E, int64_t H, int64_t I, rudnn_moe_dtype dt, int64_t rows) {
@@ -666,7 +660,8 @@ static int device_cus() {
 template <typename Cfg, bool DUAL>
 static size_t mfma_smem_bytes(int64_t E) {
     const size_t stages = (size_t)Cfg::STAGES * (Cfg::BM + (DUAL ? 2 : 1) * Cfg::BN) * Cfg::ROWB;
-    const size_t out_tile = (size_t)Cfg::BM * (Cfg::BN * 2 + 16);  // staged 16-bit output rows
+    const size_t band = (size_t)Cfg::BM * (Cfg::BN * 2 + 16);  // staged 16-bit output rows
+    const size_t out_tile = band > 160 * 1024 ? band / 2 : band;
     const size_t mt = sizeof(int) * (size_t)(E + 1);
     size_t bytes = stages > mt ? stages : mt;
     return bytes > out_tile ? bytes : out_tile;
