@@ -16,7 +16,14 @@
  *   section 5 "Expertengewichte und Verteilung" -- tokens [T,H], gate/up [E,I,H],
  *                                      down [E,H,I], no capacity drops, order inside an
  *                                      expert unspecified, a stored map restores order;
- *   section 6 "MoE aufrufen"        -- the staged call forms and the full forward.
+ *   section 6 "MoE aufrufen"        -- the staged call forms and the full forward;
+ *   section 10 "Gruppenbeschraenktes Sigmoid-MoE-Routing" -- sigmoid scores, an optional FP32
+ *                                      correction bias [E] that only steers the selection,
+ *                                      group scores (maximum, or the sum of the two largest
+ *                                      corrected scores), a choice of groups, top-k inside
+ *                                      them, weights = the original sigmoid values,
+ *                                      optionally renormalised, times `scale`, lower ids
+ *                                      winning ties.
  *
  * Arithmetic: every value is widened exactly to double; sums, exp and divisions run in
  * double; a result is rounded once (round-to-nearest-even) to its storage dtype at the
@@ -36,6 +43,12 @@
  *  - SwiGLU: h = silu(gate . x) * (up . x), silu(z) = z / (1 + exp(-z)); y = down . h;
  *    no biases (section 5: "bias-freie Expertengewichte").
  *  - An index >= E given to dispatch gets map -1 and its token's combined row is NaN.
+ *  - Sigmoid routing decides in FP32, the precision the guide gives the bias: s32 = the
+ *    sigmoid rounded once to FP32, corrected score c = s32 + bias in FP32, a group score is the
+ *    largest c of the group or the FP32 sum of its two largest; groups and then experts are
+ *    taken by descending score, equal scores by ascending group / expert id.  The weights use
+ *    the double sigmoid.  A row with a NaN corrected score or a NaN group score is a NaN
+ *    row: indices 0..k-1, NaN weights.
  */
 #include <math.h>
 #include <stdint.h>
@@ -243,6 +256,104 @@ int oracle_route(const void* logits, int ldt, int64_t T, int64_t E, int64_t k, i
 }
 
 /* ------------------------------------------------------------------------------------ */
+/* Group-limited sigmoid routing (user guide section 10).                                 */
+/* ------------------------------------------------------------------------------------ */
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* logits [T,E] (ldt), bias [E] FP32 or NULL -> expert_indices [T,k] u32, weights [T,k] (ldt).
+ * E = groups * (E / groups); groups are contiguous id ranges.  weights_exact (may be NULL)
+ * receives the double weights before the cast.  Returns 0, or -1 on bad arguments. */
+int oracle_route_sigmoid_grouped(const void* logits, int ldt, int64_t T, int64_t E, const float* bias,
+                                 int64_t k, int64_t groups, int64_t selected_groups, int top_two,
+                                 int renormalize, double scale, uint32_t* expert_indices, void* weights,
+                                 double* weights_exact) {
+    if (T < 0 || E < 1 || groups < 1 || E % groups != 0 || selected_groups < 1 || selected_groups > groups)
+        return -1;
+    const int64_t per = E / groups;
+    if (k < 1 || k > selected_groups * per || (top_two && per < 2) || !(scale > 0.0) || isinf(scale)) return -1;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)E);
+        float* c = (float*)malloc(sizeof(float) * (size_t)E);
+        float* gs = (float*)malloc(sizeof(float) * (size_t)groups);
+        unsigned char* gsel = (unsigned char*)malloc((size_t)groups);
+        unsigned char* taken = (unsigned char*)malloc((size_t)E);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            uint32_t* idx = expert_indices + t * k;
+            int nan_row = 0;
+            /* scores: sigmoid of the logit; corrected score in FP32 */
+            for (int64_t e = 0; e < E; ++e) {
+                s[e] = sigmoid(load_val(logits, ldt, t * E + e));
+                const float s32 = (float)s[e];
+                c[e] = bias ? (float)((double)s32 + (double)bias[e]) : s32;
+                if (isnan(c[e])) nan_row = 1;
+            }
+            /* group scores: the largest corrected score, or the FP32 sum of the two largest */
+            for (int64_t g = 0; g < groups && !nan_row; ++g) {
+                const float* cg = c + g * per;
+                int64_t b1 = 0;
+                for (int64_t i = 1; i < per; ++i)
+                    if (cg[i] > cg[b1]) b1 = i;
+                if (!top_two) {
+                    gs[g] = cg[b1];
+                } else {
+                    int64_t b2 = -1;
+                    for (int64_t i = 0; i < per; ++i)
+                        if (i != b1 && (b2 < 0 || cg[i] > cg[b2])) b2 = i;
+                    gs[g] = (float)((double)cg[b1] + (double)cg[b2]);
+                }
+                if (isnan(gs[g])) nan_row = 1;
+            }
+            if (nan_row) {
+                for (int64_t j = 0; j < k; ++j) {
+                    idx[j] = (uint32_t)j;
+                    store_val(weights, ldt, t * k + j, NAN);
+                    if (weights_exact) weights_exact[t * k + j] = NAN;
+                }
+                continue;
+            }
+            /* groups by descending score, lower group id on ties */
+            memset(gsel, 0, (size_t)groups);
+            for (int64_t r = 0; r < selected_groups; ++r) {
+                int64_t best = -1;
+                for (int64_t g = 0; g < groups; ++g)
+                    if (!gsel[g] && (best < 0 || gs[g] > gs[best])) best = g;
+                gsel[best] = 1;
+            }
+            /* experts of the chosen groups by descending corrected score, lower id on ties */
+            memset(taken, 0, (size_t)E);
+            for (int64_t j = 0; j < k; ++j) {
+                int64_t best = -1;
+                for (int64_t e = 0; e < E; ++e) {
+                    if (taken[e] || !gsel[e / per]) continue;
+                    if (best < 0 || c[e] > c[best]) best = e;
+                }
+                taken[best] = 1;
+                idx[j] = (uint32_t)best;
+            }
+            /* weights: the original sigmoid values, optionally renormalised, then scaled */
+            double den = 0.0;
+            for (int64_t j = 0; j < k; ++j) den += s[idx[j]];
+            for (int64_t j = 0; j < k; ++j) {
+                double v = s[idx[j]];
+                if (renormalize) v /= den;
+                v *= scale;
+                store_val(weights, ldt, t * k + j, v);
+                if (weights_exact) weights_exact[t * k + j] = v;
+            }
+        }
+        free(s);
+        free(c);
+        free(gs);
+        free(gsel);
+        free(taken);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
 /* Dispatch (user guide section 5): capacity-free grouping by expert plus the stored map. */
 /* ------------------------------------------------------------------------------------ */
 
@@ -418,6 +529,42 @@ int oracle_combine(const void* expert_output, int dt, const int32_t* token_map, 
 /* Full local forward (user guide sections 3 and 6): route -> dispatch -> experts ->      */
 /* combine.  gate == NULL means identity experts (expert output = dispatched rows).       */
 /* ------------------------------------------------------------------------------------ */
+
+static int forward_routed(const void* input, int dt, const uint32_t* idx, const void* w, int ldt, int64_t T,
+                          int64_t E, int64_t k, const void* gate, const void* up, const void* down, int64_t H,
+                          int64_t I, void* output) {
+    size_t es = dt_size(dt);
+    int32_t* offs = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t* map = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T * k));
+    void* disp = malloc(es * (size_t)(T * k * H));
+    void* y = gate ? malloc(es * (size_t)(T * k * H)) : disp;
+    int rc = oracle_dispatch(idx, T, k, E, input, dt, H, disp, offs, map, NULL);
+    if (!rc && gate) rc = oracle_experts_forward(disp, offs, E, dt, gate, up, down, H, I, y, NULL);
+    if (!rc) rc = oracle_combine(y, dt, map, w, ldt, T, k, H, output);
+    if (gate) free(y);
+    free(disp);
+    free(map);
+    free(offs);
+    return rc;
+}
+
+/* Full local forward with group-limited sigmoid routing (user guide section 10:
+ * forward_sigmoid_grouped = sigmoid routing -> dispatch -> experts -> combine). */
+int oracle_forward_sigmoid_grouped(const void* input, int dt, const void* logits, int ldt, int64_t T, int64_t E,
+                                   const float* bias, int64_t k, int64_t groups, int64_t selected_groups,
+                                   int top_two, int renormalize, double scale, const void* gate, const void* up,
+                                   const void* down, int64_t H, int64_t I, void* output) {
+    if (T < 0) return -1;
+    if (T == 0) return 0;
+    uint32_t* idx = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(T * k));
+    void* w = malloc(dt_size(ldt) * (size_t)(T * k));
+    int rc = oracle_route_sigmoid_grouped(logits, ldt, T, E, bias, k, groups, selected_groups, top_two, renormalize,
+                                          scale, idx, w, NULL);
+    if (!rc) rc = forward_routed(input, dt, idx, w, ldt, T, E, k, gate, up, down, H, I, output);
+    free(w);
+    free(idx);
+    return rc;
+}
 
 int oracle_forward(const void* input, int dt, const void* logits, int ldt, int64_t T, int64_t E,
                    int64_t k, int renormalize, const void* gate, const void* up, const void* down,

@@ -38,11 +38,16 @@ def lib() -> ctypes.CDLL:
         L.oracle_experts_forward.argtypes = [P, P, I64, I32, P, P, P, I64, I64, P, P]
         L.oracle_combine.argtypes = [P, I32, P, P, I32, I64, I64, I64, P]
         L.oracle_forward.argtypes = [P, I32, P, I32, I64, I64, I64, I32, P, P, P, I64, I64, P]
+        D = ctypes.c_double
+        L.oracle_route_sigmoid_grouped.argtypes = [P, I32, I64, I64, P, I64, I64, I64, I32, I32, D, P, P, P]
+        L.oracle_forward_sigmoid_grouped.argtypes = [P, I32, P, I32, I64, I64, P, I64, I64, I64, I32, I32, D,
+                                                     P, P, P, I64, I64, P]
         L.oracle_decode.argtypes = [P, I32, I64, P]
         L.oracle_encode.argtypes = [P, I32, I64, P]
         L.oracle_set_num_threads.argtypes = [I32]
         for f in ("oracle_route", "oracle_dispatch", "oracle_expert_rows", "oracle_experts_forward",
-                  "oracle_combine", "oracle_forward", "oracle_num_threads"):
+                  "oracle_combine", "oracle_forward", "oracle_num_threads", "oracle_route_sigmoid_grouped",
+                  "oracle_forward_sigmoid_grouped"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -176,4 +181,53 @@ def forward(x: torch.Tensor, logits: torch.Tensor, top_k: int, renormalize: bool
                               int(bool(renormalize)), _p(gate), _p(up), _p(down), H, I, _p(out))
     if rc:
         raise ValueError("oracle_forward: bad arguments")
+    return out
+
+
+def _bias(bias):
+    if bias is None:
+        return None
+    b = _cpu(bias)
+    if b.dtype != torch.float32:
+        raise TypeError("the correction bias is FP32")
+    return b
+
+
+def route_sigmoid_grouped(logits: torch.Tensor, bias, top_k: int, groups: int, selected_groups: int,
+                          top_two: bool, renormalize: bool, scale: float):
+    """Group-limited sigmoid routing (user guide section 10).  Returns ``(indices uint32 [T,k],
+    weights [T,k] in the logits dtype, exact float64 weights)``."""
+    logits = _cpu(logits)
+    b = _bias(bias)
+    T, E = logits.shape
+    idx = np.empty((T, top_k), np.uint32)
+    w = torch.empty(T, top_k, dtype=logits.dtype)
+    wx = np.empty((T, top_k), np.float64)
+    rc = lib().oracle_route_sigmoid_grouped(_p(logits), _DT_CODE[logits.dtype], T, E, _p(b), top_k, groups,
+                                            selected_groups, int(bool(top_two)), int(bool(renormalize)),
+                                            float(scale), _p(idx), _p(w), _p(wx))
+    if rc:
+        raise ValueError("oracle_route_sigmoid_grouped: bad arguments")
+    return idx, w, wx
+
+
+def forward_sigmoid_grouped(x: torch.Tensor, logits: torch.Tensor, bias, top_k: int, groups: int,
+                            selected_groups: int, top_two: bool, renormalize: bool, scale: float,
+                            gate=None, up=None, down=None):
+    """The full local forward with group-limited sigmoid routing; ``gate=None`` means identity experts."""
+    x, logits = _cpu(x), _cpu(logits)
+    b = _bias(bias)
+    T, H = x.shape
+    E = logits.shape[1]
+    I = 0
+    if gate is not None:
+        gate, up, down = _cpu(gate), _cpu(up), _cpu(down)
+        I = gate.shape[1]
+    out = torch.empty(T, H, dtype=x.dtype)
+    rc = lib().oracle_forward_sigmoid_grouped(_p(x), _DT_CODE[x.dtype], _p(logits), _DT_CODE[logits.dtype], T, E,
+                                              _p(b), top_k, groups, selected_groups, int(bool(top_two)),
+                                              int(bool(renormalize)), float(scale), _p(gate), _p(up), _p(down),
+                                              H, I, _p(out))
+    if rc:
+        raise ValueError("oracle_forward_sigmoid_grouped: bad arguments")
     return out

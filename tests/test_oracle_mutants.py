@@ -11,6 +11,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
+PINS = "test_oracle_pins.py"
+SIG = "test_oracle_sigmoid_pins.py"
+
 MUTANTS = {
     "tie_to_higher_id": ("if (best < 0 || p[e] > p[best]) best = e;", "if (best < 0 || p[e] >= p[best]) best = e;"),
     "softmax_unnormalised": ("for (int64_t e = 0; e < E; ++e) p[e] /= s;", "(void)s;"),
@@ -26,12 +29,21 @@ MUTANTS = {
     "dispatch_skips_first": ("for (int64_t a = 0; a < T * k; ++a)\n        if (expert_indices[a]", "for (int64_t a = 1; a < T * k; ++a)\n        if (expert_indices[a]"),
     "rounding_truncates": ("double r = nearbyint(x / q) * q;", "double r = trunc(x / q) * q;"),
     "hidden_not_rounded": ("hb[r * I + i] = round_to(silu(g) * u, dt);", "hb[r * I + i] = silu(g) * u;"),
+    # group-limited sigmoid routing (section 10), checked against its own pins
+    "sig_bias_in_weights": ("double v = s[idx[j]];", "double v = c[idx[j]];", SIG),
+    "sig_expert_tie_to_higher_id": ("if (best < 0 || c[e] > c[best]) best = e;", "if (best < 0 || c[e] >= c[best]) best = e;", SIG),
+    "sig_group_tie_to_higher_id": ("if (!gsel[g] && (best < 0 || gs[g] > gs[best])) best = g;",
+                                   "if (!gsel[g] && (best < 0 || gs[g] >= gs[best])) best = g;", SIG),
+    "sig_top_two_ignored": ("if (!top_two) {\n                    gs[g] = cg[b1];", "if (1) {\n                    gs[g] = cg[b1];", SIG),
+    "sig_top_two_counts_max_twice": ("if (i != b1 && (b2 < 0 || cg[i] > cg[b2])) b2 = i;", "if (b2 < 0 || cg[i] > cg[b2]) b2 = i;", SIG),
+    "sig_groups_not_enforced": ("if (taken[e] || !gsel[e / per]) continue;", "if (taken[e]) continue;", SIG),
+    "sig_scale_dropped_with_renorm": ("v *= scale;", "if (!renormalize) v *= scale;", SIG),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_fails_a_pin(name, tmp_path):
-    old, new = MUTANTS[name]
+    old, new, pins = (MUTANTS[name] + (PINS,))[:3]
     src = open(SRC).read()
     assert src.count(old) == 1, f"mutation anchor for {name} not unique"
     mut = tmp_path / "oracle_mut.c"
@@ -41,6 +53,6 @@ def test_planted_mistake_fails_a_pin(name, tmp_path):
                    check=True)
     env = dict(os.environ, ORACLE_LIB=str(lib), OMP_NUM_THREADS="4")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
