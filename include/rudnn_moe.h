@@ -173,6 +173,56 @@ rudnn_moe_status rudnn_moe_forward(const rudnn_moe_experts* ex, const void* inpu
                                    rudnn_moe_dtype logits_dtype, int64_t T, rudnn_moe_routing_options opt,
                                    void* output, void* workspace, size_t workspace_size, hipStream_t stream);
 
+/* GroupRoutingOptions of section 10 (group-limited sigmoid routing).  Experts are split into
+ * `groups` contiguous id ranges of E / groups experts.  Valid: 1 <= E <= 1024, 1 <= groups <=
+ * 128 with E % groups == 0, 1 <= selected_groups <= groups, 1 <= top_k <= 64 and top_k <=
+ * selected_groups * (E / groups), E / groups >= 2 when group_top_two, scale finite and > 0. */
+typedef struct {
+    int64_t top_k;
+    int64_t groups;
+    int64_t selected_groups;
+    int32_t group_top_two;  /* != 0: a group's score is the sum of its two largest corrected scores */
+    int32_t renormalize;    /* != 0: selected weights are divided by their sum (before `scale`) */
+    double scale;           /* multiplies the (renormalised) weights */
+} rudnn_moe_group_routing_options;
+
+/*
+ * route_sigmoid_grouped -- section 10 (route_sigmoid_grouped(logits, bias, options) ->
+ * RoutingPlan).  For each row t of logits [T, E], in FP32: s_e = 1 / (1 + exp(-x_e)); the
+ * corrected score c_e = s_e + bias[e] (bias only steers the selection).  A group's score is
+ * its largest c, or the sum of its two largest with group_top_two; the selected_groups
+ * highest-scoring groups are chosen (equal scores: lower group id), then the top_k experts
+ * of those groups by c (equal c: lower id), listed by descending c.  weights[t, j] = s of
+ * the j-th selected expert, divided by the sum of the selected s when renormalising, times
+ * scale, cast (round to nearest even) to the logits dtype.  A row with a NaN corrected score
+ * or a NaN group score (e.g. +inf and -inf biases summed) gets weights NaN, indices 0..k-1.
+ *   logits          [T, E]  logits_dtype (F32/F16/BF16)
+ *   bias            [E]     FP32 device memory, or NULL for no correction
+ *   expert_indices  [T, k]  uint32, written
+ *   weights         [T, k]  logits_dtype, written
+ * The outputs feed rudnn_moe_dispatch / rudnn_moe_combine exactly like rudnn_moe_route's.
+ * Errors: SHAPE (T < 0, E < 1), ARGUMENT (options outside the ranges above, NULL, overlap),
+ * DTYPE, UNSUPPORTED (T * top_k >= 2^31), DEVICE, RUNTIME.
+ */
+rudnn_moe_status rudnn_moe_route_sigmoid_grouped(const void* logits, rudnn_moe_dtype logits_dtype, int64_t T,
+                                                 int64_t E, const float* bias, rudnn_moe_group_routing_options opt,
+                                                 uint32_t* expert_indices, void* weights, hipStream_t stream);
+
+/*
+ * forward_sigmoid_grouped -- section 10 (SwiGluExperts::forward_sigmoid_grouped(input,
+ * logits, bias, options, strategy)): route_sigmoid_grouped -> dispatch -> experts ->
+ * combine on one stream.  One strategy here: the MFMA (BF16/F16) or FP32 kernels.
+ *   input [T, H] ex->dtype;  logits [T, E] logits_dtype;  bias [E] FP32 or NULL;
+ *   output [T, H] ex->dtype, written
+ * workspace: at least rudnn_moe_forward_workspace_size(ex, T, opt.top_k, logits_dtype) bytes.
+ * Errors: as rudnn_moe_forward, with the option checks of rudnn_moe_route_sigmoid_grouped.
+ */
+rudnn_moe_status rudnn_moe_forward_sigmoid_grouped(const rudnn_moe_experts* ex, const void* input,
+                                                   const void* logits, rudnn_moe_dtype logits_dtype, int64_t T,
+                                                   const float* bias, rudnn_moe_group_routing_options opt,
+                                                   void* output, void* workspace, size_t workspace_size,
+                                                   hipStream_t stream);
+
 /* Static, human-readable name of a status. */
 const char* rudnn_moe_status_string(rudnn_moe_status s);
 
@@ -192,7 +242,8 @@ typedef enum {
     RUDNN_MOE_KERNEL_COMBINE = 8,
     RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE = 9, /* sums the K-split partials of gate_up tail tiles */
     RUDNN_MOE_KERNEL_EXPERTS_DOWN_REDUCE = 10,   /* the same for down */
-    RUDNN_MOE_KERNEL_COUNT = 11
+    RUDNN_MOE_KERNEL_ROUTE_SIGMOID_GROUPED = 11, /* group-limited sigmoid routing */
+    RUDNN_MOE_KERNEL_COUNT = 12
 } rudnn_moe_kernel;
 
 /* For the calling host thread: record `before` on the launch stream immediately before the

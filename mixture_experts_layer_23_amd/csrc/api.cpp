@@ -3,6 +3,7 @@
 // Every check runs on the host before the first launch (the counterpart of the guide's
 // Result<_, MoeError>, ruDNN user guide sections 3 and 6); pure argument checks come first and
 // make no HIP call, so they can be exercised without a GPU.
+#include <cmath>
 #include <mutex>
 
 #include "internal.hpp"
@@ -78,6 +79,17 @@ rudnn_moe_status check_route_args(const void* logits, rudnn_moe_dtype ldt, int64
     return RUDNN_MOE_OK;
 }
 
+// Option checks of section 10 (the ranges the guide gives GroupRoutingOptions).
+rudnn_moe_status check_group_options(int64_t E, const rudnn_moe_group_routing_options& o) {
+    if (E > MAX_EXPERTS || o.groups < 1 || o.groups > 128 || E % o.groups != 0) return RUDNN_MOE_ERR_ARGUMENT;
+    const int64_t per = E / o.groups;
+    if (o.selected_groups < 1 || o.selected_groups > o.groups) return RUDNN_MOE_ERR_ARGUMENT;
+    if (o.top_k < 1 || o.top_k > MAX_TOP_K || o.top_k > o.selected_groups * per) return RUDNN_MOE_ERR_ARGUMENT;
+    if (o.group_top_two && per < 2) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!(o.scale > 0.0) || !std::isfinite(o.scale)) return RUDNN_MOE_ERR_ARGUMENT;
+    return RUDNN_MOE_OK;
+}
+
 rudnn_moe_status check_experts_view(const rudnn_moe_experts* ex) {
     if (!ex) return RUDNN_MOE_ERR_ARGUMENT;
     if (ex->num_experts < 1 || ex->hidden < 1 || ex->intermediate < 1) return RUDNN_MOE_ERR_SHAPE;
@@ -147,6 +159,26 @@ rudnn_moe_status rudnn_moe_route(const void* logits, rudnn_moe_dtype ldt, int64_
     if (st != RUDNN_MOE_OK || T == 0) return st;
     if ((st = check_device(stream, {logits, idx, w})) != RUDNN_MOE_OK) return st;
     return runtime(launch_route(logits, ldt, T, E, opt.top_k, opt.renormalize != 0, idx, w, stream));
+}
+
+rudnn_moe_status rudnn_moe_route_sigmoid_grouped(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E,
+                                                 const float* bias, rudnn_moe_group_routing_options opt, uint32_t* idx,
+                                                 void* w, hipStream_t stream) {
+    if (T < 0 || E < 1) return RUDNN_MOE_ERR_SHAPE;
+    rudnn_moe_status st = check_group_options(E, opt);
+    if (st != RUDNN_MOE_OK) return st;
+    if (!valid_dtype(ldt)) return RUDNN_MOE_ERR_DTYPE;
+    if (T * opt.top_k >= INT32_LIMIT || T * E >= ((int64_t)1 << 40)) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (T == 0) return RUDNN_MOE_OK;
+    if (!logits || !idx || !w) return RUDNN_MOE_ERR_ARGUMENT;
+    const size_t ls = dtype_size(ldt), pk = (size_t)(T * opt.top_k);
+    if (any_overlap({{idx, pk * 4}, {w, pk * ls}}, {{logits, (size_t)(T * E) * ls}, {bias, bias ? 4 * (size_t)E : 0}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    if ((st = check_device(stream, {logits, idx, w})) != RUDNN_MOE_OK) return st;
+    if (bias && (st = check_device(stream, {bias})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_route_sigmoid_grouped(logits, ldt, bias, T, E, opt.top_k, opt.groups, opt.selected_groups,
+                                                opt.group_top_two != 0, opt.renormalize != 0, opt.scale, idx, w,
+                                                stream));
 }
 
 size_t rudnn_moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E) {
@@ -264,31 +296,43 @@ size_t rudnn_moe_forward_workspace_size(const rudnn_moe_experts* ex, int64_t T, 
     return forward_layout(ex, T, top_k, logits_dtype).total;
 }
 
-rudnn_moe_status rudnn_moe_forward(const rudnn_moe_experts* ex, const void* input, const void* logits,
-                                   rudnn_moe_dtype ldt, int64_t T, rudnn_moe_routing_options opt, void* output,
-                                   void* workspace, size_t workspace_size, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward of sections 6 and 10: routing (softmax or group-limited sigmoid, chosen by
+// `sig`) -> dispatch -> experts -> combine, after the shared checks.
+rudnn_moe_status forward_common(const rudnn_moe_experts* ex, const void* input, const void* logits,
+                                rudnn_moe_dtype ldt, int64_t T, int64_t top_k, int renormalize,
+                                const rudnn_moe_group_routing_options* sig, const float* bias, void* output,
+                                void* workspace, size_t workspace_size, hipStream_t stream) {
     rudnn_moe_status st = check_experts_view(ex);
     if (st != RUDNN_MOE_OK) return st;
     if (T < 0) return RUDNN_MOE_ERR_SHAPE;
-    if (opt.top_k < 1 || opt.top_k > ex->num_experts) return RUDNN_MOE_ERR_ARGUMENT;
+    if (sig) {
+        if ((st = check_group_options(ex->num_experts, *sig)) != RUDNN_MOE_OK) return st;
+    } else if (top_k < 1 || top_k > ex->num_experts) {
+        return RUDNN_MOE_ERR_ARGUMENT;
+    }
     if (!valid_dtype(ldt)) return RUDNN_MOE_ERR_DTYPE;
-    if (opt.top_k > MAX_TOP_K || T * opt.top_k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
-    if ((st = check_experts_rows(ex, T * opt.top_k)) != RUDNN_MOE_OK) return st;
+    if (top_k > MAX_TOP_K || T * top_k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if ((st = check_experts_rows(ex, T * top_k)) != RUDNN_MOE_OK) return st;
     if (T == 0) return RUDNN_MOE_OK;
     if (!input || !logits || !output) return RUDNN_MOE_ERR_ARGUMENT;
     if (ex->dtype != RUDNN_MOE_F32 && ((uintptr_t)input % 16 || (uintptr_t)output % 16))
         return RUDNN_MOE_ERR_UNSUPPORTED;
-    const ForwardLayout L = forward_layout(ex, T, opt.top_k, ldt);
+    const ForwardLayout L = forward_layout(ex, T, top_k, ldt);
     if (!workspace || workspace_size < L.total) return RUDNN_MOE_ERR_WORKSPACE;
     const size_t es = dtype_size(ex->dtype);
     const size_t wsz = (size_t)(ex->num_experts * ex->hidden * ex->intermediate) * es;
     const size_t xb = (size_t)T * ex->hidden * es;
     if (any_overlap({{output, xb}, {workspace, L.total}},
                     {{input, xb}, {logits, (size_t)(T * ex->num_experts) * dtype_size(ldt)}, {ex->gate, wsz},
-                     {ex->up, wsz}, {ex->down, wsz}}))
+                     {ex->up, wsz}, {ex->down, wsz}, {bias, bias ? 4 * (size_t)ex->num_experts : 0}}))
         return RUDNN_MOE_ERR_ARGUMENT;
     if ((st = check_device(stream, {input, logits, output, workspace, ex->gate, ex->up, ex->down})) != RUDNN_MOE_OK)
         return st;
+    if (bias && (st = check_device(stream, {bias})) != RUDNN_MOE_OK) return st;
     unsigned char* ws = (unsigned char*)workspace;
     uint32_t* idx = (uint32_t*)(ws + L.idx);
     void* w = ws + L.w;
@@ -296,13 +340,36 @@ rudnn_moe_status rudnn_moe_forward(const rudnn_moe_experts* ex, const void* inpu
     int32_t* map = (int32_t*)(ws + L.map);
     void* disp = ws + L.disp;
     void* y = ws + L.y;
-    const int64_t E = ex->num_experts, k = opt.top_k, H = ex->hidden;
-    hipError_t e = launch_route(logits, ldt, T, E, k, opt.renormalize != 0, idx, w, stream);
+    const int64_t E = ex->num_experts, k = top_k, H = ex->hidden;
+    hipError_t e = sig ? launch_route_sigmoid_grouped(logits, ldt, bias, T, E, k, sig->groups, sig->selected_groups,
+                                                      sig->group_top_two != 0, sig->renormalize != 0, sig->scale, idx,
+                                                      w, stream)
+                       : launch_route(logits, ldt, T, E, k, renormalize != 0, idx, w, stream);
     if (e == hipSuccess)
         e = launch_dispatch(idx, T, k, E, input, (size_t)H * es, disp, offsets, map, (int32_t*)(ws + L.dws), stream);
     if (e == hipSuccess) e = launch_experts(ex, disp, offsets, T * k, y, ws + L.ews, stream);
     if (e == hipSuccess) e = launch_combine(y, ex->dtype, map, w, ldt, T, k, H, output, stream);
     return runtime(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+rudnn_moe_status rudnn_moe_forward(const rudnn_moe_experts* ex, const void* input, const void* logits,
+                                   rudnn_moe_dtype ldt, int64_t T, rudnn_moe_routing_options opt, void* output,
+                                   void* workspace, size_t workspace_size, hipStream_t stream) {
+    return forward_common(ex, input, logits, ldt, T, opt.top_k, opt.renormalize, nullptr, nullptr, output, workspace,
+                          workspace_size, stream);
+}
+
+rudnn_moe_status rudnn_moe_forward_sigmoid_grouped(const rudnn_moe_experts* ex, const void* input,
+                                                   const void* logits, rudnn_moe_dtype ldt, int64_t T,
+                                                   const float* bias, rudnn_moe_group_routing_options opt,
+                                                   void* output, void* workspace, size_t workspace_size,
+                                                   hipStream_t stream) {
+    return forward_common(ex, input, logits, ldt, T, opt.top_k, opt.renormalize, &opt, bias, output, workspace,
+                          workspace_size, stream);
 }
 
 }  // extern "C"

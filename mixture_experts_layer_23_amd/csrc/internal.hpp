@@ -43,6 +43,10 @@ void timing_after(rudnn_moe_kernel k, hipStream_t s);
 hipError_t launch_route(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E, int64_t k, bool renorm,
                         uint32_t* idx, void* w, hipStream_t s);
 
+hipError_t launch_route_sigmoid_grouped(const void* logits, rudnn_moe_dtype ldt, const float* bias, int64_t T,
+                                        int64_t E, int64_t k, int64_t groups, int64_t selected_groups, bool top_two,
+                                        bool renorm, double scale, uint32_t* idx, void* w, hipStream_t s);
+
 hipError_t launch_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input, size_t row_bytes,
                            void* dispatched, int32_t* offsets, int32_t* token_map, int32_t* chunk_counts,
                            hipStream_t s);

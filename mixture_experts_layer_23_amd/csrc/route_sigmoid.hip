@@ -1,0 +1,215 @@
+// route_sigmoid.hip -- group-limited sigmoid routing (ruDNN user guide, section 10:
+// route_sigmoid_grouped with GroupRoutingOptions top_k, groups, selected_groups,
+// group_top_two, renormalize, scale, and an optional FP32 correction bias [E]).
+//
+// A group of G adjacent lanes owns one row of logits [T, E] (the lane layout of the softmax
+// router: lane l of the group holds experts [l * NPER, (l + 1) * NPER)).  Per row, in FP32:
+//   1. s_e = 1 / (1 + exp(-x_e)); corrected score c_e = s_e + bias_e (the bias only steers the
+//      choice).  s and c go to LDS.
+//   2. Group scores from LDS, lane l taking groups l, l + G, ...: the largest c of the group,
+//      or the sum of its two largest (group_top_two).  A NaN corrected score or a NaN group
+//      score makes the row a NaN row (indices 0..k-1, NaN weights).
+//   3. selected_groups rounds over order-preserving keys (score bits above the complemented
+//      group id) choose the groups, ties to the lower group.
+//   4. k rounds over the experts of the chosen groups (keys: c bits above the complemented
+//      expert id; experts of other groups have key 0) choose the experts, ties to the lower id.
+//   5. w_j = s_j, divided by the FP32 sum of the selected s (j ascending) when renormalising,
+//      times scale, rounded once to the logits dtype.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace rudnn {
+
+constexpr int SIG_THREADS = 256;
+constexpr int SIG_MAX_GPL = 16;  // groups per lane: groups <= min(E, 128) <= 16 * G
+
+template <int G>
+__device__ __forceinline__ uint64_t sig_group_max(uint64_t key) {
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)key, m, 64), hi = __shfl_xor((uint32_t)(key >> 32), m, 64);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        key = o > key ? o : key;
+    }
+    return key;
+}
+
+// FP32 value -> order-preserving 32 bits (-0 taken as +0), above the complement of an id.
+__device__ __forceinline__ uint64_t sig_key(float v, uint32_t id) {
+    uint32_t b = __float_as_uint(v);
+    if (b == 0x80000000u) b = 0;
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint32_t)(0xffffffffu - id);
+}
+
+template <typename LT, int NPER, int G>
+__global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __restrict__ logits,
+                                                                    const float* __restrict__ bias, int64_t T, int E,
+                                                                    int k, int groups, int nsel, int top_two,
+                                                                    int renorm, float scale,
+                                                                    uint32_t* __restrict__ idx, LT* __restrict__ w) {
+    constexpr int RPB = SIG_THREADS / G;
+    extern __shared__ float smem[];  // c [RPB][E], s [RPB][E], winners [RPB][k]
+    const int lane = lane_id(), l = lane % G, rb = threadIdx.x / G;
+    const int64_t row = (int64_t)blockIdx.x * RPB + rb;
+    const bool live = row < T;  // whole groups are live or not; no early return (shuffles, barriers)
+    float* sc = smem + rb * E;
+    float* ss = smem + RPB * E + rb * E;
+    uint32_t* swin = reinterpret_cast<uint32_t*>(smem + 2 * RPB * E) + rb * k;
+    const int e0 = l * NPER, per = E / groups;
+    const LT* x = logits + (live ? row : 0) * (int64_t)E;
+
+    // 1. sigmoid and corrected scores
+    float c[NPER];
+    bool bad = false;
+#pragma unroll
+    for (int s = 0; s < NPER; ++s) {
+        const int e = e0 + s;
+        c[s] = 0.f;
+        if (e < E) {
+            const float xv = live ? to_f32(x[e]) : 0.f;
+            const float sg = 1.0f / (1.0f + expf(-xv));  // +inf -> 1, -inf -> 0, NaN -> NaN
+            c[s] = bias ? sg + bias[e] : sg;
+            bad |= c[s] != c[s];
+            sc[e] = c[s];
+            ss[e] = sg;
+        }
+    }
+    __syncthreads();
+
+    // 2. group scores
+    uint64_t gkey[SIG_MAX_GPL];
+#pragma unroll
+    for (int q = 0; q < SIG_MAX_GPL; ++q) {
+        const int g = l + q * G;
+        gkey[q] = 0;
+        if (g < groups) {
+            float t1 = -INFINITY, t2 = -INFINITY;  // the two largest corrected scores
+            for (int i = 0; i < per; ++i) {
+                const float v = sc[g * per + i];
+                if (v > t1) {
+                    t2 = t1;
+                    t1 = v;
+                } else if (v > t2) {
+                    t2 = v;
+                }
+            }
+            const float gs = top_two ? t1 + t2 : t1;
+            bad |= gs != gs;
+            gkey[q] = sig_key(gs, (uint32_t)g);
+        }
+    }
+    const int gshift = lane - l;
+    const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull);
+    const bool nan_row = ((__ballot(bad) >> gshift) & gmask) != 0;
+
+    // 3. groups by descending score
+    uint32_t chosen[4] = {0u, 0u, 0u, 0u};  // bit g: group g selected (groups <= 128)
+    uint64_t prev = ~0ull;
+    for (int r = 0; r < nsel; ++r) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int q = 0; q < SIG_MAX_GPL; ++q) best = max(best, gkey[q] < prev ? gkey[q] : (uint64_t)0);
+        const uint64_t win = sig_group_max<G>(best);
+        prev = win;
+        const uint32_t g = 0xffffffffu - (uint32_t)win;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd)
+            if ((int)(g >> 5) == wd) chosen[wd] |= 1u << (g & 31);
+    }
+
+    // 4. experts of the chosen groups by descending corrected score
+    uint64_t key[NPER];
+#pragma unroll
+    for (int s = 0; s < NPER; ++s) {
+        const int e = e0 + s;
+        key[s] = 0;
+        if (e < E) {
+            const int g = e / per;
+            const uint32_t wv = g < 32 ? chosen[0] : g < 64 ? chosen[1] : g < 96 ? chosen[2] : chosen[3];
+            if ((wv >> (g & 31)) & 1u) key[s] = sig_key(c[s], (uint32_t)e);
+        }
+    }
+    prev = ~0ull;
+    float den = 0.f;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int s = 0; s < NPER; ++s) best = max(best, key[s] < prev ? key[s] : (uint64_t)0);
+        const uint64_t win = sig_group_max<G>(best);
+        prev = win;
+        const uint32_t id = 0xffffffffu - (uint32_t)win;
+        const uint32_t idc = id < (uint32_t)E ? id : 0u;  // NaN rows may pick nothing valid
+        den += ss[idc];
+        if (l == 0) swin[j] = idc;
+    }
+    __syncthreads();
+
+    // 5. weights
+    if (!live) return;
+    for (int j = l; j < k; j += G) {
+        if (nan_row) {
+            idx[row * k + j] = (uint32_t)j;
+            w[row * k + j] = from_f32<LT>(__builtin_nanf(""));
+        } else {
+            const uint32_t id = swin[j];
+            const float v = renorm ? ss[id] / den : ss[id];
+            idx[row * k + j] = id;
+            w[row * k + j] = from_f32<LT>(v * scale);
+        }
+    }
+}
+
+template <typename LT, int NPER, int G>
+static void launch_sig_g(const LT* l, const float* bias, int64_t T, int E, int k, int groups, int nsel, int top_two,
+                         int renorm, float scale, uint32_t* idx, LT* w, hipStream_t s) {
+    constexpr int RPB = SIG_THREADS / G;
+    static_assert(SIG_MAX_GPL >= NPER, "every lane has room for its share of at most min(E, 128) groups");
+    const dim3 grid((unsigned)((T + RPB - 1) / RPB)), block(SIG_THREADS);
+    const size_t smem = (size_t)RPB * (2 * E + k) * 4;
+    route_sigmoid_kernel<LT, NPER, G><<<grid, block, smem, s>>>(l, bias, T, E, k, groups, nsel, top_two, renorm,
+                                                                scale, idx, w);
+}
+
+template <typename LT>
+static hipError_t launch_sig_t(const void* logits, const float* bias, int64_t T, int64_t E, int64_t k, int64_t groups,
+                               int64_t nsel, bool top_two, bool renorm, double scale, uint32_t* idx, void* w,
+                               hipStream_t s) {
+    const LT* l = (const LT*)logits;
+    LT* wo = (LT*)w;
+    const int Ei = (int)E, ki = (int)k, gi = (int)groups, ni = (int)nsel, t2 = top_two ? 1 : 0, r = renorm ? 1 : 0;
+    const float sc = (float)scale;
+    timing_before(RUDNN_MOE_KERNEL_ROUTE_SIGMOID_GROUPED, s);
+    // lanes per row: the smallest power of two G with 16 G >= E (at most 16 groups per lane)
+    if (E <= 16)
+        launch_sig_g<LT, 16, 1>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    else if (E <= 32)
+        launch_sig_g<LT, 16, 2>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    else if (E <= 64)
+        launch_sig_g<LT, 16, 4>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    else if (E <= 128)
+        launch_sig_g<LT, 16, 8>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    else if (E <= 256)
+        launch_sig_g<LT, 16, 16>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    else if (E <= 512)
+        launch_sig_g<LT, 16, 32>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    else
+        launch_sig_g<LT, 16, 64>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    timing_after(RUDNN_MOE_KERNEL_ROUTE_SIGMOID_GROUPED, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_sigmoid_grouped(const void* logits, rudnn_moe_dtype ldt, const float* bias, int64_t T,
+                                        int64_t E, int64_t k, int64_t groups, int64_t selected_groups, bool top_two,
+                                        bool renorm, double scale, uint32_t* idx, void* w, hipStream_t s) {
+    switch (ldt) {
+    case RUDNN_MOE_F32:
+        return launch_sig_t<float>(logits, bias, T, E, k, groups, selected_groups, top_two, renorm, scale, idx, w, s);
+    case RUDNN_MOE_F16:
+        return launch_sig_t<f16>(logits, bias, T, E, k, groups, selected_groups, top_two, renorm, scale, idx, w, s);
+    default:
+        return launch_sig_t<bf16>(logits, bias, T, E, k, groups, selected_groups, top_two, renorm, scale, idx, w, s);
+    }
+}
+
+}  // namespace rudnn

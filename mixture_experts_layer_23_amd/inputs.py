@@ -34,8 +34,8 @@ import numpy as np
 import torch
 
 __all__ = [
-    "DTYPES", "DTYPE_CODE", "SPECIAL_KINDS", "Workload", "WORKLOADS",
-    "make_logits", "make_tokens", "make_experts",
+    "DTYPES", "DTYPE_CODE", "SPECIAL_KINDS", "SIGMOID_SPECIAL_KINDS", "SigmoidRouting", "Workload", "WORKLOADS",
+    "make_logits", "make_sigmoid_logits", "make_tokens", "make_experts",
 ]
 
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -46,7 +46,23 @@ DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
 # of the routing contract (a NaN, a +inf, or nothing but -inf).
 SPECIAL_KINDS = ("uniform", "boundary_tie", "top_tie", "partial_neginf", "nan", "posinf", "all_neginf")
 
+# Special rows of the group-limited sigmoid workloads: two experts with equal logit and equal
+# bias, two groups with equal logits and equal biases, and rows with a NaN / +inf / -inf logit.
+SIGMOID_SPECIAL_KINDS = ("expert_tie", "group_tie", "nan", "posinf", "neginf")
+
 _SEP = 1e-3  # minimum gap between distinct logits of one row (after rounding to the dtype)
+
+
+@dataclass(frozen=True)
+class SigmoidRouting:
+    """Options of group-limited sigmoid routing (ruDNN user guide, section 10) and the spread of
+    the drawn FP32 correction bias."""
+    groups: int
+    selected_groups: int
+    group_top_two: bool
+    renormalize: bool
+    scale: float
+    bias_std: float
 
 
 @dataclass(frozen=True)
@@ -62,7 +78,8 @@ class Workload:
     renormalize: tuple     # the renormalisation settings this workload is run with
     zipf_s: float | None   # per-expert load skew, None for none
     seed: int
-    special: tuple = (0, 0, 0, 0, 0, 0, 0)  # row counts per SPECIAL_KINDS entry
+    special: tuple = (0, 0, 0, 0, 0, 0, 0)  # row counts per SPECIAL_KINDS (or SIGMOID_SPECIAL_KINDS) entry
+    sigmoid: SigmoidRouting | None = None   # group-limited sigmoid routing instead of softmax
 
     def with_T(self, T: int) -> "Workload":
         """Same recipe with T rows; special-row counts scale with T (at least one of each kind
@@ -94,6 +111,15 @@ WORKLOADS = {
     "mixtral": Workload("mixtral", 4096, 4096, 14336, 8, 2, "bf16", "bf16", (True,), None, 104),
     # Fine-grained, skewed load (some experts >10x the mean, some empty), fp16.
     "skewed": Workload("skewed", 8192, 2048, 768, 128, 8, "f16", "f16", (False,), 1.2, 105),
+    # Group-limited sigmoid routing (section 10) on the decode shape's 256 experts: 8 groups of
+    # 32, 4 groups chosen by the sum of their two best corrected scores, top-8, renormalised,
+    # scaled by 2.5.  Routing only, many rows: 0.5% tied rows, 0.3% rows with NaN/inf logits.
+    "sigmoid_route": Workload("sigmoid_route", 65536, 7168, None, 256, 8, "bf16", "bf16", (True,), None, 106,
+                              special=(164, 164, 66, 66, 66),
+                              sigmoid=SigmoidRouting(8, 4, True, True, 2.5, 0.05)),
+    # The decode layer routed that way.
+    "sigmoid_decode": Workload("sigmoid_decode", 16, 7168, 2048, 256, 8, "bf16", "bf16", (True,), None, 107,
+                               sigmoid=SigmoidRouting(8, 4, True, True, 2.5, 0.05)),
 }
 
 
@@ -187,6 +213,62 @@ def make_logits(w: Workload):
                 row[:] = -np.inf
     logits = torch.from_numpy(vals).to(DTYPES[w.logits_dtype])
     return logits, special
+
+
+def make_sigmoid_logits(w: Workload):
+    """Router logits and FP32 correction bias for a group-limited sigmoid workload.
+
+    Logits: N(0, 1) (stream 0), rounded to the logits dtype and separated like the softmax
+    workloads.  Bias [E]: N(0, bias_std) in FP32 (stream 1), with twins so that exact ties can
+    be built: in every group the experts 2i and 2i + 1 (i < per / 4) share a bias value, and the
+    last group repeats the second-to-last group's biases.  Returns ``(logits, bias, special)``
+    (CPU tensors; ``special`` maps each SIGMOID_SPECIAL_KINDS entry to its sorted rows)."""
+    sg = w.sigmoid
+    if sg is None:
+        raise ValueError(f"workload {w.name!r} does not use sigmoid routing")
+    T, E, G = w.T, w.E, sg.groups
+    per = E // G
+    rng0, rng1, rng2 = _np_rng(w.seed, 0), _np_rng(w.seed, 1), _np_rng(w.seed, 2)
+    bias = (rng1.standard_normal(E) * sg.bias_std).astype(np.float32)
+    for g in range(G):
+        for i in range(per // 4):
+            bias[g * per + 2 * i + 1] = bias[g * per + 2 * i]
+    if G >= 2:
+        bias[(G - 1) * per:] = bias[(G - 2) * per:(G - 1) * per]
+    noise = rng0.standard_normal((T, E), dtype=np.float32)
+    vals = _round_to(noise, w.logits_dtype)
+    if E > 1:
+        vals = _separate(vals, noise, np.zeros(E, np.float32), w.logits_dtype, rng0)
+
+    n_special = sum(w.special)
+    positions = np.sort(rng2.choice(T, size=n_special, replace=False)) if n_special else np.zeros(0, int)
+    perm = rng2.permutation(n_special)
+    special = {}
+    cursor = 0
+    for kind, count in zip(SIGMOID_SPECIAL_KINDS, w.special):
+        rows = np.sort(positions[perm[cursor:cursor + count]])
+        cursor += count
+        special[kind] = rows
+        for r in rows:
+            row = vals[r]
+            if kind == "expert_tie":
+                # a bias-twin pair takes the row's largest logit
+                if per < 4:
+                    raise ValueError("expert ties need at least 4 experts per group")
+                g, i = int(rng2.integers(G)), int(rng2.integers(per // 4))
+                row[g * per + 2 * i] = row[g * per + 2 * i + 1] = row.max()
+            elif kind == "group_tie":
+                if G < 2:
+                    raise ValueError("group ties need two groups")
+                row[(G - 1) * per:] = row[(G - 2) * per:(G - 1) * per]
+            elif kind == "nan":
+                row[rng2.integers(E)] = np.nan
+            elif kind == "posinf":
+                row[rng2.integers(E)] = np.inf
+            elif kind == "neginf":
+                row[rng2.integers(E)] = -np.inf
+    logits = torch.from_numpy(vals).to(DTYPES[w.logits_dtype])
+    return logits, torch.from_numpy(bias), special
 
 
 def _torch_gen(device, seed: int, stream: int, sub: int = 0) -> torch.Generator:

@@ -25,7 +25,8 @@ STATUS = {0: "ok", 1: "shape", 2: "dtype", 3: "argument", 4: "device", 5: "unsup
           7: "runtime"}
 
 KERNELS = ("route", "dispatch_count", "dispatch_scan", "dispatch_rank", "dispatch_copy", "experts_plan",
-           "experts_gate_up", "experts_down", "combine", "experts_gate_up_reduce", "experts_down_reduce")
+           "experts_gate_up", "experts_down", "combine", "experts_gate_up_reduce", "experts_down_reduce",
+           "route_sigmoid_grouped")
 
 
 class MoeError(RuntimeError):
@@ -37,6 +38,12 @@ class MoeError(RuntimeError):
 
 class RoutingOptions(ctypes.Structure):
     _fields_ = [("top_k", ctypes.c_int64), ("renormalize", ctypes.c_int32)]
+
+
+class GroupRoutingOptions(ctypes.Structure):
+    """GroupRoutingOptions of user guide section 10 (group-limited sigmoid routing)."""
+    _fields_ = [("top_k", ctypes.c_int64), ("groups", ctypes.c_int64), ("selected_groups", ctypes.c_int64),
+                ("group_top_two", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("scale", ctypes.c_double)]
 
 
 class ExpertsView(ctypes.Structure):
@@ -73,11 +80,14 @@ def lib() -> ctypes.CDLL:
         L.rudnn_moe_forward_workspace_size.argtypes = [EXP, I64, I64, I32]
         L.rudnn_moe_forward_workspace_size.restype = SZ
         L.rudnn_moe_forward.argtypes = [EXP, P, P, I32, I64, RoutingOptions, P, P, SZ, P]
+        L.rudnn_moe_route_sigmoid_grouped.argtypes = [P, I32, I64, I64, P, GroupRoutingOptions, P, P, P]
+        L.rudnn_moe_forward_sigmoid_grouped.argtypes = [EXP, P, P, I32, I64, P, GroupRoutingOptions, P, P, SZ, P]
         L.rudnn_moe_status_string.argtypes = [I32]
         L.rudnn_moe_status_string.restype = ctypes.c_char_p
         L.rudnn_moe_time_next_launch.argtypes = [I32, P, P]
         for f in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
-                  "rudnn_moe_forward", "rudnn_moe_time_next_launch"):
+                  "rudnn_moe_forward", "rudnn_moe_time_next_launch", "rudnn_moe_route_sigmoid_grouped",
+                  "rudnn_moe_forward_sigmoid_grouped"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -153,6 +163,10 @@ class SwiGluExperts:
                 workspace=None) -> torch.Tensor:
         return forward(self, input, logits, top_k, renormalize, out=out, workspace=workspace)
 
+    def forward_sigmoid_grouped(self, input: torch.Tensor, logits: torch.Tensor, bias, options: GroupRoutingOptions,
+                                out=None, workspace=None) -> torch.Tensor:
+        return forward_sigmoid_grouped(self, input, logits, bias, options, out=out, workspace=workspace)
+
     def forward_dispatched(self, d: "Dispatched", out=None, workspace=None) -> torch.Tensor:
         return experts_forward(self, d.dispatched, d.expert_offsets, out=out, workspace=workspace)
 
@@ -165,6 +179,29 @@ def route(logits: torch.Tensor, top_k: int, renormalize: bool):
     w = torch.empty(T, top_k, dtype=logits.dtype, device=logits.device)
     _check("rudnn_moe_route", lib().rudnn_moe_route(_ptr(logits), _dt(logits), T, E, RoutingOptions(top_k, int(renormalize)),
                                                     _ptr(idx), _ptr(w), _stream(logits)))
+    return idx, w
+
+
+def _bias(bias, logits: torch.Tensor):
+    if bias is None:
+        return None
+    bias = _contig(bias, "bias")
+    if bias.dtype != torch.float32 or bias.shape != (logits.shape[1],) or bias.device != logits.device:
+        raise ValueError("the correction bias is FP32 [E] on the logits' device")
+    return bias
+
+
+def route_sigmoid_grouped(logits: torch.Tensor, bias, options: GroupRoutingOptions):
+    """Group-limited sigmoid routing (user guide section 10).  ``bias``: FP32 [E] or None.
+    Returns ``(expert_indices [T, k] int32 holding the uint32 ids, weights [T, k] logits dtype)``."""
+    logits = _contig(logits, "logits")
+    bias = _bias(bias, logits)
+    T, E = logits.shape
+    k = options.top_k
+    idx = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, k, dtype=logits.dtype, device=logits.device)
+    _check("rudnn_moe_route_sigmoid_grouped", lib().rudnn_moe_route_sigmoid_grouped(
+        _ptr(logits), _dt(logits), T, E, _ptr(bias), options, _ptr(idx), _ptr(w), _stream(logits)))
     return idx, w
 
 
@@ -243,5 +280,23 @@ def forward(experts: SwiGluExperts, input: torch.Tensor, logits: torch.Tensor, t
                                 device=input.device)
     _check("rudnn_moe_forward", lib().rudnn_moe_forward(
         ctypes.byref(experts.view), _ptr(input), _ptr(logits), _dt(logits), T, RoutingOptions(top_k, int(renormalize)),
+        _ptr(out), _ptr(workspace), workspace.numel(), _stream(input)))
+    return out
+
+
+def forward_sigmoid_grouped(experts: SwiGluExperts, input: torch.Tensor, logits: torch.Tensor, bias,
+                            options: GroupRoutingOptions, out=None, workspace=None) -> torch.Tensor:
+    """The whole local forward with group-limited sigmoid routing (user guide section 10)."""
+    input = _contig(input, "input")
+    logits = _contig(logits, "logits")
+    bias = _bias(bias, logits)
+    T = input.shape[0]
+    if out is None:
+        out = torch.empty_like(input)
+    if workspace is None:
+        workspace = torch.empty(max(forward_workspace_size(experts, T, options.top_k, logits.dtype), 1),
+                                dtype=torch.uint8, device=input.device)
+    _check("rudnn_moe_forward_sigmoid_grouped", lib().rudnn_moe_forward_sigmoid_grouped(
+        ctypes.byref(experts.view), _ptr(input), _ptr(logits), _dt(logits), T, _ptr(bias), options,
         _ptr(out), _ptr(workspace), workspace.numel(), _stream(input)))
     return out

@@ -28,11 +28,11 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     for required in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
-                     "rudnn_moe_forward"):
+                     "rudnn_moe_forward", "rudnn_moe_route_sigmoid_grouped", "rudnn_moe_forward_sigmoid_grouped"):
         assert required in names
 
 
@@ -153,6 +153,58 @@ def test_forward_validation(L):
 
 
 def test_timing_hook_validation(L):
-    assert L.rudnn_moe_time_next_launch(11, None, None) == ARGUMENT
+    assert L.rudnn_moe_time_next_launch(12, None, None) == ARGUMENT
     assert L.rudnn_moe_time_next_launch(-1, None, None) == ARGUMENT
     assert L.rudnn_moe_time_next_launch(0, None, None) == OK
+
+
+def gopts(k=8, groups=8, sel=4, top_two=1, renorm=1, scale=2.5):
+    return moe.GroupRoutingOptions(k, groups, sel, top_two, renorm, scale)
+
+
+def test_route_sigmoid_grouped_validation(L):
+    r = L.rudnn_moe_route_sigmoid_grouped
+    idx, w = FAKE + 2**20, FAKE + 2**21
+
+    def call(T=4, E=256, bias=None, o=None, ldt=2, lg=FAKE, i=idx, ww=w):
+        return r(lg, ldt, T, E, bias, gopts() if o is None else o, i, ww, None)
+
+    assert call(T=-1) == SHAPE
+    assert call(E=0) == SHAPE
+    assert call(E=2048, o=gopts(groups=8)) == ARGUMENT          # E > 1024
+    assert call(o=gopts(groups=0)) == ARGUMENT
+    assert call(o=gopts(groups=256)) == ARGUMENT                # groups > 128
+    assert call(E=250, o=gopts(groups=8)) == ARGUMENT           # E % groups
+    assert call(o=gopts(sel=0)) == ARGUMENT
+    assert call(o=gopts(sel=9)) == ARGUMENT                     # selected_groups > groups
+    assert call(o=gopts(k=0)) == ARGUMENT
+    assert call(o=gopts(k=65, sel=8)) == ARGUMENT               # top_k > 64
+    assert call(o=gopts(k=33, sel=1)) == ARGUMENT               # top_k > selected experts (1 x 32)
+    assert call(E=8, o=gopts(k=1, groups=8, sel=1, top_two=1)) == ARGUMENT   # one expert per group, top-two
+    assert call(o=gopts(scale=0.0)) == ARGUMENT
+    assert call(o=gopts(scale=float("inf"))) == ARGUMENT
+    assert call(o=gopts(scale=float("nan"))) == ARGUMENT
+    assert call(ldt=7) == DTYPE
+    assert call(T=2**28, o=gopts(k=16)) == UNSUPPORTED          # T*k >= 2^31
+    assert call(lg=None) == ARGUMENT
+    assert call(i=None) == ARGUMENT
+    assert call(i=FAKE + 8) == ARGUMENT                         # indices overlap the logits
+    assert call(bias=w + 8) == ARGUMENT                         # weights overlap the bias
+    assert call(T=0) == OK
+
+
+def test_forward_sigmoid_grouped_validation(L):
+    f = L.rudnn_moe_forward_sigmoid_grouped
+    E, H, I, T = 16, 64, 128, 4
+    exv = moe.ExpertsView(FAKE, FAKE + 2**30, FAKE + 2**31, E, H, I, 2)
+    ws = L.rudnn_moe_forward_workspace_size(ctypes.byref(exv), T, 2, 2)
+
+    def call(o, T=T, bias=None, wsz=ws):
+        return f(ctypes.byref(exv), FAKE + 2**33, FAKE + 2**34, 2, T, bias, o, FAKE + 2**35, FAKE + 2**36, wsz, None)
+
+    assert call(gopts(k=2, groups=4, sel=2), T=-1) == SHAPE
+    assert call(gopts(k=2, groups=3, sel=2)) == ARGUMENT        # 16 % 3
+    assert call(gopts(k=9, groups=4, sel=2)) == ARGUMENT        # 9 > 2 x 4
+    assert call(gopts(k=2, groups=4, sel=2), wsz=ws - 1) == WORKSPACE
+    assert call(gopts(k=2, groups=4, sel=2), bias=FAKE + 2**35 + 64) == ARGUMENT   # bias overlaps the output
+    assert call(gopts(k=2, groups=4, sel=2), T=0) == OK

@@ -16,6 +16,7 @@ from mixture_experts_layer_23_amd import moe
 from mixture_experts_layer_23_amd.inputs import DTYPES, WORKLOADS, Workload, make_experts, make_tokens
 from mixture_experts_layer_23_amd.inputs import make_logits as _make_logits
 from oracle import oracle
+from parity_util import assert_close, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -31,39 +32,11 @@ def make_logits(w):
     return _LOGITS[w]
 
 
-def say(*a):
-    print("[gpu-case]", *a, flush=True)
-    sys.stdout.flush()
-
-
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     moe.lib()
-
-
-def assert_close(got: torch.Tensor, ref: torch.Tensor, dt: str, what: str = ""):
-    g = got.detach().double().cpu()
-    r = ref.detach().double().cpu()
-    assert g.shape == r.shape, what
-    gn, rn = torch.isnan(g), torch.isnan(r)
-    assert torch.equal(gn, rn), f"{what}: NaN positions differ ({int((gn != rn).sum())} elements)"
-    inf = torch.isinf(r)
-    assert torch.equal(g[inf], r[inf]), f"{what}: infinities differ"
-    fin = torch.isfinite(r)
-    if not fin.any():
-        return
-    d = (g - r).abs()[fin]
-    ra = r.abs()[fin]
-    if dt == "f32":
-        bound = 1e-4 * ra + 1e-5
-    else:
-        rms = r[fin].pow(2).mean().sqrt()
-        bound = 2e-2 * ra + 2e-2 * rms
-    bad = d > bound
-    assert not bad.any(), (f"{what}: {int(bad.sum())}/{d.numel()} elements out of tolerance; "
-                           f"max abs err {d.max():.3g}, max rel {(d / ra.clamp_min(1e-30)).max():.3g}")
 
 
 def gpu_route(logits, k, renorm):
