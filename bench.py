@@ -90,6 +90,8 @@ def main():
                     help="target CPU time of the oracle baseline sample (sized from an 8-token probe)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-stages", action="store_true")
+    ap.add_argument("--no-sigmoid", action="store_true",
+                    help="skip the group-limited sigmoid routing measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -170,9 +172,10 @@ def main():
     gu_tflops = gu_flops / (gu_ms / 1e3) / 1e12
 
     # per-kernel breakdown (separate pass, every kernel timed)
-    stage_ev = {kn: [(hip.event(), hip.event()) for _ in range(max(3, K // 4))] for kn in moe.KERNELS}
+    fwd_kernels = [kn for kn in moe.KERNELS if kn != "route_sigmoid_grouped"]  # what the softmax forward launches
+    stage_ev = {kn: [(hip.event(), hip.event()) for _ in range(max(3, K // 4))] for kn in fwd_kernels}
     for i in range(max(3, K // 4)):
-        for kn in moe.KERNELS:
+        for kn in fwd_kernels:
             moe.time_next_launch(kn, *stage_ev[kn][i])
         step()
     torch.cuda.synchronize()
@@ -267,6 +270,75 @@ def main():
             gbs = hbm_bytes[name] / (us / 1e6) / 1e9
             hbm[name] = {"us": us, "bytes": hbm_bytes[name], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
 
+    # ---------------- group-limited sigmoid routing (section 10) ----------------
+    sig = None
+    if not args.no_sigmoid:
+        if not args.no_hbm_stages:
+            del x2, d2, o2, dws, lg2, idx2, wt2
+        torch.cuda.empty_cache()
+        from mixture_experts_layer_23_amd.inputs import make_sigmoid_logits
+        ws_ = WORKLOADS["sigmoid_route"]
+        log("generating", ws_.name)
+        lg3_cpu, b3_cpu, _ = make_sigmoid_logits(ws_)
+        lg3, b3 = lg3_cpu.to(dev), b3_cpu.to(dev)
+        sg = ws_.sigmoid
+        o3 = moe.GroupRoutingOptions(ws_.top_k, sg.groups, sg.selected_groups, int(sg.group_top_two),
+                                     int(sg.renormalize), sg.scale)
+        T3, E3, k3 = ws_.T, ws_.E, ws_.top_k
+        idx3 = torch.empty(T3, k3, dtype=torch.int32, device=dev)
+        wt3 = torch.empty(T3, k3, dtype=lg3.dtype, device=dev)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        reps = 5
+        ev3 = [(hip.event(), hip.event()) for _ in range(reps)]
+        for i in range(reps + 1):
+            flush.fill_(i & 0xff)
+            if i:
+                hip.record(ev3[i - 1][0], stream)
+            rc = moe.lib().rudnn_moe_route_sigmoid_grouped(lg3.data_ptr(), 2, T3, E3, b3.data_ptr(), o3,
+                                                           idx3.data_ptr(), wt3.data_ptr(), stream)
+            assert rc == 0, rc
+            if i:
+                hip.record(ev3[i - 1][1], stream)
+        torch.cuda.synchronize()
+        us3 = float(np.median([hip.ms(a, b) for a, b in ev3])) * 1e3
+        b3_bytes = T3 * E3 * 2 + E3 * 4 + T3 * k3 * (4 + 2)
+        sig = {"route": {"workload": f"T={T3} E={E3} groups={sg.groups} selected={sg.selected_groups} top-two "
+                                     f"k={k3} bf16 logits + FP32 bias, cache flushed",
+                         "us": us3, "bytes": b3_bytes, "GBps": b3_bytes / (us3 / 1e6) / 1e9,
+                         "hbm_frac": b3_bytes / (us3 / 1e6) / 1e9 / HBM_PEAK_GBS}}
+        del lg3, b3, idx3, wt3, flush
+        # the decode-shaped layer routed this way (256 experts, weights streamed from HBM)
+        wd = WORKLOADS["sigmoid_decode"]
+        log("generating", wd.name)
+        lgd_cpu, bd_cpu, _ = make_sigmoid_logits(wd)
+        lgd, bd = lgd_cpu.to(dev), bd_cpu.to(dev)
+        xd = make_tokens(wd, dev)
+        gd, ud, dd = make_experts(wd, dev)
+        exd = moe.SwiGluExperts(gd, ud, dd)
+        sgd = wd.sigmoid
+        od = moe.GroupRoutingOptions(wd.top_k, sgd.groups, sgd.selected_groups, int(sgd.group_top_two),
+                                     int(sgd.renormalize), sgd.scale)
+        outd = torch.empty_like(xd)
+        wsd = torch.empty(moe.forward_workspace_size(exd, wd.T, wd.top_k, lgd.dtype), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            exd.forward_sigmoid_grouped(xd, lgd, bd, od, out=outd, workspace=wsd)
+        torch.cuda.synchronize()
+        nd = 20
+        a_, b_ = hip.event(), hip.event()
+        hip.record(a_, stream)
+        for _ in range(nd):
+            exd.forward_sigmoid_grouped(xd, lgd, bd, od, out=outd, workspace=wsd)
+        hip.record(b_, stream)
+        msd = hip.ms(a_, b_) / nd
+        active = int(torch.unique(moe.route_sigmoid_grouped(lgd, bd, od)[0]).numel())
+        wbytes = active * 3 * wd.H * wd.I * 2
+        sig["decode_forward"] = {"workload": f"T={wd.T} H={wd.H} I={wd.I} E={wd.E} k={wd.top_k} bf16, "
+                                             f"{active} active experts",
+                                 "ms": msd, "tokens_per_s": wd.T / (msd / 1e3),
+                                 "weight_GBps": wbytes / (msd / 1e3) / 1e9,
+                                 "hbm_frac": wbytes / (msd / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del gd, ud, dd, exd, wsd
+
     traffic = traffic_for("experts_gate_up", "mixtral")
     result = {
         "metric": METRIC,
@@ -290,6 +362,7 @@ def main():
         "cpu_baseline": cpu,
         "stages": stages,
         "hbm_stages": hbm,
+        "sigmoid_routing": sig,
     }
     print(json.dumps(result), flush=True)
 

@@ -21,7 +21,6 @@
 namespace rudnn {
 
 constexpr int SIG_THREADS = 256;
-constexpr int SIG_MAX_GPL = 16;  // groups per lane: groups <= min(E, 128) <= 16 * G
 
 template <int G>
 __device__ __forceinline__ uint64_t sig_group_max(uint64_t key) {
@@ -49,6 +48,8 @@ __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __
                                                                     int renorm, float scale,
                                                                     uint32_t* __restrict__ idx, LT* __restrict__ w) {
     constexpr int RPB = SIG_THREADS / G;
+    // groups per lane: groups <= min(E, 128) <= min(NPER * G, 128)
+    constexpr int GPL = (128 + G - 1) / G < NPER ? (128 + G - 1) / G : NPER;
     extern __shared__ float smem[];  // c [RPB][E], s [RPB][E], winners [RPB][k]
     const int lane = lane_id(), l = lane % G, rb = threadIdx.x / G;
     const int64_t row = (int64_t)blockIdx.x * RPB + rb;
@@ -59,44 +60,74 @@ __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __
     const int e0 = l * NPER, per = E / groups;
     const LT* x = logits + (live ? row : 0) * (int64_t)E;
 
-    // 1. sigmoid and corrected scores
+    // 1. sigmoid and corrected scores (slots past E are computed on a clamped id, then masked)
     float c[NPER];
     bool bad = false;
 #pragma unroll
     for (int s = 0; s < NPER; ++s) {
         const int e = e0 + s;
-        c[s] = 0.f;
+        const int ec = e < E ? e : E - 1;
+        const float xv = to_f32(x[ec]);
+        const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-xv));  // +inf -> 1, -inf -> 0, NaN -> NaN
+        const float cv = bias ? sg + bias[ec] : sg;
+        c[s] = cv;
         if (e < E) {
-            const float xv = live ? to_f32(x[e]) : 0.f;
-            const float sg = 1.0f / (1.0f + expf(-xv));  // +inf -> 1, -inf -> 0, NaN -> NaN
-            c[s] = bias ? sg + bias[e] : sg;
-            bad |= c[s] != c[s];
-            sc[e] = c[s];
+            bad |= cv != cv;
+            sc[e] = cv;
             ss[e] = sg;
         }
     }
     __syncthreads();
 
-    // 2. group scores
-    uint64_t gkey[SIG_MAX_GPL];
+    // 2. group scores: from registers when each group is a power-of-two run of whole lane chunks,
+    //    else from LDS (lane l taking groups l, l + G, ...)
+    uint64_t gkey[GPL];
 #pragma unroll
-    for (int q = 0; q < SIG_MAX_GPL; ++q) {
-        const int g = l + q * G;
-        gkey[q] = 0;
-        if (g < groups) {
-            float t1 = -INFINITY, t2 = -INFINITY;  // the two largest corrected scores
-            for (int i = 0; i < per; ++i) {
-                const float v = sc[g * per + i];
-                if (v > t1) {
-                    t2 = t1;
-                    t1 = v;
-                } else if (v > t2) {
-                    t2 = v;
-                }
+    for (int q = 0; q < GPL; ++q) gkey[q] = 0;
+    const int lpg = per / NPER;  // lanes per group
+    if (per % NPER == 0 && (lpg & (lpg - 1)) == 0) {
+        float t1 = -INFINITY, t2 = -INFINITY;  // this lane's two largest
+#pragma unroll
+        for (int s = 0; s < NPER; ++s) {
+            const float v = c[s];
+            if (v > t1) {
+                t2 = t1;
+                t1 = v;
+            } else if (v > t2) {
+                t2 = v;
             }
+        }
+        for (int m = 1; m < lpg; m <<= 1) {  // merge the top two of the group's lanes
+            const float o1 = __shfl_xor(t1, m, 64), o2 = __shfl_xor(t2, m, 64);
+            const float n1 = fmaxf(t1, o1);
+            const float n2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+            t1 = n1, t2 = n2;
+        }
+        const int g = e0 / per;
+        if (e0 < E && e0 % per == 0) {  // the group's first lane holds its key
             const float gs = top_two ? t1 + t2 : t1;
             bad |= gs != gs;
-            gkey[q] = sig_key(gs, (uint32_t)g);
+            gkey[0] = sig_key(gs, (uint32_t)g);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < GPL; ++q) {
+            const int g = l + q * G;
+            if (g < groups) {
+                float t1 = -INFINITY, t2 = -INFINITY;  // the two largest corrected scores
+                for (int i = 0; i < per; ++i) {
+                    const float v = sc[g * per + i];
+                    if (v > t1) {
+                        t2 = t1;
+                        t1 = v;
+                    } else if (v > t2) {
+                        t2 = v;
+                    }
+                }
+                const float gs = top_two ? t1 + t2 : t1;
+                bad |= gs != gs;
+                gkey[q] = sig_key(gs, (uint32_t)g);
+            }
         }
     }
     const int gshift = lane - l;
@@ -109,7 +140,7 @@ __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __
     for (int r = 0; r < nsel; ++r) {
         uint64_t best = 0;
 #pragma unroll
-        for (int q = 0; q < SIG_MAX_GPL; ++q) best = max(best, gkey[q] < prev ? gkey[q] : (uint64_t)0);
+        for (int q = 0; q < GPL; ++q) best = max(best, gkey[q] < prev ? gkey[q] : (uint64_t)0);
         const uint64_t win = sig_group_max<G>(best);
         prev = win;
         const uint32_t g = 0xffffffffu - (uint32_t)win;
@@ -164,7 +195,6 @@ template <typename LT, int NPER, int G>
 static void launch_sig_g(const LT* l, const float* bias, int64_t T, int E, int k, int groups, int nsel, int top_two,
                          int renorm, float scale, uint32_t* idx, LT* w, hipStream_t s) {
     constexpr int RPB = SIG_THREADS / G;
-    static_assert(SIG_MAX_GPL >= NPER, "every lane has room for its share of at most min(E, 128) groups");
     const dim3 grid((unsigned)((T + RPB - 1) / RPB)), block(SIG_THREADS);
     const size_t smem = (size_t)RPB * (2 * E + k) * 4;
     route_sigmoid_kernel<LT, NPER, G><<<grid, block, smem, s>>>(l, bias, T, E, k, groups, nsel, top_two, renorm,
@@ -180,19 +210,21 @@ static hipError_t launch_sig_t(const void* logits, const float* bias, int64_t T,
     const int Ei = (int)E, ki = (int)k, gi = (int)groups, ni = (int)nsel, t2 = top_two ? 1 : 0, r = renorm ? 1 : 0;
     const float sc = (float)scale;
     timing_before(RUDNN_MOE_KERNEL_ROUTE_SIGMOID_GROUPED, s);
-    // lanes per row: the smallest power of two G with 16 G >= E (at most 16 groups per lane)
-    if (E <= 16)
-        launch_sig_g<LT, 16, 1>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    // lanes per row: the smallest power of two G with 8 G >= E (16 G >= E once G reaches 64)
+    if (E <= 8)
+        launch_sig_g<LT, 8, 1>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    else if (E <= 16)
+        launch_sig_g<LT, 8, 2>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 32)
-        launch_sig_g<LT, 16, 2>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 8, 4>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 64)
-        launch_sig_g<LT, 16, 4>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 8, 8>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 128)
-        launch_sig_g<LT, 16, 8>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 8, 16>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 256)
-        launch_sig_g<LT, 16, 16>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 8, 32>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 512)
-        launch_sig_g<LT, 16, 32>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 8, 64>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else
         launch_sig_g<LT, 16, 64>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     timing_after(RUDNN_MOE_KERNEL_ROUTE_SIGMOID_GROUPED, s);
