@@ -43,6 +43,10 @@
  *  - SwiGLU: h = silu(gate . x) * (up . x), silu(z) = z / (1 + exp(-z)); y = down . h;
  *    no biases (section 5: "bias-freie Expertengewichte").
  *  - An index >= E given to dispatch gets map -1 and its token's combined row is NaN.
+ *  - The fused router projection (section 5 leaves the gate projection to the caller; this is
+ *    that caller step): logits[t, e] = sum_h input[t, h] * router[e, h] with the router [E, H]
+ *    in the token dtype, summed in double and rounded once to the token dtype, which is then
+ *    the logits dtype; routing follows section 4 unchanged.
  *  - Sigmoid routing decides in FP32, the precision the guide gives the bias: s32 = the
  *    sigmoid rounded once to FP32, corrected score c = s32 + bias in FP32, a group score is the
  *    largest c of the group or the FP32 sum of its two largest; groups and then experts are
@@ -253,6 +257,37 @@ int oracle_route(const void* logits, int ldt, int64_t T, int64_t E, int64_t k, i
         free(taken);
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Router projection + route: the caller's gate projection (section 5) followed by the     */
+/* section 4 routing.                                                                     */
+/* ------------------------------------------------------------------------------------ */
+
+/* input [T,H] and router [E,H] in dt -> logits [T,E] in dt (double sum, one rounding). */
+int oracle_project(const void* input, int dt, const void* router, int64_t T, int64_t H, int64_t E, void* logits) {
+    if (T < 0 || H < 1 || E < 1) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; ++h) acc += load_val(input, dt, t * H + h) * load_val(router, dt, e * H + h);
+            store_val(logits, dt, t * E + e, acc);
+        }
+    }
+    return 0;
+}
+
+/* logits = project(input, router); then oracle_route on them.  logits_out (may be NULL)
+ * receives the rounded logits. */
+int oracle_route_projected(const void* input, int dt, const void* router, int64_t T, int64_t H, int64_t E,
+                           int64_t k, int renormalize, uint32_t* expert_indices, void* weights, void* logits_out) {
+    if (T < 0 || H < 1 || E < 1 || k < 1 || k > E) return -1;
+    void* lg = logits_out ? logits_out : malloc(dt_size(dt) * (size_t)(T * E > 0 ? T * E : 1));
+    int rc = oracle_project(input, dt, router, T, H, E, lg);
+    if (!rc) rc = oracle_route(lg, dt, T, E, k, renormalize, expert_indices, weights, NULL);
+    if (!logits_out) free(lg);
+    return rc;
 }
 
 /* ------------------------------------------------------------------------------------ */
@@ -561,6 +596,21 @@ int oracle_forward_sigmoid_grouped(const void* input, int dt, const void* logits
     int rc = oracle_route_sigmoid_grouped(logits, ldt, T, E, bias, k, groups, selected_groups, top_two, renormalize,
                                           scale, idx, w, NULL);
     if (!rc) rc = forward_routed(input, dt, idx, w, ldt, T, E, k, gate, up, down, H, I, output);
+    free(w);
+    free(idx);
+    return rc;
+}
+
+/* Full local forward from the hidden states: project -> route -> dispatch -> experts -> combine. */
+int oracle_forward_projected(const void* input, int dt, const void* router, int64_t T, int64_t E, int64_t k,
+                             int renormalize, const void* gate, const void* up, const void* down, int64_t H,
+                             int64_t I, void* output) {
+    if (T < 0 || E < 1 || k < 1 || k > E || H < 1) return -1;
+    if (T == 0) return 0;
+    uint32_t* idx = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(T * k));
+    void* w = malloc(dt_size(dt) * (size_t)(T * k));
+    int rc = oracle_route_projected(input, dt, router, T, H, E, k, renormalize, idx, w, NULL);
+    if (!rc) rc = forward_routed(input, dt, idx, w, dt, T, E, k, gate, up, down, H, I, output);
     free(w);
     free(idx);
     return rc;

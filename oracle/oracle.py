@@ -38,6 +38,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_experts_forward.argtypes = [P, P, I64, I32, P, P, P, I64, I64, P, P]
         L.oracle_combine.argtypes = [P, I32, P, P, I32, I64, I64, I64, P]
         L.oracle_forward.argtypes = [P, I32, P, I32, I64, I64, I64, I32, P, P, P, I64, I64, P]
+        L.oracle_project.argtypes = [P, I32, P, I64, I64, I64, P]
+        L.oracle_route_projected.argtypes = [P, I32, P, I64, I64, I64, I64, I32, P, P, P]
+        L.oracle_forward_projected.argtypes = [P, I32, P, I64, I64, I64, I32, P, P, P, I64, I64, P]
         D = ctypes.c_double
         L.oracle_route_sigmoid_grouped.argtypes = [P, I32, I64, I64, P, I64, I64, I64, I32, I32, D, P, P, P]
         L.oracle_forward_sigmoid_grouped.argtypes = [P, I32, P, I32, I64, I64, P, I64, I64, I64, I32, I32, D,
@@ -47,7 +50,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_set_num_threads.argtypes = [I32]
         for f in ("oracle_route", "oracle_dispatch", "oracle_expert_rows", "oracle_experts_forward",
                   "oracle_combine", "oracle_forward", "oracle_num_threads", "oracle_route_sigmoid_grouped",
-                  "oracle_forward_sigmoid_grouped"):
+                  "oracle_forward_sigmoid_grouped", "oracle_project", "oracle_route_projected",
+                  "oracle_forward_projected"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -230,4 +234,49 @@ def forward_sigmoid_grouped(x: torch.Tensor, logits: torch.Tensor, bias, top_k: 
                                               H, I, _p(out))
     if rc:
         raise ValueError("oracle_forward_sigmoid_grouped: bad arguments")
+    return out
+
+
+def project(x: torch.Tensor, router: torch.Tensor) -> torch.Tensor:
+    """logits [T, E] = x [T, H] . router [E, H]^T, summed in double, rounded once to x's dtype."""
+    x, router = _cpu(x), _cpu(router)
+    T, H = x.shape
+    E = router.shape[0]
+    if router.dtype != x.dtype or router.shape[1] != H:
+        raise ValueError("router must be [E, H] in the token dtype")
+    out = torch.empty(T, E, dtype=x.dtype)
+    if lib().oracle_project(_p(x), _DT_CODE[x.dtype], _p(router), T, H, E, _p(out)):
+        raise ValueError("oracle_project: bad arguments")
+    return out
+
+
+def route_projected(x: torch.Tensor, router: torch.Tensor, top_k: int, renormalize: bool):
+    """Router projection then section 4 routing.  Returns ``(indices uint32 [T,k], weights [T,k],
+    logits [T,E])`` (weights and logits in the token dtype)."""
+    x, router = _cpu(x), _cpu(router)
+    T, H = x.shape
+    E = router.shape[0]
+    idx = np.empty((T, top_k), np.uint32)
+    w = torch.empty(T, top_k, dtype=x.dtype)
+    lg = torch.empty(T, E, dtype=x.dtype)
+    if lib().oracle_route_projected(_p(x), _DT_CODE[x.dtype], _p(router), T, H, E, top_k, int(bool(renormalize)),
+                                    _p(idx), _p(w), _p(lg)):
+        raise ValueError("oracle_route_projected: bad arguments")
+    return idx, w, lg
+
+
+def forward_projected(x: torch.Tensor, router: torch.Tensor, top_k: int, renormalize: bool, gate=None, up=None,
+                      down=None):
+    """The full local forward from hidden states: projection, route, dispatch, experts, combine."""
+    x, router = _cpu(x), _cpu(router)
+    T, H = x.shape
+    E = router.shape[0]
+    I = 0
+    if gate is not None:
+        gate, up, down = _cpu(gate), _cpu(up), _cpu(down)
+        I = gate.shape[1]
+    out = torch.empty(T, H, dtype=x.dtype)
+    if lib().oracle_forward_projected(_p(x), _DT_CODE[x.dtype], _p(router), T, E, top_k, int(bool(renormalize)),
+                                      _p(gate), _p(up), _p(down), H, I, _p(out)):
+        raise ValueError("oracle_forward_projected: bad arguments")
     return out

@@ -13,6 +13,7 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 PINS = "test_oracle_pins.py"
 SIG = "test_oracle_sigmoid_pins.py"
+PROJ = "test_oracle_projection_pins.py"
 
 MUTANTS = {
     "tie_to_higher_id": ("if (best < 0 || p[e] > p[best]) best = e;", "if (best < 0 || p[e] >= p[best]) best = e;"),
@@ -38,6 +39,10 @@ MUTANTS = {
     "sig_top_two_counts_max_twice": ("if (i != b1 && (b2 < 0 || cg[i] > cg[b2])) b2 = i;", "if (b2 < 0 || cg[i] > cg[b2]) b2 = i;", SIG),
     "sig_groups_not_enforced": ("if (taken[e] || !gsel[e / per]) continue;", "if (taken[e]) continue;", SIG),
     "sig_scale_dropped_with_renorm": ("v *= scale;", "if (!renormalize) v *= scale;", SIG),
+    # router projection, checked against its own pins
+    "proj_router_transposed": ("load_val(router, dt, e * H + h)", "load_val(router, dt, h * E + e)", PROJ),
+    "proj_half_the_sum": ("for (int64_t h = 0; h < H; ++h) acc +=", "for (int64_t h = 0; h < H / 2; ++h) acc +=", PROJ),
+    "proj_wrong_input_stride": ("load_val(input, dt, t * H + h)", "load_val(input, dt, t * E + h)", PROJ),
 }
 
 
