@@ -223,6 +223,48 @@ rudnn_moe_status rudnn_moe_forward_sigmoid_grouped(const rudnn_moe_experts* ex, 
                                                    void* output, void* workspace, size_t workspace_size,
                                                    hipStream_t stream);
 
+/* Bytes of device workspace rudnn_moe_route_projected needs (0 when it needs none): FP32
+ * partial logits when few token tiles make the kernel split the H axis over several blocks. */
+size_t rudnn_moe_route_projected_workspace_size(int64_t T, int64_t H, int64_t E, rudnn_moe_dtype dtype);
+
+/*
+ * route_projected -- the gate projection that section 5 leaves to the caller, fused with the
+ * section 4 routing (rudnn_moe_route) of its result:
+ *   logits[t, e] = dtype( sum_h input[t, h] * router[e, h] )   FP32 accumulation, one rounding
+ * then routed exactly as rudnn_moe_route routes logits [T, E] of that dtype.  The logits stay
+ * on chip; logits_out, when not NULL, receives a copy (the values that were routed).
+ *   input           [T, H]  dtype (F32/F16/BF16), 16-byte aligned
+ *   router          [E, H]  dtype, 16-byte aligned (one row of gate weights per expert)
+ *   logits_out      [T, E]  dtype, written, or NULL
+ *   expert_indices  [T, k]  uint32, written;  weights [T, k] dtype, written
+ * BF16/F16 run on the matrix cores (v_mfma_f32_32x32x16), F32 on v_mfma_f32_32x32x2f32.
+ * workspace: at least rudnn_moe_route_projected_workspace_size(T, H, E, dtype) bytes, 256-B
+ * aligned (may be NULL when that size is 0).
+ * Errors: SHAPE (T < 0, H < 1, E < 1), ARGUMENT (top_k outside [1, E], NULL, overlap), DTYPE,
+ * UNSUPPORTED (E > 256, top_k > 64, H * sizeof(dtype) not a multiple of 16, H >= 2^20,
+ * unaligned input or router, T * top_k >= 2^31), WORKSPACE, DEVICE, RUNTIME.
+ */
+rudnn_moe_status rudnn_moe_route_projected(const void* input, rudnn_moe_dtype dtype, const void* router,
+                                           int64_t T, int64_t H, int64_t E, rudnn_moe_routing_options opt,
+                                           void* logits_out, uint32_t* expert_indices, void* weights,
+                                           void* workspace, size_t workspace_size, hipStream_t stream);
+
+/* Bytes of device workspace rudnn_moe_forward_projected needs. */
+size_t rudnn_moe_forward_projected_workspace_size(const rudnn_moe_experts* ex, int64_t T, int64_t top_k);
+
+/*
+ * forward_projected -- the local forward from the hidden states: route_projected (router
+ * [E, H] in ex->dtype) -> dispatch -> experts -> combine on one stream, bit-identical to
+ * rudnn_moe_route_projected followed by rudnn_moe_dispatch, rudnn_moe_experts_forward and
+ * rudnn_moe_combine.
+ *   input [T, H] ex->dtype;  router [E, H] ex->dtype;  output [T, H] ex->dtype, written
+ * workspace: at least rudnn_moe_forward_projected_workspace_size(ex, T, opt.top_k) bytes.
+ * Errors: as rudnn_moe_forward, with the limits of rudnn_moe_route_projected.
+ */
+rudnn_moe_status rudnn_moe_forward_projected(const rudnn_moe_experts* ex, const void* input, const void* router,
+                                             int64_t T, rudnn_moe_routing_options opt, void* output,
+                                             void* workspace, size_t workspace_size, hipStream_t stream);
+
 /* Static, human-readable name of a status. */
 const char* rudnn_moe_status_string(rudnn_moe_status s);
 
@@ -243,7 +285,9 @@ typedef enum {
     RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE = 9, /* sums the K-split partials of gate_up tail tiles */
     RUDNN_MOE_KERNEL_EXPERTS_DOWN_REDUCE = 10,   /* the same for down */
     RUDNN_MOE_KERNEL_ROUTE_SIGMOID_GROUPED = 11, /* group-limited sigmoid routing */
-    RUDNN_MOE_KERNEL_COUNT = 12
+    RUDNN_MOE_KERNEL_ROUTE_PROJECTED = 12,        /* gate projection + routing */
+    RUDNN_MOE_KERNEL_ROUTE_PROJECTED_REDUCE = 13, /* adds its H-split partials and routes */
+    RUDNN_MOE_KERNEL_COUNT = 14
 } rudnn_moe_kernel;
 
 /* For the calling host thread: record `before` on the launch stream immediately before the

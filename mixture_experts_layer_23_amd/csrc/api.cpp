@@ -90,6 +90,14 @@ rudnn_moe_status check_group_options(int64_t E, const rudnn_moe_group_routing_op
     return RUDNN_MOE_OK;
 }
 
+// Limits of the fused gate projection + routing kernel (route_projected.hip).
+rudnn_moe_status check_projection(rudnn_moe_dtype dt, int64_t H, int64_t E, int64_t k, int64_t T) {
+    if (E > MAX_PROJECTED_EXPERTS || k > MAX_TOP_K || H >= MAX_PROJECTED_HIDDEN) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if ((H * (int64_t)dtype_size(dt)) % 16 || T * k >= INT32_LIMIT || T * E >= ((int64_t)1 << 40))
+        return RUDNN_MOE_ERR_UNSUPPORTED;
+    return RUDNN_MOE_OK;
+}
+
 rudnn_moe_status check_experts_view(const rudnn_moe_experts* ex) {
     if (!ex) return RUDNN_MOE_ERR_ARGUMENT;
     if (ex->num_experts < 1 || ex->hidden < 1 || ex->intermediate < 1) return RUDNN_MOE_ERR_SHAPE;
@@ -181,6 +189,36 @@ rudnn_moe_status rudnn_moe_route_sigmoid_grouped(const void* logits, rudnn_moe_d
                                                 stream));
 }
 
+size_t rudnn_moe_route_projected_workspace_size(int64_t T, int64_t H, int64_t E, rudnn_moe_dtype dt) {
+    if (T < 0 || H < 1 || E < 1 || E > MAX_PROJECTED_EXPERTS || !valid_dtype(dt)) return 0;
+    return projection_workspace_bytes(T, H, E, dt);
+}
+
+rudnn_moe_status rudnn_moe_route_projected(const void* input, rudnn_moe_dtype dt, const void* router, int64_t T,
+                                           int64_t H, int64_t E, rudnn_moe_routing_options opt, void* logits_out,
+                                           uint32_t* idx, void* w, void* workspace, size_t workspace_size,
+                                           hipStream_t stream) {
+    if (T < 0 || H < 1 || E < 1) return RUDNN_MOE_ERR_SHAPE;
+    if (opt.top_k < 1 || opt.top_k > E) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!valid_dtype(dt)) return RUDNN_MOE_ERR_DTYPE;
+    rudnn_moe_status st = check_projection(dt, H, E, opt.top_k, T);
+    if (st != RUDNN_MOE_OK || T == 0) return st;
+    if (!input || !router || !idx || !w) return RUDNN_MOE_ERR_ARGUMENT;
+    if ((uintptr_t)input % 16 || (uintptr_t)router % 16) return RUDNN_MOE_ERR_UNSUPPORTED;
+    const size_t need = projection_workspace_bytes(T, H, E, dt);
+    if (need && (!workspace || workspace_size < need)) return RUDNN_MOE_ERR_WORKSPACE;
+    const size_t es = dtype_size(dt), pk = (size_t)(T * opt.top_k);
+    if (any_overlap({{idx, pk * 4}, {w, pk * es}, {logits_out, logits_out ? (size_t)(T * E) * es : 0},
+                     {workspace, need}},
+                    {{input, (size_t)(T * H) * es}, {router, (size_t)(E * H) * es}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    if ((st = check_device(stream, {input, router, idx, w})) != RUDNN_MOE_OK) return st;
+    if (logits_out && (st = check_device(stream, {logits_out})) != RUDNN_MOE_OK) return st;
+    if (need && (st = check_device(stream, {workspace})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_route_projected(input, dt, router, T, H, E, opt.top_k, opt.renormalize != 0, logits_out,
+                                          idx, w, workspace, stream));
+}
+
 size_t rudnn_moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
     return align_up(sizeof(int32_t) * (size_t)(dispatch_chunks(T * top_k) * E));
@@ -263,10 +301,12 @@ rudnn_moe_status rudnn_moe_combine(const void* y, rudnn_moe_dtype dt, const int3
 
 namespace {
 struct ForwardLayout {
-    size_t idx, w, offsets, map, dws, disp, ews, y, total;
+    size_t idx, w, offsets, map, dws, disp, ews, y, proj, total;
 };
 
-ForwardLayout forward_layout(const rudnn_moe_experts* ex, int64_t T, int64_t k, rudnn_moe_dtype ldt) {
+// projected: the forward from the hidden states, which adds the projection's partial logits.
+ForwardLayout forward_layout(const rudnn_moe_experts* ex, int64_t T, int64_t k, rudnn_moe_dtype ldt,
+                             bool projected = false) {
     ForwardLayout L;
     const size_t es = dtype_size(ex->dtype), pk = (size_t)(T * k);
     size_t off = 0;
@@ -283,6 +323,7 @@ ForwardLayout forward_layout(const rudnn_moe_experts* ex, int64_t T, int64_t k, 
     L.disp = take(pk * ex->hidden * es);
     L.ews = take(experts_workspace_bytes(ex->num_experts, ex->hidden, ex->intermediate, ex->dtype, (int64_t)pk));
     L.y = take(pk * ex->hidden * es);
+    L.proj = take(projected ? projection_workspace_bytes(T, ex->hidden, ex->num_experts, ex->dtype) : 0);
     L.total = off;
     return L;
 }
@@ -296,16 +337,24 @@ size_t rudnn_moe_forward_workspace_size(const rudnn_moe_experts* ex, int64_t T, 
     return forward_layout(ex, T, top_k, logits_dtype).total;
 }
 
+size_t rudnn_moe_forward_projected_workspace_size(const rudnn_moe_experts* ex, int64_t T, int64_t top_k) {
+    if (!ex || T < 0 || top_k < 1 || ex->num_experts < 1 || ex->hidden < 1 || ex->intermediate < 1 ||
+        ex->num_experts > MAX_PROJECTED_EXPERTS || !valid_dtype(ex->dtype))
+        return 0;
+    return forward_layout(ex, T, top_k, ex->dtype, true).total;
+}
+
 }  // extern "C"
 
 namespace {
 
 // The forward of sections 6 and 10: routing (softmax or group-limited sigmoid, chosen by
-// `sig`) -> dispatch -> experts -> combine, after the shared checks.
+// `sig`; or, with a router, softmax routing of the fused gate projection) -> dispatch ->
+// experts -> combine, after the shared checks.
 rudnn_moe_status forward_common(const rudnn_moe_experts* ex, const void* input, const void* logits,
                                 rudnn_moe_dtype ldt, int64_t T, int64_t top_k, int renormalize,
-                                const rudnn_moe_group_routing_options* sig, const float* bias, void* output,
-                                void* workspace, size_t workspace_size, hipStream_t stream) {
+                                const rudnn_moe_group_routing_options* sig, const float* bias, const void* router,
+                                void* output, void* workspace, size_t workspace_size, hipStream_t stream) {
     rudnn_moe_status st = check_experts_view(ex);
     if (st != RUDNN_MOE_OK) return st;
     if (T < 0) return RUDNN_MOE_ERR_SHAPE;
@@ -317,20 +366,25 @@ rudnn_moe_status forward_common(const rudnn_moe_experts* ex, const void* input, 
     if (!valid_dtype(ldt)) return RUDNN_MOE_ERR_DTYPE;
     if (top_k > MAX_TOP_K || T * top_k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
     if ((st = check_experts_rows(ex, T * top_k)) != RUDNN_MOE_OK) return st;
+    if (router && (st = check_projection(ldt, ex->hidden, ex->num_experts, top_k, T)) != RUDNN_MOE_OK) return st;
     if (T == 0) return RUDNN_MOE_OK;
-    if (!input || !logits || !output) return RUDNN_MOE_ERR_ARGUMENT;
-    if (ex->dtype != RUDNN_MOE_F32 && ((uintptr_t)input % 16 || (uintptr_t)output % 16))
+    if (!input || !(router ? router : logits) || !output) return RUDNN_MOE_ERR_ARGUMENT;
+    if ((ex->dtype != RUDNN_MOE_F32 || router) && ((uintptr_t)input % 16 || (uintptr_t)output % 16))
         return RUDNN_MOE_ERR_UNSUPPORTED;
-    const ForwardLayout L = forward_layout(ex, T, top_k, ldt);
+    if (router && (uintptr_t)router % 16) return RUDNN_MOE_ERR_UNSUPPORTED;
+    const ForwardLayout L = forward_layout(ex, T, top_k, ldt, router != nullptr);
     if (!workspace || workspace_size < L.total) return RUDNN_MOE_ERR_WORKSPACE;
     const size_t es = dtype_size(ex->dtype);
     const size_t wsz = (size_t)(ex->num_experts * ex->hidden * ex->intermediate) * es;
     const size_t xb = (size_t)T * ex->hidden * es;
+    const size_t lb = logits ? (size_t)(T * ex->num_experts) * dtype_size(ldt) : 0;
+    const size_t rb = router ? (size_t)(ex->num_experts * ex->hidden) * es : 0;
     if (any_overlap({{output, xb}, {workspace, L.total}},
-                    {{input, xb}, {logits, (size_t)(T * ex->num_experts) * dtype_size(ldt)}, {ex->gate, wsz},
-                     {ex->up, wsz}, {ex->down, wsz}, {bias, bias ? 4 * (size_t)ex->num_experts : 0}}))
+                    {{input, xb}, {logits, lb}, {router, rb}, {ex->gate, wsz}, {ex->up, wsz}, {ex->down, wsz},
+                     {bias, bias ? 4 * (size_t)ex->num_experts : 0}}))
         return RUDNN_MOE_ERR_ARGUMENT;
-    if ((st = check_device(stream, {input, logits, output, workspace, ex->gate, ex->up, ex->down})) != RUDNN_MOE_OK)
+    if ((st = check_device(stream, {input, router ? router : logits, output, workspace, ex->gate, ex->up,
+                                    ex->down})) != RUDNN_MOE_OK)
         return st;
     if (bias && (st = check_device(stream, {bias})) != RUDNN_MOE_OK) return st;
     unsigned char* ws = (unsigned char*)workspace;
@@ -341,10 +395,15 @@ rudnn_moe_status forward_common(const rudnn_moe_experts* ex, const void* input, 
     void* disp = ws + L.disp;
     void* y = ws + L.y;
     const int64_t E = ex->num_experts, k = top_k, H = ex->hidden;
-    hipError_t e = sig ? launch_route_sigmoid_grouped(logits, ldt, bias, T, E, k, sig->groups, sig->selected_groups,
-                                                      sig->group_top_two != 0, sig->renormalize != 0, sig->scale, idx,
-                                                      w, stream)
-                       : launch_route(logits, ldt, T, E, k, renormalize != 0, idx, w, stream);
+    hipError_t e;
+    if (router)
+        e = launch_route_projected(input, ldt, router, T, H, E, k, renormalize != 0, nullptr, idx, w, ws + L.proj,
+                                   stream);
+    else if (sig)
+        e = launch_route_sigmoid_grouped(logits, ldt, bias, T, E, k, sig->groups, sig->selected_groups,
+                                         sig->group_top_two != 0, sig->renormalize != 0, sig->scale, idx, w, stream);
+    else
+        e = launch_route(logits, ldt, T, E, k, renormalize != 0, idx, w, stream);
     if (e == hipSuccess)
         e = launch_dispatch(idx, T, k, E, input, (size_t)H * es, disp, offsets, map, (int32_t*)(ws + L.dws), stream);
     if (e == hipSuccess) e = launch_experts(ex, disp, offsets, T * k, y, ws + L.ews, stream);
@@ -359,8 +418,8 @@ extern "C" {
 rudnn_moe_status rudnn_moe_forward(const rudnn_moe_experts* ex, const void* input, const void* logits,
                                    rudnn_moe_dtype ldt, int64_t T, rudnn_moe_routing_options opt, void* output,
                                    void* workspace, size_t workspace_size, hipStream_t stream) {
-    return forward_common(ex, input, logits, ldt, T, opt.top_k, opt.renormalize, nullptr, nullptr, output, workspace,
-                          workspace_size, stream);
+    return forward_common(ex, input, logits, ldt, T, opt.top_k, opt.renormalize, nullptr, nullptr, nullptr, output,
+                          workspace, workspace_size, stream);
 }
 
 rudnn_moe_status rudnn_moe_forward_sigmoid_grouped(const rudnn_moe_experts* ex, const void* input,
@@ -368,8 +427,16 @@ rudnn_moe_status rudnn_moe_forward_sigmoid_grouped(const rudnn_moe_experts* ex, 
                                                    const float* bias, rudnn_moe_group_routing_options opt,
                                                    void* output, void* workspace, size_t workspace_size,
                                                    hipStream_t stream) {
-    return forward_common(ex, input, logits, ldt, T, opt.top_k, opt.renormalize, &opt, bias, output, workspace,
-                          workspace_size, stream);
+    return forward_common(ex, input, logits, ldt, T, opt.top_k, opt.renormalize, &opt, bias, nullptr, output,
+                          workspace, workspace_size, stream);
+}
+
+rudnn_moe_status rudnn_moe_forward_projected(const rudnn_moe_experts* ex, const void* input, const void* router,
+                                             int64_t T, rudnn_moe_routing_options opt, void* output, void* workspace,
+                                             size_t workspace_size, hipStream_t stream) {
+    if (!ex) return RUDNN_MOE_ERR_ARGUMENT;
+    return forward_common(ex, input, nullptr, ex->dtype, T, opt.top_k, opt.renormalize, nullptr, nullptr, router,
+                          output, workspace, workspace_size, stream);
 }
 
 }  // extern "C"

@@ -47,6 +47,16 @@ hipError_t launch_route_sigmoid_grouped(const void* logits, rudnn_moe_dtype ldt,
                                         int64_t E, int64_t k, int64_t groups, int64_t selected_groups, bool top_two,
                                         bool renorm, double scale, uint32_t* idx, void* w, hipStream_t s);
 
+// Gate projection + routing (route_projected.hip).  The K split S (1: none) and the workspace
+// it needs depend on T, H, E and the dtype only.
+constexpr int64_t MAX_PROJECTED_EXPERTS = 256;
+constexpr int64_t MAX_PROJECTED_HIDDEN = (int64_t)1 << 20;
+int64_t projection_split(int64_t T, int64_t H, int64_t E, rudnn_moe_dtype dt);
+size_t projection_workspace_bytes(int64_t T, int64_t H, int64_t E, rudnn_moe_dtype dt);
+hipError_t launch_route_projected(const void* x, rudnn_moe_dtype dt, const void* router, int64_t T, int64_t H,
+                                  int64_t E, int64_t k, bool renorm, void* logits_out, uint32_t* idx, void* w,
+                                  void* workspace, hipStream_t s);
+
 hipError_t launch_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input, size_t row_bytes,
                            void* dispatched, int32_t* offsets, int32_t* token_map, int32_t* chunk_counts,
                            hipStream_t s);

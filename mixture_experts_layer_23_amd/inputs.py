@@ -23,6 +23,11 @@ Recipe (all draws are fp32, then rounded to the storage dtype with round-to-near
   the tensor lives on, seeded per (seed, stream, expert): stream 3 is tokens, 4 gate, 5 up,
   6 down.  The same seed on another device gives other (equally distributed) values, so a
   test always hands the *same bytes* to both sides.
+* The gate (router) weights of the fused projection are N(0, 1) / sqrt(H) [E, H] (stream 7),
+  so the logits of N(0, 1) tokens are about N(0, 1).  Its special inputs (numpy stream 8 picks
+  the rows): token rows holding a NaN or a +inf, all-zero token rows (every logit 0, a full
+  tie), and "twin" experts whose router row is a copy of a lower expert's (equal logits for
+  every token).
 """
 from __future__ import annotations
 
@@ -35,7 +40,8 @@ import torch
 
 __all__ = [
     "DTYPES", "DTYPE_CODE", "SPECIAL_KINDS", "SIGMOID_SPECIAL_KINDS", "SigmoidRouting", "Workload", "WORKLOADS",
-    "make_logits", "make_sigmoid_logits", "make_tokens", "make_experts",
+    "make_logits", "make_sigmoid_logits", "make_tokens", "make_experts", "make_router", "make_projection_inputs",
+    "PROJECTION_SPECIAL_KINDS",
 ]
 
 DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -49,6 +55,9 @@ SPECIAL_KINDS = ("uniform", "boundary_tie", "top_tie", "partial_neginf", "nan", 
 # Special rows of the group-limited sigmoid workloads: two experts with equal logit and equal
 # bias, two groups with equal logits and equal biases, and rows with a NaN / +inf / -inf logit.
 SIGMOID_SPECIAL_KINDS = ("expert_tie", "group_tie", "nan", "posinf", "neginf")
+
+# Special token rows of the fused gate projection: one element NaN, one element +inf, all zero.
+PROJECTION_SPECIAL_KINDS = ("nan", "posinf", "zero")
 
 _SEP = 1e-3  # minimum gap between distinct logits of one row (after rounding to the dtype)
 
@@ -301,3 +310,47 @@ def make_experts(w: Workload, device="cpu"):
             v = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
             dst[e].copy_((v * (1.0 / math.sqrt(fan_in))).to(dt))
     return gate, up, down
+
+
+def make_router(w: Workload, device="cpu") -> torch.Tensor:
+    """Gate (router) weights [E, H] ~ N(0, 1) / sqrt(H) in the token dtype, on ``device``."""
+    g = _torch_gen(device, w.seed, 7)
+    v = torch.randn(w.E, w.H, generator=g, device=device, dtype=torch.float32)
+    return (v * (1.0 / math.sqrt(w.H))).to(DTYPES[w.dtype])
+
+
+def make_projection_inputs(w: Workload, device="cpu", special=(0, 0, 0), twins: int = 0):
+    """Tokens [T, H] and router [E, H] for the fused projection, with ``special`` = counts of
+    token rows per PROJECTION_SPECIAL_KINDS and ``twins`` router rows overwritten by a copy of
+    a lower expert's row.  Returns ``(x, router, info)``: info maps each special kind to its
+    sorted token rows and ``"twins"`` to a list of (lower expert, copy) pairs."""
+    x = make_tokens(w, device)
+    router = make_router(w, device)
+    rng = _np_rng(w.seed, 8)
+    n = sum(special)
+    if n > w.T:
+        raise ValueError("more special rows than tokens")
+    rows = rng.permutation(w.T)[:n]
+    info = {}
+    at = 0
+    for kind, cnt in zip(PROJECTION_SPECIAL_KINDS, special):
+        r = np.sort(rows[at:at + cnt])
+        at += cnt
+        info[kind] = r
+        for t in r:
+            t = int(t)
+            if kind == "zero":
+                x[t].zero_()
+            else:
+                x[t, int(rng.integers(w.H))] = float("nan") if kind == "nan" else float("inf")
+    pairs = []
+    if twins:
+        if 2 * twins > w.E:
+            raise ValueError("more twins than expert pairs")
+        perm = rng.permutation(w.E)[:2 * twins].reshape(twins, 2)
+        for a, b in perm:
+            lo, hi = int(min(a, b)), int(max(a, b))
+            router[hi].copy_(router[lo])
+            pairs.append((lo, hi))
+    info["twins"] = pairs
+    return x, router, info

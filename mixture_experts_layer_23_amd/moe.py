@@ -7,7 +7,9 @@ the library is missing, or a call returns an error status, this module raises.
 
 The functions follow the ruDNN user guide's MoE API (sections 3-6): ``route``,
 ``dispatch``, ``experts_forward`` (``SwiGluExperts.forward_dispatched``), ``combine`` and
-``forward`` (``SwiGluExperts.forward``).
+``forward`` (``SwiGluExperts.forward``); group-limited sigmoid routing of section 10
+(``route_sigmoid_grouped``, ``forward_sigmoid_grouped``); and the gate projection that the
+guide leaves to the caller, fused with the routing (``route_projected``, ``forward_projected``).
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ STATUS = {0: "ok", 1: "shape", 2: "dtype", 3: "argument", 4: "device", 5: "unsup
 
 KERNELS = ("route", "dispatch_count", "dispatch_scan", "dispatch_rank", "dispatch_copy", "experts_plan",
            "experts_gate_up", "experts_down", "combine", "experts_gate_up_reduce", "experts_down_reduce",
-           "route_sigmoid_grouped")
+           "route_sigmoid_grouped", "route_projected", "route_projected_reduce")
 
 
 class MoeError(RuntimeError):
@@ -82,12 +84,18 @@ def lib() -> ctypes.CDLL:
         L.rudnn_moe_forward.argtypes = [EXP, P, P, I32, I64, RoutingOptions, P, P, SZ, P]
         L.rudnn_moe_route_sigmoid_grouped.argtypes = [P, I32, I64, I64, P, GroupRoutingOptions, P, P, P]
         L.rudnn_moe_forward_sigmoid_grouped.argtypes = [EXP, P, P, I32, I64, P, GroupRoutingOptions, P, P, SZ, P]
+        L.rudnn_moe_route_projected_workspace_size.argtypes = [I64, I64, I64, I32]
+        L.rudnn_moe_route_projected_workspace_size.restype = SZ
+        L.rudnn_moe_route_projected.argtypes = [P, I32, P, I64, I64, I64, RoutingOptions, P, P, P, P, SZ, P]
+        L.rudnn_moe_forward_projected_workspace_size.argtypes = [EXP, I64, I64]
+        L.rudnn_moe_forward_projected_workspace_size.restype = SZ
+        L.rudnn_moe_forward_projected.argtypes = [EXP, P, P, I64, RoutingOptions, P, P, SZ, P]
         L.rudnn_moe_status_string.argtypes = [I32]
         L.rudnn_moe_status_string.restype = ctypes.c_char_p
         L.rudnn_moe_time_next_launch.argtypes = [I32, P, P]
         for f in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
                   "rudnn_moe_forward", "rudnn_moe_time_next_launch", "rudnn_moe_route_sigmoid_grouped",
-                  "rudnn_moe_forward_sigmoid_grouped"):
+                  "rudnn_moe_forward_sigmoid_grouped", "rudnn_moe_route_projected", "rudnn_moe_forward_projected"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -167,6 +175,10 @@ class SwiGluExperts:
                                 out=None, workspace=None) -> torch.Tensor:
         return forward_sigmoid_grouped(self, input, logits, bias, options, out=out, workspace=workspace)
 
+    def forward_projected(self, input: torch.Tensor, router: torch.Tensor, top_k: int, renormalize: bool, out=None,
+                          workspace=None) -> torch.Tensor:
+        return forward_projected(self, input, router, top_k, renormalize, out=out, workspace=workspace)
+
     def forward_dispatched(self, d: "Dispatched", out=None, workspace=None) -> torch.Tensor:
         return experts_forward(self, d.dispatched, d.expert_offsets, out=out, workspace=workspace)
 
@@ -203,6 +215,34 @@ def route_sigmoid_grouped(logits: torch.Tensor, bias, options: GroupRoutingOptio
     _check("rudnn_moe_route_sigmoid_grouped", lib().rudnn_moe_route_sigmoid_grouped(
         _ptr(logits), _dt(logits), T, E, _ptr(bias), options, _ptr(idx), _ptr(w), _stream(logits)))
     return idx, w
+
+
+def route_projected_workspace_size(T: int, H: int, E: int, dtype: torch.dtype) -> int:
+    return lib().rudnn_moe_route_projected_workspace_size(T, H, E, _DT[dtype])
+
+
+def route_projected(input: torch.Tensor, router: torch.Tensor, top_k: int, renormalize: bool,
+                    logits_out: bool = False, workspace=None):
+    """Gate projection ``input [T, H] x router [E, H]^T`` fused with softmax routing.  Returns
+    ``(expert_indices [T, k] int32 holding the uint32 ids, weights [T, k], logits [T, E] or None)``,
+    all in the input dtype; the logits are the rounded values that were routed."""
+    input = _contig(input, "input")
+    router = _contig(router, "router")
+    T, H = input.shape
+    if router.dim() != 2 or router.shape[1] != H or router.dtype != input.dtype or router.device != input.device:
+        raise ValueError("router must be [E, H] in the input's dtype, on its device")
+    E = router.shape[0]
+    dev = input.device
+    idx = torch.empty(T, top_k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, top_k, dtype=input.dtype, device=dev)
+    lo = torch.empty(T, E, dtype=input.dtype, device=dev) if logits_out else None
+    need = route_projected_workspace_size(T, H, E, input.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check("rudnn_moe_route_projected", lib().rudnn_moe_route_projected(
+        _ptr(input), _dt(input), _ptr(router), T, H, E, RoutingOptions(top_k, int(renormalize)), _ptr(lo), _ptr(idx),
+        _ptr(w), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(input)))
+    return idx, w, lo
 
 
 @dataclass
@@ -298,5 +338,27 @@ def forward_sigmoid_grouped(experts: SwiGluExperts, input: torch.Tensor, logits:
                                 dtype=torch.uint8, device=input.device)
     _check("rudnn_moe_forward_sigmoid_grouped", lib().rudnn_moe_forward_sigmoid_grouped(
         ctypes.byref(experts.view), _ptr(input), _ptr(logits), _dt(logits), T, _ptr(bias), options,
+        _ptr(out), _ptr(workspace), workspace.numel(), _stream(input)))
+    return out
+
+
+def forward_projected_workspace_size(experts: SwiGluExperts, T: int, top_k: int) -> int:
+    return lib().rudnn_moe_forward_projected_workspace_size(ctypes.byref(experts.view), T, top_k)
+
+
+def forward_projected(experts: SwiGluExperts, input: torch.Tensor, router: torch.Tensor, top_k: int,
+                      renormalize: bool, out=None, workspace=None) -> torch.Tensor:
+    """The local forward from the hidden states: fused gate projection + routing -> dispatch ->
+    experts -> combine; ``router`` [E, H] in the experts' dtype."""
+    input = _contig(input, "input")
+    router = _contig(router, "router")
+    T = input.shape[0]
+    if out is None:
+        out = torch.empty_like(input)
+    if workspace is None:
+        workspace = torch.empty(max(forward_projected_workspace_size(experts, T, top_k), 1), dtype=torch.uint8,
+                                device=input.device)
+    _check("rudnn_moe_forward_projected", lib().rudnn_moe_forward_projected(
+        ctypes.byref(experts.view), _ptr(input), _ptr(router), T, RoutingOptions(top_k, int(renormalize)),
         _ptr(out), _ptr(workspace), workspace.numel(), _stream(input)))
     return out

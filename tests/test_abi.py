@@ -28,11 +28,12 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     for required in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
-                     "rudnn_moe_forward", "rudnn_moe_route_sigmoid_grouped", "rudnn_moe_forward_sigmoid_grouped"):
+                     "rudnn_moe_forward", "rudnn_moe_route_sigmoid_grouped", "rudnn_moe_forward_sigmoid_grouped",
+                     "rudnn_moe_route_projected", "rudnn_moe_forward_projected"):
         assert required in names
 
 
@@ -153,7 +154,8 @@ def test_forward_validation(L):
 
 
 def test_timing_hook_validation(L):
-    assert L.rudnn_moe_time_next_launch(12, None, None) == ARGUMENT
+    assert L.rudnn_moe_time_next_launch(14, None, None) == ARGUMENT
+    assert L.rudnn_moe_time_next_launch(13, None, None) == OK
     assert L.rudnn_moe_time_next_launch(-1, None, None) == ARGUMENT
     assert L.rudnn_moe_time_next_launch(0, None, None) == OK
 
@@ -208,3 +210,79 @@ def test_forward_sigmoid_grouped_validation(L):
     assert call(gopts(k=2, groups=4, sel=2), wsz=ws - 1) == WORKSPACE
     assert call(gopts(k=2, groups=4, sel=2), bias=FAKE + 2**35 + 64) == ARGUMENT   # bias overlaps the output
     assert call(gopts(k=2, groups=4, sel=2), T=0) == OK
+
+
+def test_route_projected_workspace_size(L):
+    ws = L.rudnn_moe_route_projected_workspace_size
+    # many token tiles: no split, no workspace
+    assert ws(65536, 7168, 256, 2) == 0
+    assert ws(4096, 4096, 8, 2) > 0            # 128 token tiles of 32: H split over two blocks
+    # decode: 16 tokens, H split 56 ways (two 64-element steps each), FP32 partials [S, T, 256]
+    assert ws(16, 7168, 256, 2) == 56 * 16 * 256 * 4
+    assert ws(16, 7168, 256, 2) % 256 == 0
+    assert ws(16, 64, 8, 2) == 0               # one K step: nothing to split
+    assert ws(0, 64, 8, 2) == 0
+    assert ws(16, 64, 257, 2) == 0             # unsupported shapes report 0
+    assert ws(-1, 64, 8, 2) == 0
+
+
+def test_route_projected_validation(L):
+    r = L.rudnn_moe_route_projected
+    idx, w = FAKE + 2**30, FAKE + 2**31
+    x, router = FAKE, FAKE + 2**29
+
+    def call(T=64, H=128, E=8, k=2, dt=2, xp=x, rp=router, lo=None, i=idx, ww=w, ws=None, wsz=0):
+        return r(xp, dt, rp, T, H, E, opts(k), lo, i, ww, ws, wsz, None)
+
+    assert call(T=-1) == SHAPE
+    assert call(H=0) == SHAPE
+    assert call(E=0) == SHAPE
+    assert call(k=0) == ARGUMENT
+    assert call(k=9) == ARGUMENT
+    assert call(dt=4) == DTYPE
+    assert call(E=257, k=2) == UNSUPPORTED                  # E > 256
+    assert call(E=128, k=65) == UNSUPPORTED
+    assert call(H=100) == UNSUPPORTED                      # 16-bit: H % 8
+    assert call(H=98, dt=0) == UNSUPPORTED                 # FP32: H % 4
+    assert call(H=2**20) == UNSUPPORTED
+    assert call(T=2**28, k=8, E=16) == UNSUPPORTED          # T*k >= 2^31
+    assert call(xp=None) == ARGUMENT
+    assert call(rp=None) == ARGUMENT
+    assert call(i=None) == ARGUMENT
+    assert call(xp=x + 2) == UNSUPPORTED                   # misaligned tokens
+    assert call(rp=router + 8) == UNSUPPORTED              # misaligned router
+    assert call(i=x + 64) == ARGUMENT                      # indices overlap the tokens
+    assert call(lo=router + 16) == ARGUMENT                # logits copy overlaps the router
+    assert call(lo=w + 64) == ARGUMENT                     # logits copy overlaps the weights
+    need = L.rudnn_moe_route_projected_workspace_size(16, 7168, 256, 2)
+    assert call(T=16, H=7168, E=256, ws=None, wsz=need) == WORKSPACE
+    assert call(T=16, H=7168, E=256, ws=FAKE + 2**32, wsz=need - 1) == WORKSPACE
+    assert call(T=16, H=7168, E=256, ws=x + 256, wsz=need) == ARGUMENT   # workspace overlaps the tokens
+    assert call(T=0, xp=None, rp=None, i=None, ww=None) == OK
+
+
+def test_forward_projected_validation(L):
+    f = L.rudnn_moe_forward_projected
+    E, H, I, T = 16, 64, 128, 4
+    exv = moe.ExpertsView(FAKE, FAKE + 2**30, FAKE + 2**31, E, H, I, 2)
+    ws = L.rudnn_moe_forward_projected_workspace_size(ctypes.byref(exv), T, 2)
+    assert ws >= L.rudnn_moe_forward_workspace_size(ctypes.byref(exv), T, 2, 2)
+    big = moe.ExpertsView(FAKE, FAKE + 2**30, FAKE + 2**31, 256, 7168, 2048, 2)
+    assert (L.rudnn_moe_forward_projected_workspace_size(ctypes.byref(big), 16, 8)
+            >= L.rudnn_moe_forward_workspace_size(ctypes.byref(big), 16, 8, 2)
+            + L.rudnn_moe_route_projected_workspace_size(16, 7168, 256, 2))
+    wide = moe.ExpertsView(FAKE, FAKE + 2**30, FAKE + 2**31, 512, H, I, 2)
+    assert L.rudnn_moe_forward_projected_workspace_size(ctypes.byref(wide), T, 2) == 0
+
+    def call(exv=exv, T=T, k=2, x=FAKE + 2**33, router=FAKE + 2**34, out=FAKE + 2**35, wsp=FAKE + 2**36, wsz=ws):
+        return f(ctypes.byref(exv), x, router, T, opts(k), out, wsp, wsz, None)
+
+    assert f(None, FAKE, FAKE, T, opts(2), FAKE, FAKE, ws, None) == ARGUMENT
+    assert call(T=-1) == SHAPE
+    assert call(k=17) == ARGUMENT
+    assert call(exv=wide) == UNSUPPORTED                 # E > 256
+    assert call(router=None) == ARGUMENT
+    assert call(router=FAKE + 2**34 + 4) == UNSUPPORTED  # misaligned router
+    assert call(wsz=ws - 1) == WORKSPACE
+    assert call(out=FAKE + 2**34 + 32) == ARGUMENT       # output overlaps the router
+    assert call(T=0) == OK

@@ -16,7 +16,7 @@ from mixture_experts_layer_23_amd import moe
 from mixture_experts_layer_23_amd.inputs import DTYPES, WORKLOADS, Workload, make_experts, make_tokens
 from mixture_experts_layer_23_amd.inputs import make_logits as _make_logits
 from oracle import oracle
-from parity_util import assert_close, say
+from parity_util import assert_close, sampled_oracle_forward, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -259,26 +259,6 @@ def test_forward_parity_small(name):
     assert torch.equal(again.view(ib), out.view(ib))
     for t in nan_rows_of(special):
         assert torch.isnan(out[int(t)]).all()
-
-
-def sampled_oracle_forward(x, logits, rows, k, renorm, gate, up, down):
-    """The oracle's forward on the given tokens only: route, each selected expert on the
-    token's row (only the experts used are copied to the host), combine."""
-    xs, ls = x[rows].cpu(), logits[rows].cpu()
-    ridx, rw, _ = oracle.route(ls, k, renorm)
-    used = np.unique(ridx)
-    remap = {int(e): i for i, e in enumerate(used)}
-    sel = torch.from_numpy(used.astype(np.int64)).to(gate.device)
-    g, u, dn = gate[sel].cpu(), up[sel].cpu(), down[sel].cpu()
-    n = len(rows)
-    order = np.argsort(ridx.ravel(), kind="stable")  # group rows by expert
-    xr = xs.repeat_interleave(k, 0)[torch.from_numpy(order)]
-    eor = np.array([remap[int(e)] for e in ridx.ravel()[order]], np.int32)
-    yr = oracle.expert_rows(xr, eor, g, u, dn)
-    y = torch.empty_like(yr)
-    y[torch.from_numpy(order)] = yr
-    tmap = np.arange(n * k, dtype=np.int32).reshape(n, k)
-    return oracle.combine(y, tmap, rw)
 
 
 @pytest.mark.parametrize("name,nsample", [("decode", 16), ("skewed", 64), ("mixtral", 24)])

@@ -1,9 +1,11 @@
 """The seeded input generator: determinism, separation of distinct logits, special rows, skew."""
+import math
+
 import numpy as np
 import pytest
 import torch
 
-from mixture_experts_layer_23_amd.inputs import WORKLOADS, make_experts, make_logits, make_tokens
+from mixture_experts_layer_23_amd.inputs import WORKLOADS, Workload, make_experts, make_logits, make_tokens
 
 
 def _nan_like(special):
@@ -109,3 +111,30 @@ def test_sigmoid_inputs_deterministic_and_structured():
     ordinary = np.setdiff1d(np.arange(w.T), np.concatenate(list(sa.values())))
     d = np.diff(np.sort(x[ordinary], axis=1), axis=1)
     assert d.min() >= 1e-3                               # separated logits elsewhere
+
+
+def test_projection_inputs_deterministic_and_structured():
+    from mixture_experts_layer_23_amd.inputs import PROJECTION_SPECIAL_KINDS, make_projection_inputs, make_router
+    w = Workload("proj", 200, 64, None, 16, 2, "bf16", "bf16", (True,), None, 77)
+    r = make_router(w)
+    assert r.shape == (16, 64) and r.dtype == torch.bfloat16
+    assert abs(float(r.float().std()) * math.sqrt(64) - 1.0) < 0.1      # N(0, 1) / sqrt(H)
+    x1, r1, i1 = make_projection_inputs(w, special=(2, 3, 4), twins=3)
+    x2, r2, i2 = make_projection_inputs(w, special=(2, 3, 4), twins=3)
+    assert torch.equal(x1.view(torch.int16), x2.view(torch.int16)) and torch.equal(r1.view(torch.int16),
+                                                                                 r2.view(torch.int16))
+    assert [len(i1[k]) for k in PROJECTION_SPECIAL_KINDS] == [2, 3, 4]
+    rows = np.concatenate([i1[k] for k in PROJECTION_SPECIAL_KINDS])
+    assert len(set(rows.tolist())) == 9                                  # distinct rows
+    xf = x1.float()
+    for t in i1["nan"]:
+        assert int(torch.isnan(xf[t]).sum()) == 1
+    for t in i1["posinf"]:
+        assert int((xf[t] == float("inf")).sum()) == 1
+    for t in i1["zero"]:
+        assert (xf[t] == 0).all()
+    assert len(i1["twins"]) == 3
+    for a, b in i1["twins"]:
+        assert a < b and torch.equal(r1[a].view(torch.int16), r1[b].view(torch.int16))
+    ordinary = np.setdiff1d(np.arange(w.T), rows)
+    assert torch.isfinite(xf[torch.from_numpy(ordinary)]).all()

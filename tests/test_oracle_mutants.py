@@ -21,7 +21,10 @@ MUTANTS = {
     "renorm_wrong_terms": ("for (int64_t j = 0; j < k; ++j) den += p[idx[j]];", "for (int64_t j = 0; j < k; ++j) den += p[j];"),
     # (dropping the explicit +inf / all -inf test is not a mistake: the max-subtracted
     # softmax of such rows is NaN everywhere anyway, so that copy is equivalent)
-    "nan_row_uniform": ("store_val(weights, ldt, t * k + j, NAN);", "store_val(weights, ldt, t * k + j, 1.0 / (double)E);"),
+    "nan_row_uniform": ("if (row_softmax(x, E, p)) {\n                for (int64_t j = 0; j < k; ++j) {\n"
+                        "                    idx[j] = (uint32_t)j;\n                    store_val(weights, ldt, t * k + j, NAN);",
+                        "if (row_softmax(x, E, p)) {\n                for (int64_t j = 0; j < k; ++j) {\n"
+                        "                    idx[j] = (uint32_t)j;\n                    store_val(weights, ldt, t * k + j, 1.0 / (double)E);"),
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "gate_up_swapped": ("hb[r * I + i] = round_to(silu(g) * u, dt);", "hb[r * I + i] = round_to(silu(u) * g, dt);"),
     "down_transposed": ("wd[i] = load_val(down, dt, (e * H + c) * I + i);", "wd[i] = load_val(down, dt, (e * I + i) * H + c);"),
@@ -39,6 +42,10 @@ MUTANTS = {
     "sig_top_two_counts_max_twice": ("if (i != b1 && (b2 < 0 || cg[i] > cg[b2])) b2 = i;", "if (b2 < 0 || cg[i] > cg[b2]) b2 = i;", SIG),
     "sig_groups_not_enforced": ("if (taken[e] || !gsel[e / per]) continue;", "if (taken[e]) continue;", SIG),
     "sig_scale_dropped_with_renorm": ("v *= scale;", "if (!renormalize) v *= scale;", SIG),
+    "sig_nan_row_weights_finite": ("if (nan_row) {\n                for (int64_t j = 0; j < k; ++j) {\n"
+                                   "                    idx[j] = (uint32_t)j;\n                    store_val(weights, ldt, t * k + j, NAN);",
+                                   "if (nan_row) {\n                for (int64_t j = 0; j < k; ++j) {\n"
+                                   "                    idx[j] = (uint32_t)j;\n                    store_val(weights, ldt, t * k + j, 0.0);", SIG),
     # router projection, checked against its own pins
     "proj_router_transposed": ("load_val(router, dt, e * H + h)", "load_val(router, dt, h * E + e)", PROJ),
     "proj_half_the_sum": ("for (int64_t h = 0; h < H; ++h) acc +=", "for (int64_t h = 0; h < H / 2; ++h) acc +=", PROJ),
