@@ -7,7 +7,10 @@ H=4096, I=14336, E=8, top_k=2, renormalised, bf16), all inputs resident in HBM. 
 JSON line with tokens/s, the roofline of the dominant kernel (the gate/up expert GEMM, timed
 with HIP events on its launch stream during the timed steps), a per-kernel breakdown, the HBM
 rates of route / dispatch / combine on the routing+dispatch workload (T=65536, E=128, k=8,
-H=2048, bf16, identity experts), and the CPU oracle timed on a bounded sample of the same layer.
+H=2048, bf16, identity experts), the fused gate projection + routing on the same token shapes,
+and the CPU oracle timed on a bounded sample of the same layer.  HBM-bound stages start from a
+cold cache: 512 MiB are read (not written) before each timed launch, so that the caches hold
+neither the inputs nor dirty lines whose write-back would land in the timed kernel.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -92,6 +95,8 @@ def main():
     ap.add_argument("--no-hbm-stages", action="store_true")
     ap.add_argument("--no-sigmoid", action="store_true",
                     help="skip the group-limited sigmoid routing measurements")
+    ap.add_argument("--no-projection", action="store_true",
+                    help="skip the fused gate projection + routing measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -112,6 +117,15 @@ def main():
     torch.cuda.set_device(dev)
     hip = Hip()
     stream = torch.cuda.current_stream(dev).cuda_stream
+    flush_buf, flush_sink = None, None
+
+    def flush():
+        """Evict the caches by reading 512 MiB (2x the 256 MB Infinity Cache); no dirty lines."""
+        nonlocal flush_buf, flush_sink
+        if flush_buf is None:
+            flush_buf = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+            flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
+        torch.sum(flush_buf, dim=0, out=flush_sink)
 
     if args.copy_calibration:
         n = 1 << 30
@@ -172,7 +186,9 @@ def main():
     gu_tflops = gu_flops / (gu_ms / 1e3) / 1e12
 
     # per-kernel breakdown (separate pass, every kernel timed)
-    fwd_kernels = [kn for kn in moe.KERNELS if kn != "route_sigmoid_grouped"]  # what the softmax forward launches
+    # what the softmax forward with ready logits launches
+    fwd_kernels = [kn for kn in moe.KERNELS if kn not in ("route_sigmoid_grouped", "route_projected",
+                                                          "route_projected_reduce")]
     stage_ev = {kn: [(hip.event(), hip.event()) for _ in range(max(3, K // 4))] for kn in fwd_kernels}
     for i in range(max(3, K // 4)):
         for kn in fwd_kernels:
@@ -241,7 +257,6 @@ def main():
         dws = torch.empty(max(moe.lib().rudnn_moe_dispatch_workspace_size(T2, k2, E2), 1), dtype=torch.uint8,
                           device=dev)
         o2 = torch.empty_like(x2)
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # 2x the 256 MB Infinity Cache
         reps = 5
         ev = {n_: [(hip.event(), hip.event()) for _ in range(reps)] for n_ in ("route", "dispatch", "combine")}
         for i in range(reps + 1):
@@ -251,7 +266,7 @@ def main():
                                  stream)),
                              ("dispatch", lambda: moe.dispatch(idx2, x2, E2, out=d2, workspace=dws)),
                              ("combine", lambda: moe.combine(d2.dispatched, d2.token_map, wt2, out=o2))):
-                flush.fill_(i & 0xff)
+                flush()
                 if rec:
                     hip.record(ev[name][i - 1][0], stream)
                 rc = fn()
@@ -264,7 +279,8 @@ def main():
         hbm_bytes = {"route": T2 * E2 * s + pk * (4 + s),
                      "dispatch": pk * 4 * 2 + T2 * H2 * s + pk * H2 * s + pk * 4 + 4 * (E2 + 1),
                      "combine": pk * H2 * s + pk * (s + 4) + T2 * H2 * s}
-        hbm = {"workload": "routing+dispatch T=65536 E=128 k=8 H=2048 bf16, identity experts, cache flushed"}
+        hbm = {"workload": "routing+dispatch T=65536 E=128 k=8 H=2048 bf16, identity experts, caches evicted by a "
+                           "512 MiB read before each launch"}
         for name in ("route", "dispatch", "combine"):
             us = float(np.median([hip.ms(a, b) for a, b in ev[name]])) * 1e3
             gbs = hbm_bytes[name] / (us / 1e6) / 1e9
@@ -287,11 +303,10 @@ def main():
         T3, E3, k3 = ws_.T, ws_.E, ws_.top_k
         idx3 = torch.empty(T3, k3, dtype=torch.int32, device=dev)
         wt3 = torch.empty(T3, k3, dtype=lg3.dtype, device=dev)
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         reps = 5
         ev3 = [(hip.event(), hip.event()) for _ in range(reps)]
         for i in range(reps + 1):
-            flush.fill_(i & 0xff)
+            flush()
             if i:
                 hip.record(ev3[i - 1][0], stream)
             rc = moe.lib().rudnn_moe_route_sigmoid_grouped(lg3.data_ptr(), 2, T3, E3, b3.data_ptr(), o3,
@@ -303,10 +318,10 @@ def main():
         us3 = float(np.median([hip.ms(a, b) for a, b in ev3])) * 1e3
         b3_bytes = T3 * E3 * 2 + E3 * 4 + T3 * k3 * (4 + 2)
         sig = {"route": {"workload": f"T={T3} E={E3} groups={sg.groups} selected={sg.selected_groups} top-two "
-                                     f"k={k3} bf16 logits + FP32 bias, cache flushed",
+                                     f"k={k3} bf16 logits + FP32 bias, caches evicted",
                          "us": us3, "bytes": b3_bytes, "GBps": b3_bytes / (us3 / 1e6) / 1e9,
                          "hbm_frac": b3_bytes / (us3 / 1e6) / 1e9 / HBM_PEAK_GBS}}
-        del lg3, b3, idx3, wt3, flush
+        del lg3, b3, idx3, wt3
         # the decode-shaped layer routed this way (256 experts, weights streamed from HBM)
         wd = WORKLOADS["sigmoid_decode"]
         log("generating", wd.name)
@@ -339,6 +354,12 @@ def main():
                                  "hbm_frac": wbytes / (msd / 1e3) / 1e9 / HBM_PEAK_GBS}
         del gd, ud, dd, exd, wsd
 
+    # ---------------- gate projection fused with routing ----------------
+    proj = None
+    if not args.no_projection:
+        torch.cuda.empty_cache()
+        proj = measure_projection(args, moe, hip, stream, flush, dev, ex, w, out_shape=(w.T, w.H))
+
     traffic = traffic_for("experts_gate_up", "mixtral")
     result = {
         "metric": METRIC,
@@ -363,8 +384,104 @@ def main():
         "stages": stages,
         "hbm_stages": hbm,
         "sigmoid_routing": sig,
+        "projection": proj,
     }
     print(json.dumps(result), flush=True)
+
+
+def measure_projection(args, moe, hip, stream, flush, dev, ex, wmix, out_shape):
+    """The fused gate projection + routing (rudnn_moe_route_projected): kernel time on the
+    routing+dispatch token shape (T=65536, H=2048, E=128, k=8) and on 65536 tokens of the 256-expert
+    shape (H=7168), caches evicted before each launch; and, on the Mixtral-shaped layer and the
+    decode shape, the whole call back to back next to the forward that takes ready logits."""
+    import numpy as np
+    import torch
+    from mixture_experts_layer_23_amd.inputs import WORKLOADS, make_logits, make_projection_inputs
+
+    def cold_kernel(x, router, T, H, E, k, reps=5):
+        idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+        wt = torch.empty(T, k, dtype=x.dtype, device=dev)
+        need = moe.route_projected_workspace_size(T, H, E, x.dtype)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        ev = [(hip.event(), hip.event()) for _ in range(reps)]
+        for i in range(reps + 1):
+            flush()
+            if i:
+                moe.time_next_launch("route_projected", *ev[i - 1])
+            rc = moe.lib().rudnn_moe_route_projected(x.data_ptr(), 2, router.data_ptr(), T, H, E,
+                                                     moe.RoutingOptions(k, 1), None, idx.data_ptr(), wt.data_ptr(),
+                                                     ws.data_ptr(), ws.numel(), stream)
+            assert rc == 0, rc
+        torch.cuda.synchronize()
+        us = float(np.median([hip.ms(a, b) for a, b in ev])) * 1e3
+        byts = T * H * 2 + E * H * 2 + T * k * (4 + 2)
+        flops = 2.0 * T * H * E
+        return {"workload": f"T={T} H={H} E={E} k={k} bf16, caches evicted", "kernel_us": us, "bytes": byts,
+                "GBps": byts / (us / 1e6) / 1e9, "hbm_frac": byts / (us / 1e6) / 1e9 / HBM_PEAK_GBS,
+                "TFLOPps": flops / (us / 1e6) / 1e12, "mfma_frac": flops / (us / 1e6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"]}
+
+    res = {}
+    for name, E, k in (("route_dispatch", None, None), ("sigmoid_route", None, None)):
+        wl = WORKLOADS[name]
+        log("generating projection inputs", name)
+        x, router, _ = make_projection_inputs(wl, dev)
+        res[name] = cold_kernel(x, router, wl.T, wl.H, wl.E, wl.top_k)
+        del x, router
+        torch.cuda.empty_cache()
+
+    def back_to_back(fn, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = hip.event(), hip.event()
+        hip.record(a, stream)
+        for _ in range(n):
+            fn()
+        hip.record(b, stream)
+        return hip.ms(a, b) / n
+
+    # Mixtral-shaped layer: forward from hidden states vs forward with ready logits
+    log("projection: Mixtral-shaped layer")
+    x, router, _ = make_projection_inputs(wmix, dev)
+    lg = make_logits(wmix)[0].to(dev)
+    out = torch.empty_like(x)
+    wsf = torch.empty(moe.forward_workspace_size(ex, wmix.T, wmix.top_k, lg.dtype), dtype=torch.uint8, device=dev)
+    wsp = torch.empty(moe.forward_projected_workspace_size(ex, wmix.T, wmix.top_k), dtype=torch.uint8, device=dev)
+    ms_fwd = back_to_back(lambda: ex.forward(x, lg, wmix.top_k, True, out=out, workspace=wsf))
+    ms_proj = back_to_back(lambda: ex.forward_projected(x, router, wmix.top_k, True, out=out, workspace=wsp))
+    kev = [(hip.event(), hip.event()) for _ in range(5)]
+    rev = [(hip.event(), hip.event()) for _ in range(5)]
+    for i in range(5):
+        moe.time_next_launch("route_projected", *kev[i])
+        moe.time_next_launch("route_projected_reduce", *rev[i])
+        ex.forward_projected(x, router, wmix.top_k, True, out=out, workspace=wsp)
+    torch.cuda.synchronize()
+    res["mixtral_layer"] = {
+        "workload": f"T={wmix.T} H={wmix.H} I={wmix.I} E={wmix.E} k={wmix.top_k} bf16, router [E, H]",
+        "forward_ms": ms_fwd, "forward_projected_ms": ms_proj,
+        "forward_projected_tokens_per_s": wmix.T / (ms_proj / 1e3),
+        "route_projected_kernel_us": float(np.median([hip.ms(a, b) for a, b in kev])) * 1e3,
+        "route_projected_reduce_us": float(np.median([hip.ms(a, b) for a, b in rev])) * 1e3}
+    del x, router, lg, out, wsf, wsp
+    torch.cuda.empty_cache()
+
+    # decode shape: the H split over blocks + the reduce kernel, whole call back to back
+    wd = WORKLOADS["decode"]
+    x, router, _ = make_projection_inputs(wd, dev)
+    idx = torch.empty(wd.T, wd.top_k, dtype=torch.int32, device=dev)
+    wt = torch.empty(wd.T, wd.top_k, dtype=x.dtype, device=dev)
+    ws = torch.empty(max(moe.route_projected_workspace_size(wd.T, wd.H, wd.E, x.dtype), 256), dtype=torch.uint8,
+                     device=dev)
+
+    def dec():
+        rc = moe.lib().rudnn_moe_route_projected(x.data_ptr(), 2, router.data_ptr(), wd.T, wd.H, wd.E,
+                                                 moe.RoutingOptions(wd.top_k, 1), None, idx.data_ptr(), wt.data_ptr(),
+                                                 ws.data_ptr(), ws.numel(), stream)
+        assert rc == 0, rc
+    ms_dec = back_to_back(dec, 50)
+    res["decode"] = {"workload": f"T={wd.T} H={wd.H} E={wd.E} k={wd.top_k} bf16 (H split over blocks)",
+                     "call_us": ms_dec * 1e3, "router_GBps": wd.E * wd.H * 2 / (ms_dec / 1e3) / 1e9}
+    return res
 
 
 if __name__ == "__main__":

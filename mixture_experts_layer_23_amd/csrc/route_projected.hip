@@ -8,22 +8,25 @@
 // unless the caller asks for a copy.
 //
 // project_route: a block owns BM = 32 WM token rows and every expert (E padded to EP, a multiple
-// of 32).  Its four wavefronts split the tile WM x WN x WK ways: WM bands of 32 tokens, WN bands
-// of EP / WN experts, WK interleaved quarters of each staged K step (WK > 1 when E is small, so
-// that all four SIMDs work on a 32-token tile).  The K axis is staged 128 bytes at a time
-// (64 16-bit or 32 FP32 elements): token rows and router rows go straight from global memory
-// into XOR-swizzled LDS (global_load_lds_dwordx4), two stages, the copies of step k+1 issued
-// right after the barrier that opens step k.  BF16/F16 run v_mfma_f32_32x32x16; FP32 runs
-// v_mfma_f32_32x32x2f32, full FP32 products.  The router fragment is the first MFMA operand, so
-// lane l of an accumulator block holds token l % 32.
+// of 32).  Its wavefronts (4 or 8) split the tile WM x WN x WK ways: WM bands of 32 tokens, WN
+// bands of EP / WN experts, WK interleaved parts of each staged K step (WK > 1 when E is small,
+// so that all SIMDs work on a small tile).  The K axis is staged 128 bytes at a time (64 16-bit
+// or 32 FP32 elements): token rows and router rows go straight from global memory into
+// XOR-swizzled LDS (global_load_lds_dwordx4) through a ring of NS stages, the copies of step
+// k + NS - 1 issued right after the barrier that opens step k.  The kernel streams the tokens
+// from HBM once, so its speed is set by the bytes in flight per CU: the ring depth and BM are
+// chosen per expert count within the LDS (see the tile table below).
+// BF16/F16 run v_mfma_f32_32x32x16; FP32 runs v_mfma_f32_32x32x2f32, full FP32 products.  The
+// router fragment is the first MFMA operand, so lane l of an accumulator block holds token
+// l % 32.
 // Epilogue: accumulators -> LDS [WK][BM][EP] FP32; the WK slices are added in order, rounded to
 // the dtype and routed, G lanes per row, in passes of 256 / G rows.
 //
 // Few token tiles (T / BM well below the CU count, e.g. decode) would leave most CUs idle while
 // one block streams all of W_r, so K is then split over S blocks per token tile
 // (projection_split): each stores FP32 partial logits [S][T][EP] in the workspace, and
-// route_partials adds the S partials of each logit in segment order (deterministic), rounds
-// and routes.
+// route_partials adds the S partials of each logit in a fixed order (deterministic), rounds and
+// routes.
 //
 // HBM traffic per token row: H * sizeof(dtype) read (W_r, E * H elements, is read once per
 // block from L2), k * (4 + sizeof(dtype)) written, plus E * sizeof(dtype) for the optional
@@ -41,14 +44,24 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int THREADS = 256, NWAVES = 4;
-constexpr int ROWB = 128;  // bytes of one staged row (K step)
+constexpr int ROWB = 128;           // bytes of one staged row (K step)
+constexpr int REDUCE_THREADS = 1024;  // route_partials
 
 // Chunk c (16 bytes) of staged row r sits at slot c ^ swz(r): the MFMA operand reads (one chunk
 // from each of 32 consecutive rows) then spread over all LDS banks.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier of the copy ring.  __syncthreads() would also wait for every outstanding
+// global->LDS copy of this wavefront (its release fence covers global memory), draining the
+// ring at each step; here the caller first waits for the copies it needs (wait_vmcnt), this
+// waits for the wavefront's own LDS accesses, and the "memory" clobber keeps the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // One 16-byte chunk of K per lane: the MFMA step(s) over it.  16-bit types: one 32x32x16 step
 // (lane half h holds K elements 8h .. 8h + 7 of the 16).  FP32: four 32x32x2 steps, step q
@@ -114,11 +127,11 @@ __device__ __forceinline__ void store_logits(T* out_row, int e0, int E, const ty
 
 // One staged K step: BM token rows then EP router rows, 128 bytes each, as 1 KiB wave copies
 // of 8 rows (lane i writes 16 bytes at the copy's LDS base + 16 i), dealt to the wavefronts
-// round-robin.  Token rows past the tile's last are not copied when the whole copy lies past
-// it (they only feed outputs that are never used) and re-read the last row otherwise; router
-// rows past E re-read row E - 1 (logits of padding experts are never used).  TAIL: chunks at
-// or past the row's end (K not a multiple of the step) are zeroed in both operands.
-template <int BM, int EP, bool TAIL>
+// round-robin, SLOTS copies per wavefront (the ring's waits count them, so every whole step
+// issues exactly that many).  Token rows past the tile's last re-read its last row and router
+// rows past E re-read row E - 1 (outputs of those rows are never used).  TAIL: chunks at or past
+// the row's end (K not a multiple of the step) are zeroed in both operands instead.
+template <int BM, int EP, int NWAVES, bool TAIL>
 __device__ __forceinline__ void stage(unsigned char* st, const unsigned char* xa, const unsigned char* wa, int nrows,
                                       int E, int kbytes, int k0, int wave, int lane) {
     constexpr int GA = BM / 8, GB = EP / 8, SLOTS = (GA + GB) / NWAVES;
@@ -129,7 +142,6 @@ __device__ __forceinline__ void stage(unsigned char* st, const unsigned char* xa
         const unsigned char* base;
         int r, last;
         if (gi < GA) {
-            if (gi * 8 > nrows - 1) continue;
             base = xa, r = gi * 8 + lane / 8, last = nrows - 1;
         } else {
             base = wa, r = (gi - GA) * 8 + lane / 8, last = E - 1;
@@ -145,24 +157,31 @@ __device__ __forceinline__ void stage(unsigned char* st, const unsigned char* xa
     }
 }
 
-template <int EP, int WM, int WN, int WK>
+template <int EP_, int WM_, int WN_, int WK_, int NS_>
 struct Cfg {
+    static constexpr int EP = EP_, WM = WM_, WN = WN_, WK = WK_, NS = NS_;
+    static constexpr int NWAVES = WM * WN * WK, THREADS = NWAVES * 64;
     static constexpr int BM = WM * 32, WTN = EP / WN, FN = WTN / 32;
     static constexpr int STAGE = (BM + EP) * ROWB;
+    static constexpr int SLOTS = (BM + EP) / 8 / NWAVES;     // copies per wavefront per step
     static constexpr int RP = EP + 4;                        // FP32 row pitch of the reduce tile
     static constexpr int RED = WK * BM * RP * 4;             // bytes of the reduce tile
-    static_assert(WM * WN * WK == NWAVES, "four wavefronts");
+    static_assert(NWAVES == 4 || NWAVES == 8, "four or eight wavefronts");
     static_assert(EP % (32 * WN) == 0 && 4 % WK == 0, "wave tiles of whole 32x32 blocks");
+    static_assert(NS >= 2 && (NS - 2) * SLOTS <= 63, "ring waits fit the vmcnt counter");
+    static_assert(NS * STAGE <= 160 * 1024, "ring fits the LDS");
 };
 
 // Projection of one token tile (or one K segment of it, S > 1) and, with S == 1, its routing.
-template <typename T, int EP, int WM, int WN, int WK, int NPER, int G>
-__global__ __launch_bounds__(THREADS) void project_route(const T* __restrict__ x, const T* __restrict__ wr,
-                                                         int64_t Tn, int H, int E, int k, int renorm, int S,
-                                                         float* __restrict__ partials, T* __restrict__ logits_out,
-                                                         uint32_t* __restrict__ idx, T* __restrict__ w) {
-    typedef Cfg<EP, WM, WN, WK> C;
-    constexpr int BM = C::BM, FN = C::FN, RP = C::RP, STAGE = C::STAGE;
+template <typename T, typename C, int NPER, int G>
+__global__ __launch_bounds__(C::THREADS) void project_route(const T* __restrict__ x, const T* __restrict__ wr,
+                                                            int64_t Tn, int H, int E, int k, int renorm, int S,
+                                                            int rpp, float* __restrict__ partials,
+                                                            T* __restrict__ logits_out, uint32_t* __restrict__ idx,
+                                                            T* __restrict__ w) {
+    constexpr int EP = C::EP, WM = C::WM, WN = C::WN, WK = C::WK, NS = C::NS, NWAVES = C::NWAVES;
+    constexpr int THREADS = C::THREADS, BM = C::BM, FN = C::FN, RP = C::RP, STAGE = C::STAGE;
+    (void)WM;
     typedef typename RouteBits<T>::raw R;
     typedef typename Mma<T>::frag frag;
     static_assert(G * NPER <= EP, "a row's lanes stay inside the padded tile");
@@ -183,11 +202,11 @@ __global__ __launch_bounds__(THREADS) void project_route(const T* __restrict__ x
     const unsigned char* wa = reinterpret_cast<const unsigned char*>(wr);
 
     auto issue = [&](int kt) __attribute__((always_inline)) {
-        unsigned char* st = smem + (kt & 1) * STAGE;
+        unsigned char* st = smem + (kt % NS) * STAGE;
         if (ragged && kt == KT - 1)
-            stage<BM, EP, true>(st, xa, wa, nrows, E, kbytes, kt * ROWB, wave, lane);
+            stage<BM, EP, NWAVES, true>(st, xa, wa, nrows, E, kbytes, kt * ROWB, wave, lane);
         else
-            stage<BM, EP, false>(st, xa, wa, nrows, E, kbytes, kt * ROWB, wave, lane);
+            stage<BM, EP, NWAVES, false>(st, xa, wa, nrows, E, kbytes, kt * ROWB, wave, lane);
     };
 
     f32x16 acc[FN];
@@ -197,12 +216,22 @@ __global__ __launch_bounds__(THREADS) void project_route(const T* __restrict__ x
         for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
 
     const int fr = lane & 31, fh = lane >> 5;
-    issue(kb);
+    // Ring: steps kt + 1 .. kt + NS - 2 are in flight while step kt computes.  The wait before
+    // step kt lets exactly the later steps' copies stay outstanding (copies complete in issue
+    // order); when one of those is missing or is the ragged last step (fewer copies), it waits
+    // for all.
+    const int whole_end = ragged ? KT - 1 : KT;  // steps before this one issue SLOTS copies each
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (kb + s < ke) issue(kb + s);
     for (int kt = kb; kt < ke; ++kt) {
-        wait_vmcnt0();    // this wavefront's copies of step kt have landed
-        __syncthreads();  // everyone's have; everyone is done with step kt - 1
-        if (kt + 1 < ke) issue(kt + 1);
-        const unsigned char* st = smem + (kt & 1) * STAGE;
+        if (NS > 2 && kt + NS - 2 < ke && kt + NS - 2 < whole_end)
+            wait_vmcnt<(NS - 2) * C::SLOTS>();  // this wavefront's copies of step kt have landed
+        else
+            wait_vmcnt<0>();
+        ring_barrier();  // everyone's have; everyone is done with step kt - 1
+        if (kt + NS - 1 < ke) issue(kt + NS - 1);
+        const unsigned char* st = smem + (kt % NS) * STAGE;
         const unsigned char* sx = st + (wm * 32 + fr) * ROWB;
         const unsigned char* sw = st + (BM + wn * C::WTN + fr) * ROWB;
 #pragma unroll
@@ -246,14 +275,15 @@ __global__ __launch_bounds__(THREADS) void project_route(const T* __restrict__ x
         return;
     }
 
-    // Routing, G lanes per row, 256 / G rows per pass.
-    constexpr int RPB = THREADS / G;
+    // Routing, G lanes per row, rpp <= THREADS / G rows per pass (the LDS after the reduce tile
+    // holds rpp rows of selection scratch).
     const int rb = tid / G, e0 = (lane % G) * NPER;
-    uint32_t* si = reinterpret_cast<uint32_t*>(smem + C::RED) + rb * k;
-    float* se = reinterpret_cast<float*>(smem + C::RED) + RPB * k + rb * k;
-    for (int p = 0; p < BM; p += RPB) {
+    const bool active = rb < rpp;
+    uint32_t* si = reinterpret_cast<uint32_t*>(smem + C::RED) + (active ? rb : 0) * k;
+    float* se = reinterpret_cast<float*>(smem + C::RED) + rpp * k + (active ? rb : 0) * k;
+    for (int p = 0; p < BM; p += rpp) {
         const int r = p + rb;
-        const bool live = r < nrows;
+        const bool live = active && r < nrows;
         const float* rr = red + (r < BM ? r : 0) * RP + e0;
         R raw[NPER];
 #pragma unroll
@@ -269,51 +299,97 @@ __global__ __launch_bounds__(THREADS) void project_route(const T* __restrict__ x
     }
 }
 
-// The S partial logits of each row added in segment order, rounded, stored (optional) and
-// routed; G lanes per row as in the softmax router.
+// The S partial logits of each row added, rounded, stored (optional) and routed.  A block of
+// 1024 threads owns RB rows: thread (part p, row r, column quad c) adds slabs
+// [p S / PP, (p + 1) S / PP) of its four logits in slab order (eight slabs loaded ahead), the
+// part-0 thread of each column quad then adds the other parts in part order through LDS -- a
+// fixed order for given T, H and E -- and G lanes per row route as in the softmax router.  C4 * RB * PP = 1024 with C4 = EP / 4.
 template <typename T, int NPER, int G>
-__global__ __launch_bounds__(THREADS) void route_partials(const float* __restrict__ P, int64_t Tn, int EP, int S,
-                                                          int E, int k, int renorm, T* __restrict__ logits_out,
-                                                          uint32_t* __restrict__ idx, T* __restrict__ w) {
+__global__ __launch_bounds__(REDUCE_THREADS) void route_partials(const float* __restrict__ P, int64_t Tn, int EP,
+                                                                 int S, int PP, int RB, int E, int k, int renorm,
+                                                                 T* __restrict__ logits_out,
+                                                                 uint32_t* __restrict__ idx, T* __restrict__ w) {
     typedef typename RouteBits<T>::raw R;
-    extern __shared__ float s_sel[];  // [rows per block][k] winner ids, then [rows per block][k] e_j
-    constexpr int RPB = THREADS / G;
-    const int rb = threadIdx.x / G, e0 = (lane_id() % G) * NPER;
-    const int64_t row = (int64_t)blockIdx.x * RPB + rb;
-    const bool live = row < Tn;
-    static_assert(NPER % 4 == 0, "whole float4 pieces per lane");
-    float v[NPER];
+    extern __shared__ __align__(16) float sm[];  // sums [PP][RB][EP], then [RB][k] winner ids, [RB][k] e_j
+    constexpr int AHEAD = 8;
+    const int tid = threadIdx.x, C4 = EP / 4;
+    const int c = tid % C4, r = (tid / C4) % RB, p = tid / (C4 * RB);
+    const int64_t row0 = (int64_t)blockIdx.x * RB;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row0 + r < Tn) {
+        const int s0 = (int)((int64_t)p * S / PP), s1 = (int)((int64_t)(p + 1) * S / PP);
+        const float* p0 = P + (row0 + r) * EP + 4 * c;
+        const int64_t slab = Tn * EP;
+        for (int sg = s0; sg < s1; sg += AHEAD) {
+            float4 q[AHEAD];
 #pragma unroll
-    for (int s = 0; s < NPER; ++s) v[s] = 0.f;
-    if (live) {
-        for (int sg = 0; sg < S; ++sg) {
-            const float* p = P + ((int64_t)sg * Tn + row) * EP + e0;
+            for (int a = 0; a < AHEAD; ++a)
+                if (sg + a < s1) q[a] = *reinterpret_cast<const float4*>(p0 + (sg + a) * slab);
 #pragma unroll
-            for (int c = 0; c < NPER / 4; ++c) {
-                const float4 q = *reinterpret_cast<const float4*>(p + 4 * c);
-                v[4 * c] += q.x, v[4 * c + 1] += q.y, v[4 * c + 2] += q.z, v[4 * c + 3] += q.w;
-            }
+            for (int a = 0; a < AHEAD; ++a)
+                if (sg + a < s1) acc.x += q[a].x, acc.y += q[a].y, acc.z += q[a].z, acc.w += q[a].w;
         }
     }
+    float4* sm4 = reinterpret_cast<float4*>(sm);
+    sm4[(p * RB + r) * (EP / 4) + c] = acc;
+    __syncthreads();
+    if (p == 0) {  // the parts, in part order, into part 0's slot
+        for (int q = 1; q < PP; ++q) {
+            const float4 u = sm4[(q * RB + r) * (EP / 4) + c];
+            acc.x += u.x, acc.y += u.y, acc.z += u.z, acc.w += u.w;
+        }
+        sm4[r * (EP / 4) + c] = acc;
+    }
+    __syncthreads();
+
+    const int rb = tid / G, e0 = (lane_id() % G) * NPER;
+    const int64_t row = row0 + rb;
+    const bool live = rb < RB && row < Tn;
     R raw[NPER];
 #pragma unroll
-    for (int s = 0; s < NPER; ++s) raw[s] = bits_of<T>(v[s]);
+    for (int s = 0; s < NPER; ++s) raw[s] = bits_of<T>(rb < RB ? sm[rb * EP + e0 + s] : 0.f);
     if (logits_out && live) store_logits<T, NPER>(logits_out + row * E, e0, E, raw);
-    route_row<T, NPER, G>(raw, E, k, renorm, live, row, reinterpret_cast<uint32_t*>(s_sel) + rb * k,
-                          s_sel + RPB * k + rb * k, idx, w);
+    float* scratch = sm + PP * RB * EP;
+    const int sr = rb < RB ? rb : 0;
+    route_row<T, NPER, G>(raw, E, k, renorm, live, row, reinterpret_cast<uint32_t*>(scratch) + sr * k,
+                          scratch + RB * k + sr * k, idx, w);
 }
 
 }  // namespace proj
 
 // ---- host side ----
 
+// Tile shape per expert count: EP, WM, WN, WK, NS (see project_route), the fastest of a sweep on
+// the Mixtral-, fine-grained- and 256-expert shapes: E <= 32: 64-token tiles, a 6-step ring, two
+// blocks per CU; E <= 64: 64-token tiles, 5 steps, two blocks; E <= 128: 256-token tiles of
+// eight wavefronts, 3 steps; E <= 256: 128-token tiles of eight wavefronts, 3 steps.
+#ifndef RUDNN_PROJ_E32
+#define RUDNN_PROJ_E32 32, 2, 1, 2, 6
+#endif
+#ifndef RUDNN_PROJ_E64
+#define RUDNN_PROJ_E64 64, 2, 1, 2, 5
+#endif
+#ifndef RUDNN_PROJ_E128
+#define RUDNN_PROJ_E128 128, 8, 1, 1, 3
+#endif
+#ifndef RUDNN_PROJ_E256
+#define RUDNN_PROJ_E256 256, 4, 2, 1, 3
+#endif
+typedef proj::Cfg<RUDNN_PROJ_E32> CfgE32;
+typedef proj::Cfg<RUDNN_PROJ_E64> CfgE64;
+typedef proj::Cfg<RUDNN_PROJ_E128> CfgE128;
+typedef proj::Cfg<RUDNN_PROJ_E256> CfgE256;
+static_assert(CfgE32::EP == 32 && CfgE64::EP == 64 && CfgE128::EP == 128 && CfgE256::EP == 256, "expert classes");
+
 namespace {
 
-// Padded experts and token rows per block of the tile shape chosen for E.
 int64_t padded_experts(int64_t E) { return E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256; }
-int64_t block_rows(int64_t E) { return E <= 64 ? 32 : 64; }
+int64_t block_rows(int64_t E) {
+    return E <= 32 ? CfgE32::BM : E <= 64 ? CfgE64::BM : E <= 128 ? CfgE128::BM : CfgE256::BM;
+}
 
 constexpr int64_t SPLIT_TARGET_BLOCKS = 256;  // blocks the K split aims for (about one per CU)
+constexpr size_t k_max_scratch_rows = 8;       // a routing pass holds at least this many rows at top_k = 64
 constexpr int64_t MAX_SPLIT = 64;
 
 }  // namespace
@@ -334,26 +410,34 @@ size_t projection_workspace_bytes(int64_t T, int64_t H, int64_t E, rudnn_moe_dty
 
 namespace {
 
-template <typename T, int EP, int WM, int WN, int WK, int NPER, int G>
+template <typename T, typename C, int NPER, int G>
 hipError_t go(const T* x, const T* wr, int64_t Tn, int64_t H, int64_t E, int64_t k, bool renorm, T* logits_out,
               uint32_t* idx, T* w, float* partials, int64_t S, hipStream_t s) {
-    typedef proj::Cfg<EP, WM, WN, WK> C;
-    constexpr int RPB = proj::THREADS / G;
-    static const hipError_t attr = hipFuncSetAttribute((const void*)proj::project_route<T, EP, WM, WN, WK, NPER, G>,
+    constexpr int RPB = C::THREADS / G;
+    static_assert(proj::REDUCE_THREADS % (C::EP / 4) == 0, "column quads tile the reduce block");
+    static const hipError_t attr = hipFuncSetAttribute((const void*)proj::project_route<T, C, NPER, G>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     (void)attr;
     const int64_t mblocks = (Tn + C::BM - 1) / C::BM;
-    const size_t smem =
-        std::max((size_t)2 * C::STAGE, (size_t)C::RED + (S > 1 ? 0 : (size_t)RPB * (size_t)k * 8));
+    // routing rows per pass: all groups, unless their scratch would not fit beside the reduce tile
+    constexpr size_t LDS = 160 * 1024;
+    static_assert((size_t)C::RED + (size_t)k_max_scratch_rows * 8 * 64 <= LDS, "room for a routing pass");
+    const int64_t rpp = std::min((int64_t)RPB, (int64_t)((LDS - (size_t)C::RED) / ((size_t)k * 8)));
+    const size_t smem = std::max((size_t)C::NS * C::STAGE, (size_t)C::RED + (S > 1 ? 0 : (size_t)rpp * k * 8));
     timing_before(RUDNN_MOE_KERNEL_ROUTE_PROJECTED, s);
-    proj::project_route<T, EP, WM, WN, WK, NPER, G><<<dim3((unsigned)(mblocks * S)), dim3(proj::THREADS), smem, s>>>(
-        x, wr, Tn, (int)H, (int)E, (int)k, renorm ? 1 : 0, (int)S, partials, logits_out, idx, w);
+    proj::project_route<T, C, NPER, G><<<dim3((unsigned)(mblocks * S)), dim3(C::THREADS), smem, s>>>(
+        x, wr, Tn, (int)H, (int)E, (int)k, renorm ? 1 : 0, (int)S, (int)rpp, partials, logits_out, idx, w);
     timing_after(RUDNN_MOE_KERNEL_ROUTE_PROJECTED, s);
     if (S > 1) {
+        // PP: a power of two <= min(S, 1024 / C4) parts per column quad; RB rows per block
+        constexpr int C4 = C::EP / 4;
+        int PP = 1;
+        while (PP * 2 <= S && PP * 2 <= proj::REDUCE_THREADS / C4) PP *= 2;
+        const int RB = proj::REDUCE_THREADS / (C4 * PP);
+        const size_t rsmem = ((size_t)PP * RB * C::EP + (size_t)RB * k * 2) * 4;
         timing_before(RUDNN_MOE_KERNEL_ROUTE_PROJECTED_REDUCE, s);
-        proj::route_partials<T, NPER, G><<<dim3((unsigned)((Tn + RPB - 1) / RPB)), dim3(proj::THREADS),
-                                           (size_t)RPB * (size_t)k * 8, s>>>(
-            partials, Tn, EP, (int)S, (int)E, (int)k, renorm ? 1 : 0, logits_out, idx, w);
+        proj::route_partials<T, NPER, G><<<dim3((unsigned)((Tn + RB - 1) / RB)), dim3(proj::REDUCE_THREADS), rsmem, s>>>(
+            partials, Tn, C::EP, (int)S, PP, RB, (int)E, (int)k, renorm ? 1 : 0, logits_out, idx, w);
         timing_after(RUDNN_MOE_KERNEL_ROUTE_PROJECTED_REDUCE, s);
     }
     return hipGetLastError();
@@ -367,12 +451,12 @@ hipError_t launch_t(const void* xv, const void* wv, int64_t Tn, int64_t H, int64
     T* logits_out = (T*)lo;
     T* w = (T*)wo;
     // lanes per row as in the softmax router: the smallest power of two G with G * 16 >= E
-    if (E <= 8) return go<T, 32, 1, 1, 4, 8, 1>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
-    if (E <= 16) return go<T, 32, 1, 1, 4, 16, 1>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
-    if (E <= 32) return go<T, 32, 1, 1, 4, 16, 2>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
-    if (E <= 64) return go<T, 64, 1, 2, 2, 16, 4>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
-    if (E <= 128) return go<T, 128, 2, 2, 1, 16, 8>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
-    return go<T, 256, 2, 2, 1, 16, 16>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
+    if (E <= 8) return go<T, CfgE32, 8, 1>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
+    if (E <= 16) return go<T, CfgE32, 16, 1>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
+    if (E <= 32) return go<T, CfgE32, 16, 2>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
+    if (E <= 64) return go<T, CfgE64, 16, 4>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
+    if (E <= 128) return go<T, CfgE128, 16, 8>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
+    return go<T, CfgE256, 16, 16>(x, wr, Tn, H, E, k, renorm, logits_out, idx, w, partials, S, s);
 }
 
 }  // namespace

@@ -100,8 +100,8 @@ __device__ __forceinline__ uint32_t key_id(typename RouteBits<LT>::key k) {
 // Routes one row held by a group of G lanes (steps 1-4 above) and, for a live row, stores its
 // k indices and weights at idx/w[row * k ..].  raw: this lane's NPER logit bits, experts
 // e0 = (lane % G) * NPER onwards (entries at e >= E are ignored).  si/se: this group's k-entry
-// LDS scratch (winner ids, e_j).  Every thread of the block must call it together (it holds a
-// barrier); whole groups are live or not.
+// LDS scratch (winner ids, e_j), touched only by live rows.  Every thread of the block must call
+// it together (it holds a barrier); whole groups are live or not.
 template <typename LT, int NPER, int G>
 __device__ __forceinline__ void route_row(const typename RouteBits<LT>::raw (&raw)[NPER], int E, int k, int renorm,
                                           bool live, int64_t row, uint32_t* si, float* se, uint32_t* __restrict__ idx,
@@ -138,7 +138,7 @@ __device__ __forceinline__ void route_row(const typename RouteBits<LT>::raw (&ra
         if (j == 0) m = xw;
         const float e = expf(xw - m);  // -inf logits give 0 exactly
         den += e;
-        if (l == 0) {
+        if (live && l == 0) {
             si[j] = key_id<LT>(win);
             se[j] = e;
         }

@@ -97,6 +97,10 @@ EDGE = [
     (640, 1024, 32, 32, "f16"),
     (3, 8, 5, 2, "f32"),
     (16, 7168, 256, 8, "bf16"),
+    (700, 64, 128, 64, "f16"),       # one K step: no split, routing scratch for top_k = 64
+    (300, 32, 256, 64, "f32"),
+    (40000, 200, 16, 4, "bf16"),     # ring deeper than the K loop, ragged tail, no split
+    (33000, 4104, 128, 8, "bf16"),   # ring over many steps, ragged tail, 129 token tiles
 ]
 
 
