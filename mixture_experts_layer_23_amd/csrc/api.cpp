@@ -221,7 +221,7 @@ rudnn_moe_status rudnn_moe_route_projected(const void* input, rudnn_moe_dtype dt
 
 size_t rudnn_moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
-    return align_up(sizeof(int32_t) * (size_t)(dispatch_chunks(T * top_k) * E));
+    return dispatch_workspace_bytes(T * top_k, E);
 }
 
 rudnn_moe_status rudnn_moe_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input,

@@ -5,14 +5,15 @@
 // (256..4096, see dispatch_chunk).  Four kernels:
 //   count  one block per chunk: LDS histogram of the chunk's expert ids, stored as
 //          chunk_counts[c, e] (every entry written, so nothing needs clearing first);
-//   scan   one block: per expert, the exclusive sum of its counts over the chunks (in place,
-//          turning counts into per-chunk bases; the chunks are split over 1024 / E thread
-//          groups), then the exclusive sum over experts -> expert_offsets[E+1];
-//   rank   one block per chunk: the stable rank of each pair among the chunk's pairs of the
-//          same expert (wavefront ballots for lanes with equal ids, LDS counters across the
-//          block's waves and rounds); token_map[a] = offsets[e] + base[c, e] + rank.  Rows of
-//          an expert therefore follow (t, j) order, and the result does not depend on
-//          scheduling (no global atomics);
+//   scan   one block per expert: the exclusive sum of its counts over the chunks (a block scan,
+//          in place, turning counts into per-chunk bases) and the expert's total;
+//   rank   one block per chunk: the exclusive sum of the totals over experts (every block, in
+//          LDS; block 0 stores it as expert_offsets[E+1]), then the stable rank of each pair
+//          among the chunk's pairs of the same expert (the lanes of a wavefront holding the
+//          same id are found with one ballot per id bit, LDS counters carry across the block's
+//          waves and rounds); token_map[a] = offsets[e] + base[c, e] + rank.  Rows of an expert
+//          therefore follow (t, j) order, and the result does not depend on scheduling (no
+//          global atomics);
 //   copy   one wavefront per (token, 2 KiB piece of the row): the piece is read from HBM once
 //          in 16-byte vectors and written to the token's k dispatched rows (plain stores
 //          measured faster here than non-temporal ones).
@@ -37,55 +38,46 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const uint32_t* __r
     for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunks, int E,
-                                                            int32_t* __restrict__ offsets) {
+// Block e: the exclusive prefix of expert e's counts over the chunks, 256 chunks per pass.
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunks, int E,
+                                                            int32_t* __restrict__ totals) {
     __shared__ int scratch[17];
-    __shared__ int part[1024];  // [group][expert] chunk-range totals, then their prefix
-    const int groups = max(1, min(1024 / E, nchunks));
-    const int per = (nchunks + groups - 1) / groups;
-    const int t = threadIdx.x, e = t % E, grp = t / E;
-    const bool active = grp < groups;
-    const int c0 = min(nchunks, grp * per), c1 = min(nchunks, c0 + per);
-    int sum = 0;
-    if (active) {
-#pragma unroll 8
-        for (int c = c0; c < c1; ++c) sum += chunk_counts[(int64_t)c * E + e];
+    const int e = blockIdx.x;
+    int running = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += blockDim.x) {
+        const int c = c0 + (int)threadIdx.x;
+        const int v = c < nchunks ? chunk_counts[(int64_t)c * E + e] : 0;
+        int pass_total;
+        const int excl = block_exclusive_scan(v, scratch, &pass_total);
+        if (c < nchunks) chunk_counts[(int64_t)c * E + e] = running + excl;
+        running += pass_total;
     }
-    if (active) part[grp * E + e] = sum;
-    __syncthreads();
-    int total = 0;
-    if (t < E) {  // exclusive prefix over the groups of expert t
-        for (int g = 0; g < groups; ++g) {
-            const int v = part[g * E + t];
-            part[g * E + t] = total;
-            total += v;
-        }
-    }
-    __syncthreads();
-    if (active) {  // per-chunk bases inside the expert, in place
-        int run = part[grp * E + e];
-#pragma unroll 8
-        for (int c = c0; c < c1; ++c) {
-            const int n = chunk_counts[(int64_t)c * E + e];
-            chunk_counts[(int64_t)c * E + e] = run;
-            run += n;
-        }
-    }
-    int grand;
-    const int excl = block_exclusive_scan(t < E ? total : 0, scratch, &grand);
-    if (t < E) offsets[t] = excl;
-    if (t == 0) offsets[E] = grand;
+    if (threadIdx.x == 0) totals[e] = running;
 }
 
 __global__ __launch_bounds__(256) void dispatch_rank_kernel(const uint32_t* __restrict__ idx, int64_t pairs, int E,
-                                                            int chunk, const int32_t* __restrict__ chunk_base,
-                                                            const int32_t* __restrict__ offsets,
+                                                            int id_bits, int chunk,
+                                                            const int32_t* __restrict__ chunk_base,
+                                                            const int32_t* __restrict__ totals,
+                                                            int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ token_map) {
     extern __shared__ int sm[];
-    int* run = sm;       // [E]    pairs of expert e already ranked in earlier rounds
-    int* wcnt = sm + E;  // [4][E] pairs of expert e held by wave w in this round
-    for (int i = threadIdx.x; i < 5 * E; i += blockDim.x) sm[i] = 0;
+    __shared__ int scratch[17];
+    int* off = sm;           // [E]    expert offsets (exclusive sum of the totals)
+    int* run = sm + E;       // [E]    pairs of expert e already ranked in earlier rounds
+    int* wcnt = sm + 2 * E;  // [4][E] pairs of expert e held by wave w in this round
+    for (int i = threadIdx.x; i < 5 * E; i += blockDim.x) sm[E + i] = 0;
+    for (int e0 = 0, carry = 0; e0 < E; e0 += blockDim.x) {  // E <= 1024: at most 4 passes
+        const int e = e0 + (int)threadIdx.x;
+        int pass_total;
+        const int excl = block_exclusive_scan(e < E ? totals[e] : 0, scratch, &pass_total);
+        if (e < E) off[e] = carry + excl;
+        carry += pass_total;
+        if (blockIdx.x == 0 && threadIdx.x == 0 && e0 + (int)blockDim.x >= E) offsets[E] = carry;
+    }
     __syncthreads();
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = off[e];
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int64_t a0 = (int64_t)blockIdx.x * chunk;
@@ -96,31 +88,26 @@ __global__ __launch_bounds__(256) void dispatch_rank_kernel(const uint32_t* __re
         const bool in = a < a1;
         const uint32_t e = in ? idx[a] : 0xffffffffu;
         const bool valid = in && e < (uint32_t)E;
-        // Group the wave's lanes by expert id: one iteration per distinct id.
-        uint64_t rem = __ballot(valid);
-        int rank = 0, group = 0;
-        while (rem != 0) {
-            const int leader = __builtin_ctzll(rem);
-            const uint32_t le = (uint32_t)readlane((int)e, leader);
-            const uint64_t peers = __ballot(valid && e == le);
-            if (valid && e == le) {
-                rank = __popcll(peers & lt_mask);
-                if (lane == leader) group = __popcll(peers);
-            }
-            rem &= ~peers;
+        // Lanes holding the same id: agree with this lane on every id bit.
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < id_bits; ++b) {
+            const uint64_t ones = __ballot(valid && ((e >> b) & 1u));
+            peers &= ((e >> b) & 1u) ? ones : ~ones;
         }
-        if (group) wcnt[wave * E + e] = group;
+        const int rank = __popcll(peers & lt_mask);
+        const bool leader = valid && rank == 0;  // the lowest lane of its id
+        if (leader) wcnt[wave * E + e] = __popcll(peers);
         __syncthreads();
         if (valid) {
             int r = run[e] + rank;
             for (int w = 0; w < wave; ++w) r += wcnt[w * E + e];
-            token_map[a] = offsets[e] + base[e] + r;
+            token_map[a] = off[e] + base[e] + r;
         } else if (in) {
             token_map[a] = -1;
         }
         __syncthreads();
-        if (group) {
-            atomicAdd(&run[e], group);
+        if (leader) {  // one leader per id and wave: waves holding the same id add concurrently
+            atomicAdd(&run[e], __popcll(peers));
             wcnt[wave * E + e] = 0;
         }
         __syncthreads();
@@ -186,12 +173,15 @@ hipError_t launch_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E,
     timing_before(RUDNN_MOE_KERNEL_DISPATCH_COUNT, s);
     dispatch_count_kernel<<<nchunks, 256, E * sizeof(int), s>>>(idx, pairs, Ei, chunk, chunk_counts);
     timing_after(RUDNN_MOE_KERNEL_DISPATCH_COUNT, s);
+    int32_t* totals = (int32_t*)((unsigned char*)chunk_counts + dispatch_totals_offset(pairs, E));
+    int id_bits = 0;
+    while (((int64_t)1 << id_bits) < E) ++id_bits;
     timing_before(RUDNN_MOE_KERNEL_DISPATCH_SCAN, s);
-    dispatch_scan_kernel<<<1, 1024, 0, s>>>(chunk_counts, nchunks, Ei, offsets);
+    dispatch_scan_kernel<<<Ei, 256, 0, s>>>(chunk_counts, nchunks, Ei, totals);
     timing_after(RUDNN_MOE_KERNEL_DISPATCH_SCAN, s);
     timing_before(RUDNN_MOE_KERNEL_DISPATCH_RANK, s);
-    dispatch_rank_kernel<<<nchunks, 256, 5 * E * sizeof(int), s>>>(idx, pairs, Ei, chunk, chunk_counts, offsets,
-                                                                    token_map);
+    dispatch_rank_kernel<<<nchunks, 256, 6 * E * sizeof(int), s>>>(idx, pairs, Ei, id_bits, chunk, chunk_counts,
+                                                                    totals, offsets, token_map);
     timing_after(RUDNN_MOE_KERNEL_DISPATCH_RANK, s);
     const int ki = (int)k;
     auto copy = [&](auto unit) {

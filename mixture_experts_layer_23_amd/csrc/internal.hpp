@@ -12,9 +12,9 @@ namespace rudnn {
 
 // Dispatch works on chunks of consecutive (token, slot) pairs; one block of the count and rank
 // kernels owns one chunk.  The chunk is 256..4096 pairs (a multiple of the 256-thread block),
-// about pairs / 512: enough blocks for the count and rank kernels, few enough chunks for the
-// one-block scan.  Workspace: [nchunks, E] int32 per-chunk counts that the scan kernel turns
-// into per-chunk bases in place.
+// about pairs / 512: enough blocks for the count and rank kernels.  Workspace: [nchunks, E]
+// int32 per-chunk counts that the scan kernel turns into per-chunk bases in place, then [E]
+// int32 expert totals.
 #ifndef RUDNN_DISPATCH_CHUNKS
 #define RUDNN_DISPATCH_CHUNKS 512
 #endif
@@ -33,6 +33,13 @@ constexpr int64_t MAX_EXPERTS = 1024;
 constexpr int64_t MAX_TOP_K = 64;
 
 inline size_t align_up(size_t n, size_t a = 256) { return (n + a - 1) / a * a; }
+// Bytes of the dispatch workspace (see dispatch_chunk) and the offset of its expert totals.
+inline size_t dispatch_totals_offset(int64_t pairs, int64_t E) {
+    return align_up(sizeof(int32_t) * (size_t)(dispatch_chunks(pairs) * E));
+}
+inline size_t dispatch_workspace_bytes(int64_t pairs, int64_t E) {
+    return dispatch_totals_offset(pairs, E) + align_up(sizeof(int32_t) * (size_t)E);
+}
 inline size_t dtype_size(rudnn_moe_dtype d) { return d == RUDNN_MOE_F32 ? 4 : 2; }
 
 // Per-thread one-shot timing hook (rudnn_moe_time_next_launch).
