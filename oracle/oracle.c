@@ -17,6 +17,10 @@
  *                                      down [E,H,I], no capacity drops, order inside an
  *                                      expert unspecified, a stored map restores order;
  *   section 6 "MoE aufrufen"        -- the staged call forms and the full forward;
+ *   section 12 "MoE-Training erster Ordnung" -- FP32 weights of a fixed selection and their
+ *                                      logits gradients (softmax or sigmoid scoring, optional
+ *                                      renormalisation, then scale; gather semantics), and the
+ *                                      backward chain combine -> experts -> dispatch -> router;
  *   section 10 "Gruppenbeschraenktes Sigmoid-MoE-Routing" -- sigmoid scores, an optional FP32
  *                                      correction bias [E] that only steers the selection,
  *                                      group scores (maximum, or the sum of the two largest
@@ -47,6 +51,22 @@
  *    that caller step): logits[t, e] = sum_h input[t, h] * router[e, h] with the router [E, H]
  *    in the token dtype, summed in double and rounded once to the token dtype, which is then
  *    the logits dtype; routing follows section 4 unchanged.
+ *  - Training (section 12 "MoE-Training erster Ordnung"): the weights of a fixed selection are
+ *    w_j = scale * score(idx_j) / S, score = the softmax over all E (or the sigmoid) of the
+ *    row, S = the sum of score(idx_j') over the k selected entries when renormalising (a
+ *    repeated index counts each time it appears), else 1; they are FP32.  Their logits
+ *    gradient is the chain rule through that formula, rounded once to the logits dtype.  An
+ *    index outside [0, E) makes the whole row NaN (weights and gradient).
+ *  - combine_backward: dexpert[map[t,j]] = dt(w[t,j] * dout[t]), dweights[t,j] = FP32 of
+ *    sum_h dout[t,h] * y[map[t,j],h]; a token with a map entry outside [0, rows) gets NaN
+ *    dweights (its forward output is NaN) and no dexpert row for that entry.
+ *  - dispatch_backward: dinput[t] = dt(sum_j ddispatched[map[t,j]]), j ascending, no weights;
+ *    NaN row for a token with an invalid map entry, as in combine.
+ *  - experts backward, per dispatched row of expert e: dh = down_e^T dy; dg = dt(dh * u *
+ *    silu'(g)), du = dt(dh * silu(g)) (stored in the dtype, like h in the forward, because
+ *    they are the operands of the products that follow); dx = dt(gate_e^T dg + up_e^T du);
+ *    dgate_e = FP32(sum_r dg_r x_r^T), dup_e likewise with du, ddown_e = FP32(sum_r dy_r h_r^T)
+ *    with h the forward's stored activation.  silu'(z) = s (1 + z (1 - s)), s = 1/(1 + e^-z).
  *  - Sigmoid routing decides in FP32, the precision the guide gives the bias: s32 = the
  *    sigmoid rounded once to FP32, corrected score c = s32 + bias in FP32, a group score is the
  *    largest c of the group or the FP32 sum of its two largest; groups and then experts are
@@ -639,4 +659,240 @@ int oracle_forward(const void* input, int dt, const void* logits, int ldt, int64
     free(w);
     free(idx);
     return rc;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* First-order training (user guide section 12).                                          */
+/* ------------------------------------------------------------------------------------ */
+
+enum { OR_SCORE_SOFTMAX = 0, OR_SCORE_SIGMOID = 1 };
+
+/* Scores of one row: the softmax over all E experts (max-subtracted, double) or the sigmoid of
+ * each logit.  No NaN-row rule here: NaN and infinities propagate by IEEE arithmetic. */
+static void row_scores(const double* x, int64_t E, int scoring, double* sc) {
+    if (scoring == OR_SCORE_SIGMOID) {
+        for (int64_t e = 0; e < E; ++e) sc[e] = sigmoid(x[e]);
+        return;
+    }
+    double m = -INFINITY;
+    for (int64_t e = 0; e < E; ++e)
+        if (x[e] > m) m = x[e];
+    double z = 0.0;
+    for (int64_t e = 0; e < E; ++e) {
+        sc[e] = exp(x[e] - m);
+        z += sc[e];
+    }
+    for (int64_t e = 0; e < E; ++e) sc[e] /= z;
+}
+
+/* d score_i / d x_e of one row. */
+static double score_partial(const double* sc, int scoring, int64_t i, int64_t e) {
+    if (scoring == OR_SCORE_SIGMOID) return i == e ? sc[i] * (1.0 - sc[i]) : 0.0;
+    return sc[i] * ((i == e ? 1.0 : 0.0) - sc[e]);
+}
+
+/* FP32 weights of a fixed selection idx [T,k] (int64; outside [0, E) = invalid): w_j = scale *
+ * score(idx_j) / S.  weights_exact (may be NULL) receives the double values. */
+int oracle_selected_router_weights(const void* logits, int ldt, int64_t T, int64_t E, const int64_t* idx,
+                                   int64_t k, int scoring, int renormalize, double scale, float* weights,
+                                   double* weights_exact) {
+    if (T < 0 || E < 1 || k < 1 || (scoring != OR_SCORE_SOFTMAX && scoring != OR_SCORE_SIGMOID)) return -1;
+#pragma omp parallel
+    {
+        double* x = (double*)malloc(sizeof(double) * (size_t)E);
+        double* sc = (double*)malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t* ix = idx + t * k;
+            int bad = 0;
+            for (int64_t j = 0; j < k; ++j)
+                if (ix[j] < 0 || ix[j] >= E) bad = 1;
+            for (int64_t e = 0; e < E; ++e) x[e] = load_val(logits, ldt, t * E + e);
+            if (!bad) row_scores(x, E, scoring, sc);
+            double S = 1.0;
+            if (!bad && renormalize) {
+                S = 0.0;
+                for (int64_t j = 0; j < k; ++j) S += sc[ix[j]];
+            }
+            for (int64_t j = 0; j < k; ++j) {
+                double v = bad ? NAN : scale * sc[ix[j]] / S;
+                weights[t * k + j] = (float)v;
+                if (weights_exact) weights_exact[t * k + j] = v;
+            }
+        }
+        free(x);
+        free(sc);
+    }
+    return 0;
+}
+
+/* Logits gradient [T,E] (ldt) of the weights above, given grad_weights [T,k] (FP32):
+ * dx_e = sum_j g_j d w_j / d x_e with the quotient rule written out,
+ * d w_j / d x_e = scale * (d score_{i_j}/d x_e * S - score_{i_j} * d S / d x_e) / S^2,
+ * d S / d x_e = sum_j' d score_{i_j'} / d x_e (0 without renormalisation). */
+int oracle_selected_router_backward(const void* logits, int ldt, int64_t T, int64_t E, const int64_t* idx,
+                                    int64_t k, int scoring, int renormalize, double scale,
+                                    const float* grad_weights, void* grad_logits) {
+    if (T < 0 || E < 1 || k < 1 || (scoring != OR_SCORE_SOFTMAX && scoring != OR_SCORE_SIGMOID)) return -1;
+#pragma omp parallel
+    {
+        double* x = (double*)malloc(sizeof(double) * (size_t)E);
+        double* sc = (double*)malloc(sizeof(double) * (size_t)E);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t* ix = idx + t * k;
+            int bad = 0;
+            for (int64_t j = 0; j < k; ++j)
+                if (ix[j] < 0 || ix[j] >= E) bad = 1;
+            if (bad) {
+                for (int64_t e = 0; e < E; ++e) store_val(grad_logits, ldt, t * E + e, NAN);
+                continue;
+            }
+            for (int64_t e = 0; e < E; ++e) x[e] = load_val(logits, ldt, t * E + e);
+            row_scores(x, E, scoring, sc);
+            double S = 1.0;
+            if (renormalize) {
+                S = 0.0;
+                for (int64_t j = 0; j < k; ++j) S += sc[ix[j]];
+            }
+            for (int64_t e = 0; e < E; ++e) {
+                double dS = 0.0;
+                if (renormalize)
+                    for (int64_t j = 0; j < k; ++j) dS += score_partial(sc, scoring, ix[j], e);
+                double acc = 0.0;
+                for (int64_t j = 0; j < k; ++j) {
+                    const double dw = scale * (score_partial(sc, scoring, ix[j], e) * S - sc[ix[j]] * dS) / (S * S);
+                    acc += (double)grad_weights[t * k + j] * dw;
+                }
+                store_val(grad_logits, ldt, t * E + e, acc);
+            }
+        }
+        free(x);
+        free(sc);
+    }
+    return 0;
+}
+
+/* Backward of combine: dexpert [rows,H] (dt, only rows named by valid map entries are written)
+ * and dweights [T,k] FP32. */
+int oracle_combine_backward(const void* expert_output, int dt, const int32_t* token_map, const void* weights,
+                            int wdt, const void* grad_output, int64_t T, int64_t k, int64_t H, int64_t rows,
+                            void* grad_expert, float* grad_weights) {
+    if (T < 0 || k < 1 || H < 1 || rows < 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        int bad = 0;
+        for (int64_t j = 0; j < k; ++j)
+            if (token_map[t * k + j] < 0 || token_map[t * k + j] >= rows) bad = 1;
+        for (int64_t j = 0; j < k; ++j) {
+            const int64_t r = token_map[t * k + j];
+            const int ok = r >= 0 && r < rows;
+            const double w = load_val(weights, wdt, t * k + j);
+            double dw = 0.0;
+            for (int64_t c = 0; c < H; ++c) {
+                const double go = load_val(grad_output, dt, t * H + c);
+                if (ok) {
+                    store_val(grad_expert, dt, r * H + c, w * go);
+                    dw += go * load_val(expert_output, dt, r * H + c);
+                }
+            }
+            grad_weights[t * k + j] = bad ? NAN : (float)dw;
+        }
+    }
+    return 0;
+}
+
+/* Backward of dispatch: dinput[t] = dt(sum_j ddispatched[map[t,j]]), j ascending. */
+int oracle_dispatch_backward(const void* grad_dispatched, int dt, const int32_t* token_map, int64_t T, int64_t k,
+                             int64_t H, int64_t rows, void* grad_input) {
+    if (T < 0 || k < 1 || H < 1 || rows < 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        int bad = 0;
+        for (int64_t j = 0; j < k; ++j)
+            if (token_map[t * k + j] < 0 || token_map[t * k + j] >= rows) bad = 1;
+        for (int64_t c = 0; c < H; ++c) {
+            double s = 0.0;
+            if (bad)
+                s = NAN;
+            else
+                for (int64_t j = 0; j < k; ++j) s += load_val(grad_dispatched, dt, (int64_t)token_map[t * k + j] * H + c);
+            store_val(grad_input, dt, t * H + c, s);
+        }
+    }
+    return 0;
+}
+
+static double silu_grad(double z) {
+    const double s = sigmoid(z);
+    return s * (1.0 + z * (1.0 - s));
+}
+
+/* Backward of the SwiGLU experts on the dispatched rows: rows [offsets[e], offsets[e+1]) of
+ * dispatched/grad_expert_output belong to expert e.  Writes grad_dispatched [rows,H] (dt) for
+ * those rows and the FP32 weight gradients dgate, dup [E,I,H] and ddown [E,H,I] (all entries). */
+int oracle_experts_backward(const void* dispatched, const int32_t* expert_offsets, int64_t E, int dt,
+                            const void* gate, const void* up, const void* down, int64_t H, int64_t I,
+                            const void* grad_expert_output, void* grad_dispatched, float* dgate, float* dup,
+                            float* ddown) {
+    if (E < 1 || H < 1 || I < 1) return -1;
+    for (int64_t e = 0; e < E; ++e)
+        if (expert_offsets[e + 1] < expert_offsets[e]) return -1;
+    for (int64_t e = 0; e < E; ++e) {
+        const int64_t a = expert_offsets[e], n = expert_offsets[e + 1] - a;
+        double* X = (double*)calloc((size_t)(n * H) + 1, sizeof(double));
+        double* DY = (double*)calloc((size_t)(n * H) + 1, sizeof(double));
+        double* Hh = (double*)calloc((size_t)(n * I) + 1, sizeof(double)); /* h, as stored (dt) */
+        double* DG = (double*)calloc((size_t)(n * I) + 1, sizeof(double));
+        double* DU = (double*)calloc((size_t)(n * I) + 1, sizeof(double));
+        for (int64_t r = 0; r < n; ++r)
+            for (int64_t c = 0; c < H; ++c) {
+                X[r * H + c] = load_val(dispatched, dt, (a + r) * H + c);
+                DY[r * H + c] = load_val(grad_expert_output, dt, (a + r) * H + c);
+            }
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < I; ++i) {
+            for (int64_t r = 0; r < n; ++r) {
+                double g = 0.0, u = 0.0, dh = 0.0;
+                for (int64_t c = 0; c < H; ++c) {
+                    g += load_val(gate, dt, (e * I + i) * H + c) * X[r * H + c];
+                    u += load_val(up, dt, (e * I + i) * H + c) * X[r * H + c];
+                    dh += load_val(down, dt, (e * H + c) * I + i) * DY[r * H + c];
+                }
+                Hh[r * I + i] = round_to(silu(g) * u, dt);
+                DG[r * I + i] = round_to(dh * u * silu_grad(g), dt);
+                DU[r * I + i] = round_to(dh * silu(g), dt);
+            }
+        }
+        /* dx = gate^T dg + up^T du */
+#pragma omp parallel for schedule(static)
+        for (int64_t c = 0; c < H; ++c)
+            for (int64_t r = 0; r < n; ++r) {
+                double s = 0.0;
+                for (int64_t i = 0; i < I; ++i)
+                    s += load_val(gate, dt, (e * I + i) * H + c) * DG[r * I + i] +
+                         load_val(up, dt, (e * I + i) * H + c) * DU[r * I + i];
+                store_val(grad_dispatched, dt, (a + r) * H + c, s);
+            }
+        /* weight gradients: sums over the expert's rows */
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < I; ++i)
+            for (int64_t c = 0; c < H; ++c) {
+                double sg = 0.0, su = 0.0, sd = 0.0;
+                for (int64_t r = 0; r < n; ++r) {
+                    sg += DG[r * I + i] * X[r * H + c];
+                    su += DU[r * I + i] * X[r * H + c];
+                    sd += DY[r * H + c] * Hh[r * I + i];
+                }
+                dgate[(e * I + i) * H + c] = (float)sg;
+                dup[(e * I + i) * H + c] = (float)su;
+                ddown[(e * H + c) * I + i] = (float)sd;
+            }
+        free(X);
+        free(DY);
+        free(Hh);
+        free(DG);
+        free(DU);
+    }
+    return 0;
 }

@@ -45,13 +45,19 @@ def lib() -> ctypes.CDLL:
         L.oracle_route_sigmoid_grouped.argtypes = [P, I32, I64, I64, P, I64, I64, I64, I32, I32, D, P, P, P]
         L.oracle_forward_sigmoid_grouped.argtypes = [P, I32, P, I32, I64, I64, P, I64, I64, I64, I32, I32, D,
                                                      P, P, P, I64, I64, P]
+        L.oracle_selected_router_weights.argtypes = [P, I32, I64, I64, P, I64, I32, I32, D, P, P]
+        L.oracle_selected_router_backward.argtypes = [P, I32, I64, I64, P, I64, I32, I32, D, P, P]
+        L.oracle_combine_backward.argtypes = [P, I32, P, P, I32, P, I64, I64, I64, I64, P, P]
+        L.oracle_dispatch_backward.argtypes = [P, I32, P, I64, I64, I64, I64, P]
+        L.oracle_experts_backward.argtypes = [P, P, I64, I32, P, P, P, I64, I64, P, P, P, P, P]
         L.oracle_decode.argtypes = [P, I32, I64, P]
         L.oracle_encode.argtypes = [P, I32, I64, P]
         L.oracle_set_num_threads.argtypes = [I32]
         for f in ("oracle_route", "oracle_dispatch", "oracle_expert_rows", "oracle_experts_forward",
                   "oracle_combine", "oracle_forward", "oracle_num_threads", "oracle_route_sigmoid_grouped",
                   "oracle_forward_sigmoid_grouped", "oracle_project", "oracle_route_projected",
-                  "oracle_forward_projected"):
+                  "oracle_forward_projected", "oracle_selected_router_weights", "oracle_selected_router_backward",
+                  "oracle_combine_backward", "oracle_dispatch_backward", "oracle_experts_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -280,3 +286,93 @@ def forward_projected(x: torch.Tensor, router: torch.Tensor, top_k: int, renorma
                                       _p(gate), _p(up), _p(down), H, I, _p(out)):
         raise ValueError("oracle_forward_projected: bad arguments")
     return out
+
+
+# ---------------------------------------------------------------------------------------------
+# First-order training (user guide section 12)
+# ---------------------------------------------------------------------------------------------
+
+SCORING = {"softmax": 0, "sigmoid": 1}
+
+
+def _idx64(indices) -> np.ndarray:
+    a = indices.cpu().numpy() if isinstance(indices, torch.Tensor) else np.asarray(indices)
+    return np.ascontiguousarray(a.astype(np.int64))
+
+
+def selected_router_weights(logits: torch.Tensor, indices, scoring: str, renormalize: bool, scale: float):
+    """FP32 weights [T,k] of the fixed selection ``indices`` (any integer type; outside [0, E) =
+    invalid row) and their double values."""
+    logits = _cpu(logits)
+    T, E = logits.shape
+    ix = _idx64(indices)
+    k = ix.shape[1]
+    w = np.empty((T, k), np.float32)
+    wx = np.empty((T, k), np.float64)
+    if lib().oracle_selected_router_weights(_p(logits), _DT_CODE[logits.dtype], T, E, _p(ix), k, SCORING[scoring],
+                                            int(bool(renormalize)), float(scale), _p(w), _p(wx)):
+        raise ValueError("oracle_selected_router_weights: bad arguments")
+    return torch.from_numpy(w), wx
+
+
+def selected_router_backward(logits: torch.Tensor, indices, grad_weights, scoring: str, renormalize: bool,
+                             scale: float) -> torch.Tensor:
+    """Logits gradient [T,E] in the logits dtype."""
+    logits = _cpu(logits)
+    T, E = logits.shape
+    ix = _idx64(indices)
+    k = ix.shape[1]
+    g = np.ascontiguousarray(np.asarray(grad_weights.cpu() if isinstance(grad_weights, torch.Tensor) else grad_weights,
+                                        dtype=np.float32))
+    out = torch.empty(T, E, dtype=logits.dtype)
+    if lib().oracle_selected_router_backward(_p(logits), _DT_CODE[logits.dtype], T, E, _p(ix), k, SCORING[scoring],
+                                             int(bool(renormalize)), float(scale), _p(g), _p(out)):
+        raise ValueError("oracle_selected_router_backward: bad arguments")
+    return out
+
+
+def combine_backward(expert_output: torch.Tensor, token_map, weights: torch.Tensor, grad_output: torch.Tensor,
+                     grad_expert: torch.Tensor | None = None):
+    """Returns ``(dexpert [rows,H] (rows not named by a valid map entry keep grad_expert's
+    values, zeros by default), dweights [T,k] FP32)``."""
+    y, w, go = _cpu(expert_output), _cpu(weights), _cpu(grad_output)
+    tm = np.ascontiguousarray(np.asarray(token_map.cpu() if isinstance(token_map, torch.Tensor) else token_map,
+                                         dtype=np.int32))
+    T, k = tm.shape
+    rows, H = y.shape
+    dexp = torch.zeros(rows, H, dtype=y.dtype) if grad_expert is None else grad_expert.cpu().clone()
+    dw = np.empty((T, k), np.float32)
+    if lib().oracle_combine_backward(_p(y), _DT_CODE[y.dtype], _p(tm), _p(w), _DT_CODE[w.dtype], _p(go), T, k, H,
+                                     rows, _p(dexp), _p(dw)):
+        raise ValueError("oracle_combine_backward: bad arguments")
+    return dexp, torch.from_numpy(dw)
+
+
+def dispatch_backward(grad_dispatched: torch.Tensor, token_map) -> torch.Tensor:
+    d = _cpu(grad_dispatched)
+    tm = np.ascontiguousarray(np.asarray(token_map.cpu() if isinstance(token_map, torch.Tensor) else token_map,
+                                         dtype=np.int32))
+    T, k = tm.shape
+    rows, H = d.shape
+    out = torch.empty(T, H, dtype=d.dtype)
+    if lib().oracle_dispatch_backward(_p(d), _DT_CODE[d.dtype], _p(tm), T, k, H, rows, _p(out)):
+        raise ValueError("oracle_dispatch_backward: bad arguments")
+    return out
+
+
+def experts_backward(dispatched: torch.Tensor, offsets, gate, up, down, grad_expert_output: torch.Tensor):
+    """Returns ``(grad_dispatched [rows,H] dtype, dgate [E,I,H], dup [E,I,H], ddown [E,H,I] FP32)``;
+    rows outside [offsets[0], offsets[E]) of grad_dispatched are zero."""
+    x, dy = _cpu(dispatched), _cpu(grad_expert_output)
+    gate, up, down = _cpu(gate), _cpu(up), _cpu(down)
+    E, I, H = gate.shape
+    offs = np.ascontiguousarray(np.asarray(offsets.cpu() if isinstance(offsets, torch.Tensor) else offsets,
+                                           dtype=np.int32))
+    dx = torch.zeros(x.shape[0], H, dtype=x.dtype)
+    dg = torch.empty(E, I, H, dtype=torch.float32)
+    du = torch.empty(E, I, H, dtype=torch.float32)
+    dd = torch.empty(E, H, I, dtype=torch.float32)
+    if lib().oracle_experts_backward(_p(x), _p(offs), E, _DT_CODE[x.dtype], _p(gate), _p(up), _p(down), H, I, _p(dy),
+                                     _p(dx), _p(dg), _p(du), _p(dd)):
+        raise ValueError("oracle_experts_backward: bad arguments")
+    return dx, dg, du, dd

@@ -14,6 +14,7 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PINS = "test_oracle_pins.py"
 SIG = "test_oracle_sigmoid_pins.py"
 PROJ = "test_oracle_projection_pins.py"
+BWD = "test_oracle_backward_pins.py"
 
 MUTANTS = {
     "tie_to_higher_id": ("if (best < 0 || p[e] > p[best]) best = e;", "if (best < 0 || p[e] >= p[best]) best = e;"),
@@ -50,6 +51,20 @@ MUTANTS = {
     "proj_router_transposed": ("load_val(router, dt, e * H + h)", "load_val(router, dt, h * E + e)", PROJ),
     "proj_half_the_sum": ("for (int64_t h = 0; h < H; ++h) acc +=", "for (int64_t h = 0; h < H / 2; ++h) acc +=", PROJ),
     "proj_wrong_input_stride": ("load_val(input, dt, t * H + h)", "load_val(input, dt, t * E + h)", PROJ),
+    # first-order training, checked against its own pins
+    "bwd_quotient_rule_sign": ("(score_partial(sc, scoring, ix[j], e) * S - sc[ix[j]] * dS)",
+                               "(score_partial(sc, scoring, ix[j], e) * S + sc[ix[j]] * dS)", BWD),
+    "bwd_softmax_partial_index": ("return sc[i] * ((i == e ? 1.0 : 0.0) - sc[e]);",
+                                  "return sc[i] * ((i == e ? 1.0 : 0.0) - sc[i]);", BWD),
+    "bwd_scale_dropped": ("const double dw = scale * (", "const double dw = (", BWD),
+    "bwd_silu_grad_sign": ("return s * (1.0 + z * (1.0 - s));", "return s * (1.0 - z * (1.0 - s));", BWD),
+    "bwd_du_without_silu": ("DU[r * I + i] = round_to(dh * silu(g), dt);", "DU[r * I + i] = round_to(dh * g, dt);", BWD),
+    "bwd_ddown_from_input": ("sd += DY[r * H + c] * Hh[r * I + i];", "sd += DY[r * H + c] * X[r * H + (i % H)];", BWD),
+    "bwd_dx_without_up": ("s += load_val(gate, dt, (e * I + i) * H + c) * DG[r * I + i] +\n                         load_val(up, dt, (e * I + i) * H + c) * DU[r * I + i];",
+                          "s += load_val(gate, dt, (e * I + i) * H + c) * DG[r * I + i];", BWD),
+    "bwd_dweights_from_weight": ("dw += go * load_val(expert_output, dt, r * H + c);", "dw += go * w;", BWD),
+    "bwd_dispatch_skips_last": ("for (int64_t j = 0; j < k; ++j) s += load_val(grad_dispatched",
+                                "for (int64_t j = 0; j + 1 < k; ++j) s += load_val(grad_dispatched", BWD),
 }
 
 
