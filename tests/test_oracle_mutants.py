@@ -29,7 +29,8 @@ MUTANTS = {
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "gate_up_swapped": ("hb[r * I + i] = round_to(silu(g) * u, dt);", "hb[r * I + i] = round_to(silu(u) * g, dt);"),
     "down_transposed": ("wd[i] = load_val(down, dt, (e * H + c) * I + i);", "wd[i] = load_val(down, dt, (e * I + i) * H + c);"),
-    "combine_one_weight": ("double w = load_val(weights, wdt, t * k + j);", "double w = load_val(weights, wdt, t * k);"),
+    "combine_one_weight": ("double w = load_val(weights, wdt, t * k + j);\n                    s += w *",
+                           "double w = load_val(weights, wdt, t * k);\n                    s += w *"),
     "combine_drops_last": ("for (int64_t j = 0; j < k; ++j) {\n                    double w", "for (int64_t j = 0; j + 1 < k; ++j) {\n                    double w"),
     "dispatch_skips_first": ("for (int64_t a = 0; a < T * k; ++a)\n        if (expert_indices[a]", "for (int64_t a = 1; a < T * k; ++a)\n        if (expert_indices[a]"),
     "rounding_truncates": ("double r = nearbyint(x / q) * q;", "double r = trunc(x / q) * q;"),
