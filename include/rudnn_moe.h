@@ -265,6 +265,79 @@ rudnn_moe_status rudnn_moe_forward_projected(const rudnn_moe_experts* ex, const 
                                              int64_t T, rudnn_moe_routing_options opt, void* output,
                                              void* workspace, size_t workspace_size, hipStream_t stream);
 
+/* ---- First-order training (section 12 "MoE-Training erster Ordnung") ---- */
+
+/* Integer type of caller-provided expert indices (section 12: U32, I32 or I64). */
+typedef enum { RUDNN_MOE_U32 = 0, RUDNN_MOE_I32 = 1, RUDNN_MOE_I64 = 2 } rudnn_moe_index_type;
+
+/* RouterWeightOptions of section 12: RouterScoring::Softmax (0) or Sigmoid (1), optional
+ * renormalisation of the selected weights, then a finite positive scale. */
+typedef struct {
+    int32_t scoring;      /* 0: softmax over all E experts, 1: sigmoid of each logit */
+    int32_t renormalize;  /* != 0: divide by the sum of the selected scores */
+    double scale;
+} rudnn_moe_router_weight_options;
+
+/*
+ * selected_router_weights -- section 12 (selected_router_weights(&logits, &indices, options)).
+ * For each row t: w[t, j] = scale * score(indices[t, j]) / S, score = the FP32 softmax over all
+ * E experts of the row (or the sigmoid of each logit), S = sum_j score(indices[t, j]) when
+ * renormalising (gather semantics: a repeated index counts each time), else 1.
+ *   logits [T, E] logits_dtype;  indices [T, top_k] index_type;  weights [T, top_k] FP32, written
+ * An index outside [0, E) makes the row's weights NaN; nothing is read through it.
+ * Errors: SHAPE (T < 0, E < 1), ARGUMENT (top_k outside [1, min(E, 64)], scoring not 0/1, scale
+ * not finite and > 0, NULL, overlap), DTYPE (logits or index type), DEVICE, RUNTIME.
+ */
+rudnn_moe_status rudnn_moe_selected_router_weights(const void* logits, rudnn_moe_dtype logits_dtype, int64_t T,
+                                                   int64_t E, const void* indices, rudnn_moe_index_type index_type,
+                                                   int64_t top_k, rudnn_moe_router_weight_options opt,
+                                                   float* weights, hipStream_t stream);
+
+/*
+ * selected_router_backward -- section 12 (selected_router_backward(&logits, &indices,
+ * &grad_weights, options); RouterTrainingPlan::backward).  grad_logits[t, e] = sum_j
+ * grad_weights[t, j] * d w[t, j] / d logits[t, e] for the weights above: the gradient of the
+ * continuous weights of the fixed selection (not of the selection itself), computed in FP32 and
+ * rounded once to the logits dtype.  An index outside [0, E) makes the row NaN.
+ *   grad_weights [T, top_k] FP32;  grad_logits [T, E] logits_dtype, written
+ * Errors: as rudnn_moe_selected_router_weights.
+ */
+rudnn_moe_status rudnn_moe_selected_router_backward(const void* logits, rudnn_moe_dtype logits_dtype, int64_t T,
+                                                    int64_t E, const void* indices, rudnn_moe_index_type index_type,
+                                                    int64_t top_k, rudnn_moe_router_weight_options opt,
+                                                    const float* grad_weights, void* grad_logits,
+                                                    hipStream_t stream);
+
+/*
+ * combine_backward -- section 12 step 1 (dispatched.combine_backward(&expert_output,
+ * grad_output) -> (dexpert, dweights)), the backward of rudnn_moe_combine:
+ *   grad_expert_output[token_map[t, j]] = dtype(weights[t, j] * grad_output[t])
+ *   grad_weights[t, j] = sum_h grad_output[t, h] * expert_output[token_map[t, j], h]   (FP32)
+ *   expert_output, grad_expert_output [T*k, H] dtype;  token_map [T, k] int32;
+ *   weights [T, k] weights_dtype;  grad_output [T, H] dtype;  grad_weights [T, k] FP32
+ * Rows of grad_expert_output named by no valid map entry are not written.  A token with a map
+ * entry outside [0, T*k) gets NaN grad_weights and no row for that entry.  One strategy here.
+ * Errors: SHAPE, ARGUMENT, DTYPE, UNSUPPORTED (top_k > 64, H * sizeof(dtype) not a multiple
+ * of 16 or unaligned rows, T*k >= 2^31), DEVICE, RUNTIME.
+ */
+rudnn_moe_status rudnn_moe_combine_backward(const void* expert_output, rudnn_moe_dtype dtype,
+                                            const int32_t* token_map, const void* weights,
+                                            rudnn_moe_dtype weights_dtype, const void* grad_output, int64_t T,
+                                            int64_t top_k, int64_t H, void* grad_expert_output, float* grad_weights,
+                                            hipStream_t stream);
+
+/*
+ * dispatch_backward -- section 12 step 3 (dispatched.dispatch_backward(dinput)): the selected
+ * rows summed back into their token, without the routing weights:
+ *   grad_input[t] = dtype(sum_{j ascending} grad_dispatched[token_map[t, j]])   (FP32)
+ *   grad_dispatched [T*k, H] dtype;  token_map [T, k] int32;  grad_input [T, H] dtype, written
+ * A token with a map entry outside [0, T*k) gets a NaN row.
+ * Errors: as rudnn_moe_combine_backward.
+ */
+rudnn_moe_status rudnn_moe_dispatch_backward(const void* grad_dispatched, rudnn_moe_dtype dtype,
+                                             const int32_t* token_map, int64_t T, int64_t top_k, int64_t H,
+                                             void* grad_input, hipStream_t stream);
+
 /* Static, human-readable name of a status. */
 const char* rudnn_moe_status_string(rudnn_moe_status s);
 
@@ -287,7 +360,10 @@ typedef enum {
     RUDNN_MOE_KERNEL_ROUTE_SIGMOID_GROUPED = 11, /* group-limited sigmoid routing */
     RUDNN_MOE_KERNEL_ROUTE_PROJECTED = 12,        /* gate projection + routing */
     RUDNN_MOE_KERNEL_ROUTE_PROJECTED_REDUCE = 13, /* adds its H-split partials and routes */
-    RUDNN_MOE_KERNEL_COUNT = 14
+    RUDNN_MOE_KERNEL_SELECTED_ROUTER = 14,        /* router weights of a fixed selection, or their gradient */
+    RUDNN_MOE_KERNEL_COMBINE_BACKWARD = 15,
+    RUDNN_MOE_KERNEL_DISPATCH_BACKWARD = 16,
+    RUDNN_MOE_KERNEL_COUNT = 17
 } rudnn_moe_kernel;
 
 /* For the calling host thread: record `before` on the launch stream immediately before the

@@ -219,6 +219,92 @@ rudnn_moe_status rudnn_moe_route_projected(const void* input, rudnn_moe_dtype dt
                                           idx, w, workspace, stream));
 }
 
+static bool valid_index_type(rudnn_moe_index_type t) {
+    return t == RUDNN_MOE_U32 || t == RUDNN_MOE_I32 || t == RUDNN_MOE_I64;
+}
+
+static rudnn_moe_status selected_router_common(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E,
+                                               const void* idx, rudnn_moe_index_type it, int64_t k,
+                                               const rudnn_moe_router_weight_options& o, const float* gw,
+                                               float* w, void* gl, hipStream_t stream) {
+    if (T < 0 || E < 1) return RUDNN_MOE_ERR_SHAPE;
+    if (k < 1 || k > E || k > MAX_TOP_K) return RUDNN_MOE_ERR_ARGUMENT;
+    if ((o.scoring != 0 && o.scoring != 1) || !(o.scale > 0.0) || !std::isfinite(o.scale))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    if (!valid_dtype(ldt) || !valid_index_type(it)) return RUDNN_MOE_ERR_DTYPE;
+    if (E >= INT32_LIMIT || T * E >= ((int64_t)1 << 40) || T * k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (T == 0) return RUDNN_MOE_OK;
+    if (!logits || !idx || (gw ? !gl : !w)) return RUDNN_MOE_ERR_ARGUMENT;
+    const size_t ls = dtype_size(ldt), is = it == RUDNN_MOE_I64 ? 8 : 4, pk = (size_t)(T * k);
+    const Range out = gw ? Range{gl, (size_t)(T * E) * ls} : Range{w, pk * 4};
+    if (any_overlap({out}, {{logits, (size_t)(T * E) * ls}, {idx, pk * is}, {gw, gw ? pk * 4 : 0}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    rudnn_moe_status st;
+    if ((st = check_device(stream, {logits, idx, gw ? (const void*)gl : (const void*)w})) != RUDNN_MOE_OK) return st;
+    if (gw && (st = check_device(stream, {gw})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_selected_router(logits, ldt, T, E, idx, it, k, o.scoring == 1, o.renormalize != 0, o.scale,
+                                          gw, w, gl, stream));
+}
+
+rudnn_moe_status rudnn_moe_selected_router_weights(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E,
+                                                   const void* indices, rudnn_moe_index_type it, int64_t top_k,
+                                                   rudnn_moe_router_weight_options opt, float* weights,
+                                                   hipStream_t stream) {
+    return selected_router_common(logits, ldt, T, E, indices, it, top_k, opt, nullptr, weights, nullptr, stream);
+}
+
+rudnn_moe_status rudnn_moe_selected_router_backward(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E,
+                                                    const void* indices, rudnn_moe_index_type it, int64_t top_k,
+                                                    rudnn_moe_router_weight_options opt, const float* grad_weights,
+                                                    void* grad_logits, hipStream_t stream) {
+    if (!grad_weights && T > 0) return RUDNN_MOE_ERR_ARGUMENT;
+    return selected_router_common(logits, ldt, T, E, indices, it, top_k, opt, grad_weights ? grad_weights : nullptr,
+                                  nullptr, grad_logits, stream);
+}
+
+// Rows of 16-byte vectors (the combine/dispatch backward kernels).
+static rudnn_moe_status check_vector_rows(rudnn_moe_dtype dt, int64_t H, std::initializer_list<const void*> ptrs) {
+    if ((H * (int64_t)dtype_size(dt)) % 16) return RUDNN_MOE_ERR_UNSUPPORTED;
+    for (const void* p : ptrs)
+        if ((uintptr_t)p % 16) return RUDNN_MOE_ERR_UNSUPPORTED;
+    return RUDNN_MOE_OK;
+}
+
+rudnn_moe_status rudnn_moe_combine_backward(const void* y, rudnn_moe_dtype dt, const int32_t* token_map,
+                                            const void* w, rudnn_moe_dtype wdt, const void* dout, int64_t T, int64_t k,
+                                            int64_t H, void* dexp, float* dw, hipStream_t stream) {
+    if (T < 0 || H < 1) return RUDNN_MOE_ERR_SHAPE;
+    if (k < 1) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!valid_dtype(dt) || !valid_dtype(wdt)) return RUDNN_MOE_ERR_DTYPE;
+    if (k > MAX_TOP_K || T * k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (T == 0) return RUDNN_MOE_OK;
+    if (!y || !token_map || !w || !dout || !dexp || !dw) return RUDNN_MOE_ERR_ARGUMENT;
+    rudnn_moe_status st;
+    if ((st = check_vector_rows(dt, H, {y, dout, dexp})) != RUDNN_MOE_OK) return st;
+    const size_t es = dtype_size(dt), pk = (size_t)(T * k);
+    if (any_overlap({{dexp, pk * H * es}, {dw, pk * 4}},
+                    {{y, pk * H * es}, {token_map, pk * 4}, {w, pk * dtype_size(wdt)}, {dout, (size_t)T * H * es}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    if ((st = check_device(stream, {y, token_map, w, dout, dexp, dw})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_combine_backward(y, dt, token_map, w, wdt, dout, T, k, H, T * k, dexp, dw, stream));
+}
+
+rudnn_moe_status rudnn_moe_dispatch_backward(const void* d, rudnn_moe_dtype dt, const int32_t* token_map, int64_t T,
+                                             int64_t k, int64_t H, void* out, hipStream_t stream) {
+    if (T < 0 || H < 1) return RUDNN_MOE_ERR_SHAPE;
+    if (k < 1) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!valid_dtype(dt)) return RUDNN_MOE_ERR_DTYPE;
+    if (k > MAX_TOP_K || T * k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (T == 0) return RUDNN_MOE_OK;
+    if (!d || !token_map || !out) return RUDNN_MOE_ERR_ARGUMENT;
+    rudnn_moe_status st;
+    if ((st = check_vector_rows(dt, H, {d, out})) != RUDNN_MOE_OK) return st;
+    const size_t es = dtype_size(dt), pk = (size_t)(T * k);
+    if (any_overlap({{out, (size_t)T * H * es}}, {{d, pk * H * es}, {token_map, pk * 4}})) return RUDNN_MOE_ERR_ARGUMENT;
+    if ((st = check_device(stream, {d, token_map, out})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_dispatch_backward(d, dt, token_map, T, k, H, T * k, out, stream));
+}
+
 size_t rudnn_moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
     return dispatch_workspace_bytes(T * top_k, E);

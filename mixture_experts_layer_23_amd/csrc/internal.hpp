@@ -68,6 +68,16 @@ hipError_t launch_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E,
                            void* dispatched, int32_t* offsets, int32_t* token_map, int32_t* chunk_counts,
                            hipStream_t s);
 
+// First-order training (train.hip).
+hipError_t launch_selected_router(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E, const void* idx,
+                                  rudnn_moe_index_type it, int64_t k, bool sigmoid, bool renorm, double scale,
+                                  const float* grad_weights, float* weights, void* grad_logits, hipStream_t s);
+hipError_t launch_combine_backward(const void* y, rudnn_moe_dtype dt, const int32_t* map, const void* w,
+                                   rudnn_moe_dtype wdt, const void* dout, int64_t T, int64_t k, int64_t H,
+                                   int64_t rows, void* dexp, float* dw, hipStream_t s);
+hipError_t launch_dispatch_backward(const void* d, rudnn_moe_dtype dt, const int32_t* map, int64_t T, int64_t k,
+                                    int64_t H, int64_t rows, void* out, hipStream_t s);
+
 // n int32 values set to v (a kernel, so that the call stays capturable in a HIP graph).
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 

@@ -28,7 +28,8 @@ STATUS = {0: "ok", 1: "shape", 2: "dtype", 3: "argument", 4: "device", 5: "unsup
 
 KERNELS = ("route", "dispatch_count", "dispatch_scan", "dispatch_rank", "dispatch_copy", "experts_plan",
            "experts_gate_up", "experts_down", "combine", "experts_gate_up_reduce", "experts_down_reduce",
-           "route_sigmoid_grouped", "route_projected", "route_projected_reduce")
+           "route_sigmoid_grouped", "route_projected", "route_projected_reduce", "selected_router", "combine_backward",
+           "dispatch_backward")
 
 
 class MoeError(RuntimeError):
@@ -46,6 +47,13 @@ class GroupRoutingOptions(ctypes.Structure):
     """GroupRoutingOptions of user guide section 10 (group-limited sigmoid routing)."""
     _fields_ = [("top_k", ctypes.c_int64), ("groups", ctypes.c_int64), ("selected_groups", ctypes.c_int64),
                 ("group_top_two", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("scale", ctypes.c_double)]
+
+
+class RouterWeightOptions(ctypes.Structure):
+    """RouterWeightOptions of user guide section 12: scoring 0 = softmax, 1 = sigmoid."""
+    _fields_ = [("scoring", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("scale", ctypes.c_double)]
+
+
 
 
 class ExpertsView(ctypes.Structure):
@@ -90,12 +98,18 @@ def lib() -> ctypes.CDLL:
         L.rudnn_moe_forward_projected_workspace_size.argtypes = [EXP, I64, I64]
         L.rudnn_moe_forward_projected_workspace_size.restype = SZ
         L.rudnn_moe_forward_projected.argtypes = [EXP, P, P, I64, RoutingOptions, P, P, SZ, P]
+        L.rudnn_moe_selected_router_weights.argtypes = [P, I32, I64, I64, P, I32, I64, RouterWeightOptions, P, P]
+        L.rudnn_moe_selected_router_backward.argtypes = [P, I32, I64, I64, P, I32, I64, RouterWeightOptions, P, P, P]
+        L.rudnn_moe_combine_backward.argtypes = [P, I32, P, P, I32, P, I64, I64, I64, P, P, P]
+        L.rudnn_moe_dispatch_backward.argtypes = [P, I32, P, I64, I64, I64, P, P]
         L.rudnn_moe_status_string.argtypes = [I32]
         L.rudnn_moe_status_string.restype = ctypes.c_char_p
         L.rudnn_moe_time_next_launch.argtypes = [I32, P, P]
         for f in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
                   "rudnn_moe_forward", "rudnn_moe_time_next_launch", "rudnn_moe_route_sigmoid_grouped",
-                  "rudnn_moe_forward_sigmoid_grouped", "rudnn_moe_route_projected", "rudnn_moe_forward_projected"):
+                  "rudnn_moe_forward_sigmoid_grouped", "rudnn_moe_route_projected", "rudnn_moe_forward_projected",
+                  "rudnn_moe_selected_router_weights", "rudnn_moe_selected_router_backward",
+                  "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -361,4 +375,82 @@ def forward_projected(experts: SwiGluExperts, input: torch.Tensor, router: torch
     _check("rudnn_moe_forward_projected", lib().rudnn_moe_forward_projected(
         ctypes.byref(experts.view), _ptr(input), _ptr(router), T, RoutingOptions(top_k, int(renormalize)),
         _ptr(out), _ptr(workspace), workspace.numel(), _stream(input)))
+    return out
+
+
+
+# ---------------------------------------------------------------------------------------------
+# First-order training (user guide section 12)
+# ---------------------------------------------------------------------------------------------
+
+def _index_type(indices: torch.Tensor, unsigned: bool) -> int:
+    """0 = U32 (an int32 tensor holding uint32 ids, as ``route`` returns), 1 = I32, 2 = I64."""
+    if indices.dtype == torch.int64:
+        return 2
+    if indices.dtype != torch.int32:
+        raise TypeError("indices must be int32 (holding uint32 or int32 ids) or int64")
+    return 0 if unsigned else 1
+
+
+def _router_opts(scoring: str, renormalize: bool, scale: float) -> RouterWeightOptions:
+    return RouterWeightOptions({"softmax": 0, "sigmoid": 1}[scoring], int(bool(renormalize)), float(scale))
+
+
+def selected_router_weights(logits: torch.Tensor, indices: torch.Tensor, scoring: str = "softmax",
+                            renormalize: bool = False, scale: float = 1.0, unsigned: bool = True) -> torch.Tensor:
+    """FP32 weights [T, k] of the fixed selection ``indices`` (user guide section 12)."""
+    logits, indices = _contig(logits, "logits"), _contig(indices, "indices")
+    T, E = logits.shape
+    k = indices.shape[1]
+    w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _check("rudnn_moe_selected_router_weights", lib().rudnn_moe_selected_router_weights(
+        _ptr(logits), _dt(logits), T, E, _ptr(indices), _index_type(indices, unsigned), k,
+        _router_opts(scoring, renormalize, scale), _ptr(w), _stream(logits)))
+    return w
+
+
+def selected_router_backward(logits: torch.Tensor, indices: torch.Tensor, grad_weights: torch.Tensor,
+                             scoring: str = "softmax", renormalize: bool = False, scale: float = 1.0,
+                             unsigned: bool = True) -> torch.Tensor:
+    """Logits gradient [T, E] (logits dtype) of those weights for FP32 ``grad_weights`` [T, k]."""
+    logits, indices = _contig(logits, "logits"), _contig(indices, "indices")
+    grad_weights = _contig(grad_weights, "grad_weights")
+    if grad_weights.dtype != torch.float32:
+        raise TypeError("grad_weights is FP32")
+    T, E = logits.shape
+    k = indices.shape[1]
+    g = torch.empty_like(logits)
+    _check("rudnn_moe_selected_router_backward", lib().rudnn_moe_selected_router_backward(
+        _ptr(logits), _dt(logits), T, E, _ptr(indices), _index_type(indices, unsigned), k,
+        _router_opts(scoring, renormalize, scale), _ptr(grad_weights), _ptr(g), _stream(logits)))
+    return g
+
+
+def combine_backward(expert_output: torch.Tensor, token_map: torch.Tensor, weights: torch.Tensor,
+                     grad_output: torch.Tensor, grad_expert_output: torch.Tensor | None = None):
+    """Returns ``(grad_expert_output [T*k, H], grad_weights [T, k] FP32)`` (user guide section 12, step 1).
+    Rows of grad_expert_output named by no valid map entry keep their previous contents."""
+    expert_output = _contig(expert_output, "expert_output")
+    grad_output = _contig(grad_output, "grad_output")
+    T, k = token_map.shape
+    H = expert_output.shape[1]
+    if grad_expert_output is None:
+        grad_expert_output = torch.zeros_like(expert_output)
+    gw = torch.empty(T, k, dtype=torch.float32, device=expert_output.device)
+    _check("rudnn_moe_combine_backward", lib().rudnn_moe_combine_backward(
+        _ptr(expert_output), _dt(expert_output), _ptr(_contig(token_map, "token_map")), _ptr(_contig(weights, "weights")),
+        _dt(weights), _ptr(grad_output), T, k, H, _ptr(grad_expert_output), _ptr(gw), _stream(expert_output)))
+    return grad_expert_output, gw
+
+
+def dispatch_backward(grad_dispatched: torch.Tensor, token_map: torch.Tensor, out=None) -> torch.Tensor:
+    """grad_input [T, H]: the selected rows summed back to their token (user guide section 12, step 3)."""
+    grad_dispatched = _contig(grad_dispatched, "grad_dispatched")
+    T, k = token_map.shape
+    H = grad_dispatched.shape[1]
+    if out is None:
+        out = torch.empty(T, H, dtype=grad_dispatched.dtype, device=grad_dispatched.device)
+    _check("rudnn_moe_dispatch_backward", lib().rudnn_moe_dispatch_backward(
+        _ptr(grad_dispatched), _dt(grad_dispatched), _ptr(_contig(token_map, "token_map")), T, k, H, _ptr(out),
+        _stream(grad_dispatched)))
     return out

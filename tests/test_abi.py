@@ -28,12 +28,13 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
     for required in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
                      "rudnn_moe_forward", "rudnn_moe_route_sigmoid_grouped", "rudnn_moe_forward_sigmoid_grouped",
-                     "rudnn_moe_route_projected", "rudnn_moe_forward_projected"):
+                     "rudnn_moe_route_projected", "rudnn_moe_forward_projected", "rudnn_moe_selected_router_weights",
+                     "rudnn_moe_selected_router_backward", "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward"):
         assert required in names
 
 
@@ -154,8 +155,8 @@ def test_forward_validation(L):
 
 
 def test_timing_hook_validation(L):
-    assert L.rudnn_moe_time_next_launch(14, None, None) == ARGUMENT
-    assert L.rudnn_moe_time_next_launch(13, None, None) == OK
+    assert L.rudnn_moe_time_next_launch(17, None, None) == ARGUMENT
+    assert L.rudnn_moe_time_next_launch(16, None, None) == OK
     assert L.rudnn_moe_time_next_launch(-1, None, None) == ARGUMENT
     assert L.rudnn_moe_time_next_launch(0, None, None) == OK
 
@@ -286,3 +287,67 @@ def test_forward_projected_validation(L):
     assert call(wsz=ws - 1) == WORKSPACE
     assert call(out=FAKE + 2**34 + 32) == ARGUMENT       # output overlaps the router
     assert call(T=0) == OK
+
+
+def ropts(scoring=0, renorm=1, scale=1.0):
+    return moe.RouterWeightOptions(scoring, renorm, scale)
+
+
+def test_selected_router_validation(L):
+    fw, fb = L.rudnn_moe_selected_router_weights, L.rudnn_moe_selected_router_backward
+    lg, ix, out, g = FAKE, FAKE + 2**24, FAKE + 2**26, FAKE + 2**28
+
+    def w(T=16, E=8, k=2, dt=2, it=0, o=None, l=lg, i=ix, ww=out):
+        return fw(l, dt, T, E, i, it, k, ropts() if o is None else o, ww, None)
+
+    def b(T=16, E=8, k=2, dt=2, it=0, o=None, gw=g, gl=out):
+        return fb(lg, dt, T, E, ix, it, k, ropts() if o is None else o, gw, gl, None)
+
+    assert w(T=-1) == SHAPE
+    assert w(E=0) == SHAPE
+    assert w(k=0) == ARGUMENT
+    assert w(k=9) == ARGUMENT                       # top_k > E
+    assert w(E=128, k=65) == ARGUMENT               # top_k > 64
+    assert w(o=ropts(scoring=2)) == ARGUMENT
+    assert w(o=ropts(scale=0.0)) == ARGUMENT
+    assert w(o=ropts(scale=float("inf"))) == ARGUMENT
+    assert w(dt=5) == DTYPE
+    assert w(it=3) == DTYPE
+    assert w(l=None) == ARGUMENT
+    assert w(ww=None) == ARGUMENT
+    assert w(ww=lg + 8) == ARGUMENT                  # weights overlap the logits
+    assert w(T=0, l=None, i=None, ww=None) == OK
+    assert b(gw=None) == ARGUMENT
+    assert b(gl=None) == ARGUMENT
+    assert b(gl=g + 4) == ARGUMENT                  # gradient overlaps grad_weights
+    assert b(T=0, gw=None, gl=None) == OK
+
+
+def test_combine_and_dispatch_backward_validation(L):
+    c, d = L.rudnn_moe_combine_backward, L.rudnn_moe_dispatch_backward
+    y, tm, w, go, dexp, dw = FAKE, FAKE + 2**26, FAKE + 2**27, FAKE + 2**28, FAKE + 2**30, FAKE + 2**31
+
+    def cb(T=10, k=2, H=64, dt=2, wdt=2, **kw):
+        a = dict(y=y, tm=tm, w=w, go=go, dexp=dexp, dw=dw)
+        a.update(kw)
+        return c(a["y"], dt, a["tm"], a["w"], wdt, a["go"], T, k, H, a["dexp"], a["dw"], None)
+
+    assert cb(T=-1) == SHAPE
+    assert cb(H=0) == SHAPE
+    assert cb(k=0) == ARGUMENT
+    assert cb(dt=4) == DTYPE
+    assert cb(wdt=4) == DTYPE
+    assert cb(k=65) == UNSUPPORTED
+    assert cb(H=60) == UNSUPPORTED                  # bf16 rows of 120 bytes: not 16-byte vectors
+    assert cb(y=y + 2) == UNSUPPORTED               # unaligned rows
+    assert cb(dw=None) == ARGUMENT
+    assert cb(dexp=y + 64) == ARGUMENT              # dexpert overlaps the expert output
+    assert cb(dw=go + 4) == ARGUMENT                # dweights overlap grad_output
+    assert cb(T=0, y=None, tm=None, w=None, go=None, dexp=None, dw=None) == OK
+    assert d(y, 2, tm, -1, 2, 64, dexp, None) == SHAPE
+    assert d(y, 2, tm, 10, 0, 64, dexp, None) == ARGUMENT
+    assert d(y, 7, tm, 10, 2, 64, dexp, None) == DTYPE
+    assert d(y, 2, tm, 10, 2, 60, dexp, None) == UNSUPPORTED
+    assert d(y, 2, tm, 10, 2, 64, None, None) == ARGUMENT
+    assert d(y, 2, tm, 10, 2, 64, y + 16, None) == ARGUMENT
+    assert d(None, 2, None, 0, 2, 64, None, None) == OK
