@@ -338,6 +338,32 @@ rudnn_moe_status rudnn_moe_dispatch_backward(const void* grad_dispatched, rudnn_
                                              const int32_t* token_map, int64_t T, int64_t top_k, int64_t H,
                                              void* grad_input, hipStream_t stream);
 
+/* Bytes of device workspace rudnn_moe_experts_backward needs for `rows` dispatched rows. */
+size_t rudnn_moe_experts_backward_workspace_size(const rudnn_moe_experts* ex, int64_t rows);
+
+/*
+ * experts_backward -- section 12 step 2 (cache.backward(dexpert) -> dinput for the dispatched
+ * rows and FP32 dgate, dup, ddown), the backward of rudnn_moe_experts_forward.  The "cache" is
+ * the forward's inputs (dispatched rows and offsets): gate . x and up . x are recomputed in
+ * FP32.  For every expert e and row r in [expert_offsets[e], expert_offsets[e+1]):
+ *   dh = down_e^T dy_r (FP32);  dg = dtype(dh * u * silu'(g)),  du = dtype(dh * silu(g))
+ *   grad_dispatched[r] = dtype(gate_e^T dg + up_e^T du)
+ *   grad_gate[e] = sum_r dg_r x_r^T,  grad_up[e] = sum_r du_r x_r^T,
+ *   grad_down[e] = sum_r dy_r h_r^T with h = dtype(silu(g) * u)            (all FP32)
+ *   dispatched, grad_expert_output, grad_dispatched [rows, H] dtype
+ *   grad_gate, grad_up [E, I, H] FP32, grad_down [E, H, I] FP32, every entry written (an
+ *   expert without rows gets zeros); rows of grad_dispatched outside the experts' ranges are
+ *   not written.  BF16/F16 on the matrix cores, F32 on v_mfma_f32_32x32x2f32.
+ * workspace: at least rudnn_moe_experts_backward_workspace_size(ex, rows) bytes, 256-B aligned.
+ * Errors: as rudnn_moe_experts_forward; also UNSUPPORTED when H or I is not a multiple of
+ * 16 / sizeof(dtype) or a pointer is not 16-byte aligned.
+ */
+rudnn_moe_status rudnn_moe_experts_backward(const rudnn_moe_experts* ex, const void* dispatched,
+                                            const int32_t* expert_offsets, int64_t rows,
+                                            const void* grad_expert_output, void* grad_dispatched, float* grad_gate,
+                                            float* grad_up, float* grad_down, void* workspace, size_t workspace_size,
+                                            hipStream_t stream);
+
 /* Static, human-readable name of a status. */
 const char* rudnn_moe_status_string(rudnn_moe_status s);
 
@@ -363,7 +389,12 @@ typedef enum {
     RUDNN_MOE_KERNEL_SELECTED_ROUTER = 14,        /* router weights of a fixed selection, or their gradient */
     RUDNN_MOE_KERNEL_COMBINE_BACKWARD = 15,
     RUDNN_MOE_KERNEL_DISPATCH_BACKWARD = 16,
-    RUDNN_MOE_KERNEL_COUNT = 17
+    RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_PLAN = 17,  /* m-tiles per expert */
+    RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_GU = 18,    /* gate . x and up . x recomputed in FP32 */
+    RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DH = 19,    /* dh = down^T dy with the dg / du / h epilogue */
+    RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DX = 20,    /* grad_dispatched */
+    RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DW = 21,    /* the weight gradients (three launches) */
+    RUDNN_MOE_KERNEL_COUNT = 22
 } rudnn_moe_kernel;
 
 /* For the calling host thread: record `before` on the launch stream immediately before the

@@ -15,7 +15,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librudnn_moe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "route_sigmoid.hip", "route_projected.hip", "dispatch.hip", "experts.hip", "combine.hip", "train.hip", "api.cpp"]
+SOURCES = ["route.hip", "route_sigmoid.hip", "route_projected.hip", "dispatch.hip", "experts.hip", "combine.hip", "train.hip", "experts_backward.hip", "api.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]

@@ -367,6 +367,40 @@ rudnn_moe_status rudnn_moe_experts_forward(const rudnn_moe_experts* ex, const vo
     return runtime(launch_experts(ex, dispatched, offsets, rows, out, workspace, stream));
 }
 
+size_t rudnn_moe_experts_backward_workspace_size(const rudnn_moe_experts* ex, int64_t rows) {
+    if (!ex || rows < 0 || ex->num_experts < 1 || ex->intermediate < 1 || !valid_dtype(ex->dtype)) return 0;
+    return experts_backward_workspace_bytes(ex->num_experts, ex->intermediate, ex->dtype, rows);
+}
+
+rudnn_moe_status rudnn_moe_experts_backward(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets,
+                                            int64_t rows, const void* dy, void* dx, float* dgate, float* dup,
+                                            float* ddown, void* workspace, size_t workspace_size,
+                                            hipStream_t stream) {
+    rudnn_moe_status st = check_experts_view(ex);
+    if (st != RUDNN_MOE_OK) return st;
+    if ((st = check_experts_rows(ex, rows)) != RUDNN_MOE_OK) return st;
+    const int64_t E = ex->num_experts, H = ex->hidden, I = ex->intermediate;
+    const size_t es = dtype_size(ex->dtype);
+    if ((H * (int64_t)es) % 16 || (I * (int64_t)es) % 16) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (!offsets || !dgate || !dup || !ddown) return RUDNN_MOE_ERR_ARGUMENT;
+    if (rows > 0 && (!x || !dy || !dx)) return RUDNN_MOE_ERR_ARGUMENT;
+    for (const void* p : {(const void*)x, dy, (const void*)dx, (const void*)dgate, (const void*)dup,
+                          (const void*)ddown, ex->gate, ex->up, ex->down})
+        if ((uintptr_t)p % 16) return RUDNN_MOE_ERR_UNSUPPORTED;
+    const size_t need = rudnn_moe_experts_backward_workspace_size(ex, rows);
+    if (!workspace || workspace_size < need) return RUDNN_MOE_ERR_WORKSPACE;
+    const size_t wsz = (size_t)(E * H * I) * es, gsz = (size_t)(E * H * I) * 4, xb = (size_t)rows * H * es;
+    if (any_overlap({{dx, xb}, {dgate, gsz}, {dup, gsz}, {ddown, gsz}, {workspace, need}},
+                    {{x, xb}, {dy, xb}, {offsets, 4 * (size_t)(E + 1)}, {ex->gate, wsz}, {ex->up, wsz},
+                     {ex->down, wsz}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    if ((st = check_device(stream, {offsets, dgate, dup, ddown, workspace, ex->gate, ex->up, ex->down})) !=
+        RUDNN_MOE_OK)
+        return st;
+    if (rows > 0 && (st = check_device(stream, {x, dy, dx})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_experts_backward(ex, x, offsets, rows, dy, dx, dgate, dup, ddown, workspace, stream));
+}
+
 rudnn_moe_status rudnn_moe_combine(const void* y, rudnn_moe_dtype dt, const int32_t* token_map, const void* w,
                                    rudnn_moe_dtype wdt, int64_t T, int64_t k, int64_t H, void* out,
                                    hipStream_t stream) {

@@ -89,4 +89,10 @@ size_t experts_workspace_bytes(int64_t E, int64_t H, int64_t I, rudnn_moe_dtype 
 hipError_t launch_experts(const rudnn_moe_experts* ex, const void* dispatched, const int32_t* offsets, int64_t rows,
                           void* out, void* workspace, hipStream_t s);
 
+// Experts backward (experts_backward.hip).
+size_t experts_backward_workspace_bytes(int64_t E, int64_t I, rudnn_moe_dtype dt, int64_t rows);
+hipError_t launch_experts_backward(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int64_t rows,
+                                   const void* dy, void* dx, float* dgate, float* dup, float* ddown, void* workspace,
+                                   hipStream_t s);
+
 }  // namespace rudnn

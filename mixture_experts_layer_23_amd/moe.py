@@ -29,7 +29,8 @@ STATUS = {0: "ok", 1: "shape", 2: "dtype", 3: "argument", 4: "device", 5: "unsup
 KERNELS = ("route", "dispatch_count", "dispatch_scan", "dispatch_rank", "dispatch_copy", "experts_plan",
            "experts_gate_up", "experts_down", "combine", "experts_gate_up_reduce", "experts_down_reduce",
            "route_sigmoid_grouped", "route_projected", "route_projected_reduce", "selected_router", "combine_backward",
-           "dispatch_backward")
+           "dispatch_backward", "experts_backward_plan", "experts_backward_gu", "experts_backward_dh",
+           "experts_backward_dx", "experts_backward_dw")
 
 
 class MoeError(RuntimeError):
@@ -102,6 +103,9 @@ def lib() -> ctypes.CDLL:
         L.rudnn_moe_selected_router_backward.argtypes = [P, I32, I64, I64, P, I32, I64, RouterWeightOptions, P, P, P]
         L.rudnn_moe_combine_backward.argtypes = [P, I32, P, P, I32, P, I64, I64, I64, P, P, P]
         L.rudnn_moe_dispatch_backward.argtypes = [P, I32, P, I64, I64, I64, P, P]
+        L.rudnn_moe_experts_backward_workspace_size.argtypes = [EXP, I64]
+        L.rudnn_moe_experts_backward_workspace_size.restype = SZ
+        L.rudnn_moe_experts_backward.argtypes = [EXP, P, P, I64, P, P, P, P, P, P, SZ, P]
         L.rudnn_moe_status_string.argtypes = [I32]
         L.rudnn_moe_status_string.restype = ctypes.c_char_p
         L.rudnn_moe_time_next_launch.argtypes = [I32, P, P]
@@ -109,7 +113,7 @@ def lib() -> ctypes.CDLL:
                   "rudnn_moe_forward", "rudnn_moe_time_next_launch", "rudnn_moe_route_sigmoid_grouped",
                   "rudnn_moe_forward_sigmoid_grouped", "rudnn_moe_route_projected", "rudnn_moe_forward_projected",
                   "rudnn_moe_selected_router_weights", "rudnn_moe_selected_router_backward",
-                  "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward"):
+                  "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward", "rudnn_moe_experts_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -195,6 +199,11 @@ class SwiGluExperts:
 
     def forward_dispatched(self, d: "Dispatched", out=None, workspace=None) -> torch.Tensor:
         return experts_forward(self, d.dispatched, d.expert_offsets, out=out, workspace=workspace)
+
+    def backward_dispatched(self, d: "Dispatched", grad_expert_output: torch.Tensor, workspace=None):
+        """Backward of forward_dispatched (user guide section 12, step 2): ``(grad_dispatched,
+        dgate, dup, ddown)``, the weight gradients FP32."""
+        return experts_backward(self, d.dispatched, d.expert_offsets, grad_expert_output, workspace=workspace)
 
 
 def route(logits: torch.Tensor, top_k: int, renormalize: bool):
@@ -454,3 +463,29 @@ def dispatch_backward(grad_dispatched: torch.Tensor, token_map: torch.Tensor, ou
         _ptr(grad_dispatched), _dt(grad_dispatched), _ptr(_contig(token_map, "token_map")), T, k, H, _ptr(out),
         _stream(grad_dispatched)))
     return out
+
+
+def experts_backward_workspace_size(experts: SwiGluExperts, rows: int) -> int:
+    return lib().rudnn_moe_experts_backward_workspace_size(ctypes.byref(experts.view), rows)
+
+
+def experts_backward(experts: SwiGluExperts, dispatched: torch.Tensor, expert_offsets: torch.Tensor,
+                     grad_expert_output: torch.Tensor, workspace=None):
+    """Returns ``(grad_dispatched [rows, H] (rows outside the experts' ranges zero), dgate, dup [E, I, H],
+    ddown [E, H, I] FP32)``."""
+    dispatched = _contig(dispatched, "dispatched")
+    grad_expert_output = _contig(grad_expert_output, "grad_expert_output")
+    rows = dispatched.shape[0]
+    dev = dispatched.device
+    E, I, H = experts.E, experts.I, experts.H
+    dx = torch.zeros_like(dispatched)
+    dg = torch.empty(E, I, H, dtype=torch.float32, device=dev)
+    du = torch.empty(E, I, H, dtype=torch.float32, device=dev)
+    dd = torch.empty(E, H, I, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(experts_backward_workspace_size(experts, rows), 1), dtype=torch.uint8, device=dev)
+    _check("rudnn_moe_experts_backward", lib().rudnn_moe_experts_backward(
+        ctypes.byref(experts.view), _ptr(dispatched), _ptr(_contig(expert_offsets, "expert_offsets")), rows,
+        _ptr(grad_expert_output), _ptr(dx), _ptr(dg), _ptr(du), _ptr(dd), _ptr(workspace), workspace.numel(),
+        _stream(dispatched)))
+    return dx, dg, du, dd

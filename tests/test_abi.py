@@ -28,13 +28,14 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
     for required in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
                      "rudnn_moe_forward", "rudnn_moe_route_sigmoid_grouped", "rudnn_moe_forward_sigmoid_grouped",
                      "rudnn_moe_route_projected", "rudnn_moe_forward_projected", "rudnn_moe_selected_router_weights",
-                     "rudnn_moe_selected_router_backward", "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward"):
+                     "rudnn_moe_selected_router_backward", "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward",
+                     "rudnn_moe_experts_backward"):
         assert required in names
 
 
@@ -155,8 +156,8 @@ def test_forward_validation(L):
 
 
 def test_timing_hook_validation(L):
-    assert L.rudnn_moe_time_next_launch(17, None, None) == ARGUMENT
-    assert L.rudnn_moe_time_next_launch(16, None, None) == OK
+    assert L.rudnn_moe_time_next_launch(22, None, None) == ARGUMENT
+    assert L.rudnn_moe_time_next_launch(21, None, None) == OK
     assert L.rudnn_moe_time_next_launch(-1, None, None) == ARGUMENT
     assert L.rudnn_moe_time_next_launch(0, None, None) == OK
 
@@ -351,3 +352,32 @@ def test_combine_and_dispatch_backward_validation(L):
     assert d(y, 2, tm, 10, 2, 64, None, None) == ARGUMENT
     assert d(y, 2, tm, 10, 2, 64, y + 16, None) == ARGUMENT
     assert d(None, 2, None, 0, 2, 64, None, None) == OK
+
+
+def test_experts_backward_validation(L):
+    f = L.rudnn_moe_experts_backward
+    ex = _experts()
+    need = L.rudnn_moe_experts_backward_workspace_size(ctypes.byref(ex), 256)
+    assert need >= 256 * 96 * 4 * 2 and need % 256 == 0
+    x, offs, dy, dx = FAKE + 2**33, FAKE + 2**34, FAKE + 2**35, FAKE + 2**36
+    dg, du, dd, ws = FAKE + 2**37, FAKE + 2**38, FAKE + 2**39, FAKE + 2**40
+
+    def call(exv=ex, rows=256, **kw):
+        a = dict(x=x, offs=offs, dy=dy, dx=dx, dg=dg, du=du, dd=dd, ws=ws, wsz=need)
+        a.update(kw)
+        return f(ctypes.byref(exv), a["x"], a["offs"], rows, a["dy"], a["dx"], a["dg"], a["du"], a["dd"], a["ws"],
+                 a["wsz"], None)
+
+    assert call(exv=_experts(E=0)) == SHAPE
+    assert call(exv=_experts(dt=9)) == DTYPE
+    assert call(rows=-1) == SHAPE
+    assert call(dg=None) == ARGUMENT
+    assert call(offs=None) == ARGUMENT
+    assert call(x=None) == ARGUMENT
+    assert call(exv=_experts(dt=0, H=62)) == UNSUPPORTED        # FP32 rows of 248 bytes
+    assert call(dy=dy + 4) == UNSUPPORTED                       # unaligned
+    assert call(wsz=need - 1) == WORKSPACE
+    assert call(dx=x + 64) == ARGUMENT                          # grad_dispatched overlaps the input rows
+    assert call(dd=FAKE + 2**30 + 64) == ARGUMENT               # a weight gradient overlaps the up weights
+    # no rows: only the (zero) weight gradients are written, the row buffers may be NULL
+    assert L.rudnn_moe_experts_backward_workspace_size(ctypes.byref(ex), 0) > 0
