@@ -97,6 +97,8 @@ def main():
                     help="skip the group-limited sigmoid routing measurements")
     ap.add_argument("--no-projection", action="store_true",
                     help="skip the fused gate projection + routing measurements")
+    ap.add_argument("--no-training", action="store_true",
+                    help="skip the first-order training (backward chain) measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -187,8 +189,8 @@ def main():
 
     # per-kernel breakdown (separate pass, every kernel timed)
     # what the softmax forward with ready logits launches
-    fwd_kernels = [kn for kn in moe.KERNELS if kn not in ("route_sigmoid_grouped", "route_projected",
-                                                          "route_projected_reduce")]
+    fwd_kernels = ["route", "dispatch_count", "dispatch_scan", "dispatch_rank", "dispatch_copy", "experts_plan",
+                   "experts_gate_up", "experts_down", "combine", "experts_gate_up_reduce", "experts_down_reduce"]
     stage_ev = {kn: [(hip.event(), hip.event()) for _ in range(max(3, K // 4))] for kn in fwd_kernels}
     for i in range(max(3, K // 4)):
         for kn in fwd_kernels:
@@ -360,6 +362,12 @@ def main():
         torch.cuda.empty_cache()
         proj = measure_projection(args, moe, hip, stream, flush, dev, ex, w, out_shape=(w.T, w.H))
 
+    # ---------------- first-order training: the backward chain ----------------
+    train = None
+    if not args.no_training:
+        torch.cuda.empty_cache()
+        train = measure_training(moe, hip, stream, flush, dev, ex, w, logits, x)
+
     traffic = traffic_for("experts_gate_up", "mixtral")
     result = {
         "metric": METRIC,
@@ -385,6 +393,7 @@ def main():
         "hbm_stages": hbm,
         "sigmoid_routing": sig,
         "projection": proj,
+        "training": train,
     }
     print(json.dumps(result), flush=True)
 
@@ -481,6 +490,101 @@ def measure_projection(args, moe, hip, stream, flush, dev, ex, wmix, out_shape):
     ms_dec = back_to_back(dec, 50)
     res["decode"] = {"workload": f"T={wd.T} H={wd.H} E={wd.E} k={wd.top_k} bf16 (H split over blocks)",
                      "call_us": ms_dec * 1e3, "router_GBps": wd.E * wd.H * 2 / (ms_dec / 1e3) / 1e9}
+    return res
+
+
+def measure_training(moe, hip, stream, flush, dev, ex, w, logits, x):
+    """The backward chain of section 12 on the Mixtral-shaped layer: combine_backward ->
+    experts_backward (gate/up recomputed in FP32) -> dispatch_backward -> selected_router_backward,
+    timed back to back per step with every kernel's time; and combine/dispatch backward on the
+    routing+dispatch workload with the caches evicted."""
+    import numpy as np
+    import torch
+    from mixture_experts_layer_23_amd.inputs import WORKLOADS, make_logits, make_tokens
+
+    idx, wt = moe.route(logits, w.top_k, True)
+    d = moe.dispatch(idx, x, w.E)
+    y = ex.forward_dispatched(d)
+    g = torch.Generator(device=dev).manual_seed(1)
+    dout = (torch.randn(w.T, w.H, generator=g, device=dev) * 0.05).bfloat16()
+    rows = d.dispatched.shape[0]
+    ws = torch.empty(moe.experts_backward_workspace_size(ex, rows), dtype=torch.uint8, device=dev)
+    dexp = torch.zeros_like(y)
+
+    def chain():
+        _, dw = moe.combine_backward(y, d.token_map, wt, dout, grad_expert_output=dexp)
+        dx, _, _, _ = moe.experts_backward(ex, d.dispatched, d.expert_offsets, dexp, workspace=ws)
+        moe.dispatch_backward(dx, d.token_map)
+        moe.selected_router_backward(logits, idx, dw, "softmax", True, 1.0)
+
+    for _ in range(2):
+        chain()
+    torch.cuda.synchronize()
+    names = ["combine_backward", "experts_backward_gu", "experts_backward_dh", "experts_backward_dx",
+             "experts_backward_dw", "dispatch_backward", "selected_router"]
+    per = {n: [] for n in names}
+    tot = []
+    for _ in range(5):
+        ev = {n: (hip.event(), hip.event()) for n in names}
+        for n in names:
+            moe.time_next_launch(n, *ev[n])
+        a, b = hip.event(), hip.event()
+        hip.record(a, stream)
+        chain()
+        hip.record(b, stream)
+        torch.cuda.synchronize()
+        for n in names:
+            per[n].append(hip.ms(*ev[n]))
+        tot.append(hip.ms(a, b))
+    us = {n: float(np.median(v)) * 1e3 for n, v in per.items()}
+    ms = float(np.median(tot))
+    H, I = w.H, w.I
+    fl = {"experts_backward_gu": 4.0 * rows * H * I, "experts_backward_dh": 2.0 * rows * H * I,
+          "experts_backward_dx": 4.0 * rows * H * I, "experts_backward_dw": 2.0 * rows * H * I}
+    kern = {n: {"us": us[n]} for n in names}
+    for n, f in fl.items():
+        kern[n]["TFLOPps"] = f / (us[n] / 1e6) / 1e12
+        kern[n]["mfma_frac"] = kern[n]["TFLOPps"] / MFMA_PEAK_TFLOPS["bf16"]
+    kern["experts_backward_dw"]["note"] = "the last of three launches (ddown); dgate and dup have the same shape"
+    res = {"mixtral_layer": {
+        "workload": f"T={w.T} H={H} I={I} E={w.E} k={w.top_k} bf16, softmax router renormalised",
+        "backward_chain_ms": ms, "backward_tokens_per_s": w.T / (ms / 1e3),
+        "experts_backward_TFLOPps": 12.0 * rows * H * I / (ms / 1e3) / 1e12,
+        "note": "experts backward algorithmic flops 12 rows H I (plus 4 rows H I of recomputed gate/up)",
+        "kernels": kern}}
+    del d, y, ws, dexp, dout
+    torch.cuda.empty_cache()
+
+    # combine / dispatch backward on the routing+dispatch workload, caches evicted
+    w2 = WORKLOADS["route_dispatch"]
+    lg2 = make_logits(w2)[0].to(dev)
+    x2 = make_tokens(w2, dev)
+    idx2, wt2 = moe.route(lg2, w2.top_k, True)
+    d2 = moe.dispatch(idx2, x2, w2.E)
+    dout2 = torch.randn(w2.T, w2.H, generator=g, device=dev).bfloat16()
+    dexp2 = torch.empty_like(d2.dispatched)
+    din2 = torch.empty_like(x2)
+    reps = 5
+    ev = {n: [(hip.event(), hip.event()) for _ in range(reps)] for n in ("combine_backward", "dispatch_backward")}
+    for i in range(reps + 1):
+        flush()
+        if i:
+            moe.time_next_launch("combine_backward", *ev["combine_backward"][i - 1])
+        moe.combine_backward(d2.dispatched, d2.token_map, wt2, dout2, grad_expert_output=dexp2)
+        flush()
+        if i:
+            moe.time_next_launch("dispatch_backward", *ev["dispatch_backward"][i - 1])
+        moe.dispatch_backward(dexp2, d2.token_map, out=din2)
+    torch.cuda.synchronize()
+    T2, k2, H2 = w2.T, w2.top_k, w2.H
+    nbytes = {"combine_backward": 2 * T2 * k2 * H2 * 2 + T2 * H2 * 2 + T2 * k2 * (4 + 2 + 4),
+              "dispatch_backward": T2 * k2 * H2 * 2 + T2 * H2 * 2 + T2 * k2 * 4}
+    hb = {"workload": "routing+dispatch T=65536 H=2048 k=8 bf16, caches evicted"}
+    for n in nbytes:
+        u = float(np.median([hip.ms(a, b) for a, b in ev[n]])) * 1e3
+        gbs = nbytes[n] / (u / 1e6) / 1e9
+        hb[n] = {"us": u, "bytes": nbytes[n], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    res["hbm_stages"] = hb
     return res
 
 
