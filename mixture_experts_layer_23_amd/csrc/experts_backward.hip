@@ -9,11 +9,12 @@
 // silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z).
 //
 // One MFMA kernel serves all five products: C[m, n] = sum_k A(m, k) B(n, k), 128 x 128 tiles,
-// K staged 64 bytes per row, four wavefronts of 64 x 64 (v_mfma_f32_32x32x16 for BF16/F16,
+// K staged 128 bytes per row, four wavefronts of 64 x 64 (v_mfma_f32_32x32x16 for BF16/F16,
 // 32x32x2f32 for FP32).  An operand is either "K-major" (k contiguous: staged as 16-byte pieces)
-// or "X-major" (its row/column index contiguous: 16-byte pieces of 8 (or 4) consecutive x at
-// one k, scattered into the [x][k] LDS tile by element stores).  The operand tiles go through
-// registers: step k+1 is loaded while step k computes, then written to the other LDS stage.
+// or "X-major" (its row/column index contiguous): a thread then loads a block of CE rows of k by
+// CE consecutive x (CE = elements per 16 bytes), transposes it in registers and stores CE
+// 16-byte pieces of the [x][k] LDS tile.  The operand tiles go through registers: step k+1 is
+// loaded while step k computes, then written to the other LDS stage.
 // Two operand sources may be stacked along the operand's outer index (gate over up).
 // Grouping: ROWS tiles the expert's rows along M (a device-side plan of m-tiles per expert);
 // KROWS uses the expert's rows as the contraction axis, every (expert, m, n) tile (an expert
@@ -28,7 +29,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, ROWB = 64, THREADS = 256;
+constexpr int BM = 128, BN = 128, ROWB = 128, THREADS = 256;
+constexpr int LDS_BYTES = 2 * (BM + BN) * ROWB;  // two stages
 
 template <typename T>
 struct Mma;
@@ -57,8 +59,33 @@ struct Mma<float> {  // four 32x32x2 steps over one 16-byte chunk per lane half 
     }
 };
 
-// 64-byte staged rows: chunk c of row r at slot c ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// 128-byte staged rows: chunk c (16 bytes) of row r at slot c ^ swz(r); the MFMA operand reads
+// (one chunk from each of 32 consecutive rows) then spread over all LDS banks.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// CE x CE block transpose of 16-byte rows (CE elements each): out[x] holds element x of in[0..CE).
+__device__ __forceinline__ void transpose_block(const uint4 (&in)[8], uint4 (&out)[8]) {  // 16-bit elements
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a = reinterpret_cast<const uint32_t*>(&in[2 * j])[x >> 1];
+            const uint32_t b = reinterpret_cast<const uint32_t*>(&in[2 * j + 1])[x >> 1];
+            d[j] = (x & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        }
+        out[x] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+}
+__device__ __forceinline__ void transpose_block(const uint4 (&in)[4], uint4 (&out)[4]) {  // 32-bit elements
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = reinterpret_cast<const uint32_t*>(&in[j])[x];
+        out[x] = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+}
 
 // An operand: element (outer o, inner i) at src(o) + e * estride + o' * ld + i, with src = p0 and
 // o' = o for o < split, else p1 and o' = o - split.  K-major: outer = the operand's row (m or n),
@@ -78,6 +105,20 @@ __device__ __forceinline__ const T* opnd_row(const Opnd& o, int e, int64_t outer
 }
 
 enum { EPI_F32 = 0, EPI_DT = 1, EPI_SWIGLU = 2 };
+
+// Four adjacent outputs rounded to T, one store (8 bytes for 16-bit T, 16 for FP32); p is
+// aligned to four elements (N and the column are multiples of 4).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
+    if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+    } else {
+        T v[4] = {from_f32<T>(a), from_f32<T>(b), from_f32<T>(c), from_f32<T>(d)};
+        uint2 q;
+        __builtin_memcpy(&q, v, 8);
+        *reinterpret_cast<uint2*>(p) = q;
+    }
+}
 enum { ROWS = 0, KROWS = 1 };
 
 struct Plan {
@@ -122,10 +163,14 @@ template <typename T, int MODE, int EPI, bool AK, bool BK>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(Opnd A, Opnd B, int M, int N, int K, int E, Plan plan,
                                                        const int32_t* __restrict__ offsets, int rows, int NT, int MT,
                                                        Epi ep) {
-    constexpr int CE = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+    constexpr int CE = 16 / (int)sizeof(T);     // elements per 16-byte chunk
     constexpr int BKE = ROWB / (int)sizeof(T);  // K elements per step
+    constexpr int NCH = ROWB / 16;              // chunks per staged row
+    constexpr int KQ = BM * NCH / THREADS;      // K-major pieces per thread
+    constexpr int NB = (BKE / CE) * (BM / CE);  // X-major CE x CE blocks per operand tile
+    static_assert(NB == 128 || NB == 256, "at most one X-major block per thread and operand");
     typedef typename Mma<T>::frag frag;
-    __shared__ __align__(16) unsigned char lds[2][(BM + BN) * ROWB];
+    extern __shared__ __align__(1024) unsigned char lds[];
 
     // ---- which tile ----
     int e, m0, n0, mlim, kb, kn;  // expert, tile origin, valid rows, K origin and length
@@ -162,79 +207,83 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Opnd A, Opnd B, int M, in
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // ---- staging: two 16-byte pieces per thread per operand per step ----
-    uint4 ra[2], rb[2];
-    auto load_k = [&](const Opnd& o, bool is_a, int xlim, int k0, uint4 (&r)[2]) __attribute__((always_inline)) {
-        // K-major: piece c -> row x = c / 4, chunk c % 4
+    // The outer index of an operand's tile row x (A: a dispatched row or m, B: n).
+    auto x_outer = [&](bool is_a, int x) -> int64_t {
+        return is_a ? (MODE == ROWS ? row0 + x : (int64_t)(m0 + x)) : (int64_t)(n0 + x);
+    };
+    // K-major staging: piece c -> row x = c / NCH, chunk c % NCH.
+    auto load_k = [&](const Opnd& o, bool is_a, int xlim, int k0, uint4 (&r)[KQ]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = tid + q * THREADS, x = c >> 2, kc = c & 3;
-            const int k = k0 + kc * CE;
+        for (int q = 0; q < KQ; ++q) {
+            const int c = tid + q * THREADS, x = c / NCH, k = k0 + (c % NCH) * CE;
             r[q] = make_uint4(0, 0, 0, 0);
-            if (x < xlim && k < kn) {
-                const int64_t outer = is_a ? (MODE == ROWS ? row0 + x : (int64_t)(m0 + x)) : (int64_t)(n0 + x);
-                const T* p = opnd_row<T>(o, MODE == ROWS && is_a ? 0 : e, outer) + kb + k;
-                r[q] = *reinterpret_cast<const uint4*>(p);
-            }
+            if (x < xlim && k < kn)
+                r[q] = *reinterpret_cast<const uint4*>(
+                    opnd_row<T>(o, MODE == ROWS && is_a ? 0 : e, x_outer(is_a, x)) + kb + k);
         }
     };
-    auto load_x = [&](const Opnd& o, bool is_a, int xlim, int k0, uint4 (&r)[2]) __attribute__((always_inline)) {
-        // X-major: piece c -> k row kk = c / (128 / CE), x chunk c % (128 / CE)
-        constexpr int CPK = 128 / CE;
+    auto store_k = [&](unsigned char* st, const uint4 (&r)[KQ]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = tid + q * THREADS, kk = c / CPK, x = (c % CPK) * CE;
-            const int k = k0 + kk;
-            r[q] = make_uint4(0, 0, 0, 0);
-            if (x < xlim && k < kn) {
-                const int64_t outer = kb + k;
-                const int64_t xo = is_a ? (MODE == ROWS ? row0 + x : (int64_t)(m0 + x)) : (int64_t)(n0 + x);
-                const T* p = opnd_row<T>(o, MODE == KROWS ? 0 : e, outer) + xo;
-                r[q] = *reinterpret_cast<const uint4*>(p);
-            }
-        }
-    };
-    auto store_k = [&](unsigned char* st, const uint4 (&r)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = tid + q * THREADS, x = c >> 2, kc = c & 3;
+        for (int q = 0; q < KQ; ++q) {
+            const int c = tid + q * THREADS, x = c / NCH, kc = c % NCH;
             *reinterpret_cast<uint4*>(st + x * ROWB + ((kc ^ swz(x)) * 16)) = r[q];
         }
     };
-    auto store_x = [&](unsigned char* st, const uint4 (&r)[2]) __attribute__((always_inline)) {
-        constexpr int CPK = 128 / CE;
+    // X-major staging: block b -> k group b / (BM / CE) (CE rows of k), x group b % (BM / CE).
+    // A takes block tid, B block (tid + 128) mod 256: with 128 blocks per operand (16-bit
+    // elements) the two operands occupy different threads; with 256 (FP32) every thread takes
+    // one block of each.
+    auto block_of = [&](bool is_a) { return (tid + (is_a ? 0 : 128)) & (THREADS - 1); };
+    auto load_x = [&](const Opnd& o, bool is_a, int xlim, int k0, uint4 (&r)[CE]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = tid + q * THREADS, kk = c / CPK, x0 = (c % CPK) * CE;
-            const T* v = reinterpret_cast<const T*>(&r[q]);
+        for (int i = 0; i < CE; ++i) r[i] = make_uint4(0, 0, 0, 0);
+        const int bb = block_of(is_a);
+        if (bb >= NB) return;
+        const int kg = bb / (BM / CE), x = (bb % (BM / CE)) * CE;
+        if (x >= xlim) return;
+        const int64_t xo = x_outer(is_a, x);
 #pragma unroll
-            for (int i = 0; i < CE; ++i) {
-                const int x = x0 + i;
-                *reinterpret_cast<T*>(st + x * ROWB + (((kk / CE) ^ swz(x)) * 16) + (kk % CE) * (int)sizeof(T)) = v[i];
-            }
+        for (int i = 0; i < CE; ++i) {
+            const int k = k0 + kg * CE + i;
+            if (k < kn) r[i] = *reinterpret_cast<const uint4*>(opnd_row<T>(o, MODE == KROWS ? 0 : e, kb + k) + xo);
         }
     };
+    auto store_x = [&](unsigned char* st, bool is_a, const uint4 (&r)[CE]) __attribute__((always_inline)) {
+        const int bb = block_of(is_a);
+        if (bb >= NB) return;
+        const int kg = bb / (BM / CE), x0 = (bb % (BM / CE)) * CE;
+        uint4 t[CE];
+        transpose_block(r, t);
+#pragma unroll
+        for (int i = 0; i < CE; ++i) {
+            const int x = x0 + i;
+            *reinterpret_cast<uint4*>(st + x * ROWB + ((kg ^ swz(x)) * 16)) = t[i];
+        }
+    };
+
+    uint4 ka[AK ? KQ : 1], kbr[BK ? KQ : 1];
+    uint4 xa[AK ? 1 : CE], xb[BK ? 1 : CE];
     auto load_step = [&](int kt) __attribute__((always_inline)) {
         const int k0 = kt * BKE;
-        if (AK)
-            load_k(A, true, mlim, k0, ra);
+        if constexpr (AK)
+            load_k(A, true, mlim, k0, ka);
         else
-            load_x(A, true, mlim, k0, ra);
-        if (BK)
-            load_k(B, false, nlim, k0, rb);
+            load_x(A, true, mlim, k0, xa);
+        if constexpr (BK)
+            load_k(B, false, nlim, k0, kbr);
         else
-            load_x(B, false, nlim, k0, rb);
+            load_x(B, false, nlim, k0, xb);
     };
     auto store_step = [&](int kt) __attribute__((always_inline)) {
-        unsigned char* st = lds[kt & 1];
-        if (AK)
-            store_k(st, ra);
+        unsigned char* st = lds + (kt & 1) * (BM + BN) * ROWB;
+        if constexpr (AK)
+            store_k(st, ka);
         else
-            store_x(st, ra);
-        if (BK)
-            store_k(st + BM * ROWB, rb);
+            store_x(st, true, xa);
+        if constexpr (BK)
+            store_k(st + BM * ROWB, kbr);
         else
-            store_x(st + BM * ROWB, rb);
+            store_x(st + BM * ROWB, false, xb);
     };
 
     f32x16 acc[2][2];
@@ -254,11 +303,11 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Opnd A, Opnd B, int M, in
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         if (kt + 1 < KT) load_step(kt + 1);  // into registers, under this step's MFMAs
-        const unsigned char* st = lds[kt & 1];
+        const unsigned char* st = lds + (kt & 1) * (BM + BN) * ROWB;
         const unsigned char* sa = st + (wm * 64 + fr) * ROWB;
         const unsigned char* sb = st + BM * ROWB + (wn * 64 + fr) * ROWB;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < NCH / 2; ++ks) {
             const int off = ((ks * 2 + fh) ^ swz(fr)) * 16;
             frag fa[2], fb[2];
 #pragma unroll
@@ -293,21 +342,26 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Opnd A, Opnd B, int M, in
                     *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.c) + crow * ep.ldc + n) =
                         make_float4(v0, v1, v2, v3);
                 } else if (EPI == EPI_DT) {
-                    T* c = reinterpret_cast<T*>(ep.c) + crow * ep.ldc + n;
-                    c[0] = from_f32<T>(v0), c[1] = from_f32<T>(v1), c[2] = from_f32<T>(v2), c[3] = from_f32<T>(v3);
+                    store4<T>(reinterpret_cast<T*>(ep.c) + crow * ep.ldc + n, v0, v1, v2, v3);
                 } else {  // dh -> dg, du, h; N = I
                     const float dh[4] = {v0, v1, v2, v3};
                     const float* gr = ep.gu + crow * 2 * (int64_t)N + n;
-                    T* dg = reinterpret_cast<T*>(ep.dgu) + crow * 2 * (int64_t)N + n;
-                    T* hh = reinterpret_cast<T*>(ep.h) + crow * (int64_t)N + n;
+                    const float4 g4 = *reinterpret_cast<const float4*>(gr);
+                    const float4 u4 = *reinterpret_cast<const float4*>(gr + N);
+                    const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
+                    float dgv[4], duv[4], hv[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const float g = gr[t], u = gr[N + t];
+                        const float g = gv[t], u = uv[t];
                         const float s = 1.f / (1.f + expf(-g));
-                        dg[t] = from_f32<T>(dh[t] * u * (s * (1.f + g * (1.f - s))));
-                        dg[N + t] = from_f32<T>(dh[t] * (g * s));
-                        hh[t] = from_f32<T>(g * s * u);
+                        dgv[t] = dh[t] * u * (s * (1.f + g * (1.f - s)));
+                        duv[t] = dh[t] * (g * s);
+                        hv[t] = g * s * u;
                     }
+                    T* dg = reinterpret_cast<T*>(ep.dgu) + crow * 2 * (int64_t)N + n;
+                    store4<T>(dg, dgv[0], dgv[1], dgv[2], dgv[3]);
+                    store4<T>(dg + N, duv[0], duv[1], duv[2], duv[3]);
+                    store4<T>(reinterpret_cast<T*>(ep.h) + crow * (int64_t)N + n, hv[0], hv[1], hv[2], hv[3]);
                 }
             }
     }
@@ -331,8 +385,11 @@ void gemm(bwd::Opnd A, bwd::Opnd B, int M, int N, int K, int E, bwd::Plan plan, 
     const int NT = (N + bwd::BN - 1) / bwd::BN, MT = (M + bwd::BM - 1) / bwd::BM;
     const int64_t blocks = MODE == bwd::ROWS ? ((int64_t)rows / bwd::BM + E) * NT : (int64_t)E * MT * NT;
     if (blocks <= 0) return;
+    static const hipError_t attr = hipFuncSetAttribute((const void*)bwd::gemm_kernel<T, MODE, EPI, AK, BK>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, bwd::LDS_BYTES);
+    (void)attr;
     timing_before(kid, s);
-    bwd::gemm_kernel<T, MODE, EPI, AK, BK><<<dim3((unsigned)blocks), dim3(bwd::THREADS), 0, s>>>(
+    bwd::gemm_kernel<T, MODE, EPI, AK, BK><<<dim3((unsigned)blocks), dim3(bwd::THREADS), bwd::LDS_BYTES, s>>>(
         A, B, M, N, K, E, plan, offsets, rows, NT, MT, ep);
     timing_after(kid, s);
 }
