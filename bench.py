@@ -494,9 +494,11 @@ def measure_projection(args, moe, hip, stream, flush, dev, ex, wmix, out_shape):
 
 
 def measure_training(moe, hip, stream, flush, dev, ex, w, logits, x):
-    """The backward chain of section 12 on the Mixtral-shaped layer: combine_backward ->
-    experts_backward (gate/up recomputed in FP32) -> dispatch_backward -> selected_router_backward,
-    timed back to back per step with every kernel's time; and combine/dispatch backward on the
+    """The first-order training step of section 12 on the Mixtral-shaped layer: the experts
+    forward that keeps its FP32 pre-activations as the cache (next to the plain forward), then the
+    backward chain combine_backward -> experts backward from that cache -> dispatch_backward ->
+    selected_router_backward, timed back to back per step with every kernel's time (and the same
+    chain recomputing gate/up instead of reading a cache); combine/dispatch backward on the
     routing+dispatch workload with the caches evicted."""
     import numpy as np
     import torch
@@ -504,55 +506,75 @@ def measure_training(moe, hip, stream, flush, dev, ex, w, logits, x):
 
     idx, wt = moe.route(logits, w.top_k, True)
     d = moe.dispatch(idx, x, w.E)
-    y = ex.forward_dispatched(d)
+    rows = d.dispatched.shape[0]
+    fws = torch.empty(moe.experts_workspace_size(ex, rows), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(d.dispatched)
+    pre = torch.empty(rows, 2 * w.I, dtype=torch.float32, device=dev)
     g = torch.Generator(device=dev).manual_seed(1)
     dout = (torch.randn(w.T, w.H, generator=g, device=dev) * 0.05).bfloat16()
-    rows = d.dispatched.shape[0]
     ws = torch.empty(moe.experts_backward_workspace_size(ex, rows), dtype=torch.uint8, device=dev)
     dexp = torch.zeros_like(y)
 
-    def chain():
+    def timed(fn, names, reps=5):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        per = {n: [] for n in names}
+        tot = []
+        for _ in range(reps):
+            ev = {n: (hip.event(), hip.event()) for n in names}
+            for n in names:
+                moe.time_next_launch(n, *ev[n])
+            a, b = hip.event(), hip.event()
+            hip.record(a, stream)
+            fn()
+            hip.record(b, stream)
+            torch.cuda.synchronize()
+            for n in names:
+                per[n].append(hip.ms(*ev[n]))
+            tot.append(hip.ms(a, b))
+        return {n: float(np.median(v)) * 1e3 for n, v in per.items()}, float(np.median(tot))
+
+    fwd_names = ["experts_plan", "experts_gate_up", "experts_gate_up_reduce", "experts_down", "experts_down_reduce"]
+    us_plain, ms_plain = timed(lambda: moe.experts_forward(ex, d.dispatched, d.expert_offsets, out=y, workspace=fws),
+                               fwd_names)
+    us_train, ms_train = timed(lambda: moe.experts_forward_training(ex, d.dispatched, d.expert_offsets, out=y,
+                                                                    cache=pre, workspace=fws), fwd_names)
+
+    def chain(cache):
         _, dw = moe.combine_backward(y, d.token_map, wt, dout, grad_expert_output=dexp)
-        dx, _, _, _ = moe.experts_backward(ex, d.dispatched, d.expert_offsets, dexp, workspace=ws)
+        dx, _, _, _ = moe.experts_backward(ex, d.dispatched, d.expert_offsets, dexp, cache=cache, workspace=ws)
         moe.dispatch_backward(dx, d.token_map)
         moe.selected_router_backward(logits, idx, dw, "softmax", True, 1.0)
 
-    for _ in range(2):
-        chain()
-    torch.cuda.synchronize()
-    names = ["combine_backward", "experts_backward_gu", "experts_backward_dh", "experts_backward_dx",
-             "experts_backward_dw", "dispatch_backward", "selected_router"]
-    per = {n: [] for n in names}
-    tot = []
-    for _ in range(5):
-        ev = {n: (hip.event(), hip.event()) for n in names}
-        for n in names:
-            moe.time_next_launch(n, *ev[n])
-        a, b = hip.event(), hip.event()
-        hip.record(a, stream)
-        chain()
-        hip.record(b, stream)
-        torch.cuda.synchronize()
-        for n in names:
-            per[n].append(hip.ms(*ev[n]))
-        tot.append(hip.ms(a, b))
-    us = {n: float(np.median(v)) * 1e3 for n, v in per.items()}
-    ms = float(np.median(tot))
+    names = ["combine_backward", "experts_backward_dh", "experts_backward_dx", "experts_backward_dw",
+             "dispatch_backward", "selected_router"]
+    us, ms = timed(lambda: chain(pre), names)
+    us_rc, ms_rc = timed(lambda: chain(None), names + ["experts_backward_gu"])
     H, I = w.H, w.I
-    fl = {"experts_backward_gu": 4.0 * rows * H * I, "experts_backward_dh": 2.0 * rows * H * I,
-          "experts_backward_dx": 4.0 * rows * H * I, "experts_backward_dw": 2.0 * rows * H * I}
+    fl = {"experts_backward_dh": 2.0 * rows * H * I, "experts_backward_dx": 4.0 * rows * H * I,
+          "experts_backward_dw": 2.0 * rows * H * I}
     kern = {n: {"us": us[n]} for n in names}
     for n, f in fl.items():
         kern[n]["TFLOPps"] = f / (us[n] / 1e6) / 1e12
         kern[n]["mfma_frac"] = kern[n]["TFLOPps"] / MFMA_PEAK_TFLOPS["bf16"]
     kern["experts_backward_dw"]["note"] = "the last of three launches (ddown); dgate and dup have the same shape"
+    gu_us = us_rc["experts_backward_gu"]
     res = {"mixtral_layer": {
         "workload": f"T={w.T} H={H} I={I} E={w.E} k={w.top_k} bf16, softmax router renormalised",
+        "experts_forward_ms": ms_plain, "experts_forward_training_ms": ms_train,
+        "gate_up_us": {"forward": us_plain["experts_gate_up"], "forward_training": us_train["experts_gate_up"]},
+        "cache_bytes": rows * 2 * I * 4,
         "backward_chain_ms": ms, "backward_tokens_per_s": w.T / (ms / 1e3),
         "experts_backward_TFLOPps": 12.0 * rows * H * I / (ms / 1e3) / 1e12,
-        "note": "experts backward algorithmic flops 12 rows H I (plus 4 rows H I of recomputed gate/up)",
+        "training_step_ms": ms_train + ms,
+        "backward_chain_recompute_ms": ms_rc,
+        "recomputed_gate_up": {"us": gu_us, "TFLOPps": 4.0 * rows * H * I / (gu_us / 1e6) / 1e12},
+        "note": "backward from the forward's FP32 pre-activation cache; experts backward algorithmic flops "
+                "12 rows H I; training_step_ms = experts forward with cache + backward chain (routing, dispatch "
+                "and combine forward not included)",
         "kernels": kern}}
-    del d, y, ws, dexp, dout
+    del d, y, ws, dexp, dout, pre, fws
     torch.cuda.empty_cache()
 
     # combine / dispatch backward on the routing+dispatch workload, caches evicted

@@ -338,14 +338,34 @@ rudnn_moe_status rudnn_moe_dispatch_backward(const void* grad_dispatched, rudnn_
                                              const int32_t* token_map, int64_t T, int64_t top_k, int64_t H,
                                              void* grad_input, hipStream_t stream);
 
-/* Bytes of device workspace rudnn_moe_experts_backward needs for `rows` dispatched rows. */
-size_t rudnn_moe_experts_backward_workspace_size(const rudnn_moe_experts* ex, int64_t rows);
+/*
+ * experts_forward_training -- section 12 (SwiGluExperts::forward_dispatched_training ->
+ * (output, cache)).  rudnn_moe_experts_forward, and in the same pass the cache the backward
+ * reads instead of recomputing the gate and up products:
+ *   cache[r] = [ gate_e . x_r | up_e . x_r ]   [rows, 2*I] FP32, the FP32 accumulations the
+ *                                              forward's silu(g) * u is formed from
+ * expert_output is bit-identical to rudnn_moe_experts_forward's.  Same workspace.  The cache
+ * belongs to the caller and must stay unchanged until the backward has run (section 12: stored
+ * inputs stay unmodified).
+ * Errors: as rudnn_moe_experts_forward; ARGUMENT for a NULL cache (rows > 0) or one that
+ * overlaps another buffer; UNSUPPORTED for a cache that is not 16-byte aligned.
+ */
+rudnn_moe_status rudnn_moe_experts_forward_training(const rudnn_moe_experts* ex, const void* dispatched,
+                                                    const int32_t* expert_offsets, int64_t rows, void* expert_output,
+                                                    float* cache, void* workspace, size_t workspace_size,
+                                                    hipStream_t stream);
+
+/* Bytes of device workspace rudnn_moe_experts_backward needs for `rows` dispatched rows; with
+ * cached != 0 (a cache from rudnn_moe_experts_forward_training is passed) it leaves out the
+ * recomputed [rows, 2*I] FP32 pre-activations. */
+size_t rudnn_moe_experts_backward_workspace_size(const rudnn_moe_experts* ex, int64_t rows, int cached);
 
 /*
  * experts_backward -- section 12 step 2 (cache.backward(dexpert) -> dinput for the dispatched
- * rows and FP32 dgate, dup, ddown), the backward of rudnn_moe_experts_forward.  The "cache" is
- * the forward's inputs (dispatched rows and offsets): gate . x and up . x are recomputed in
- * FP32.  For every expert e and row r in [expert_offsets[e], expert_offsets[e+1]):
+ * rows and FP32 dgate, dup, ddown), the backward of rudnn_moe_experts_forward.  cache: the
+ * [rows, 2*I] FP32 pre-activations [g | u] written by rudnn_moe_experts_forward_training for
+ * the same dispatched rows and offsets, or NULL, and then g = gate . x and u = up . x are
+ * recomputed in FP32.  For every expert e and row r in [expert_offsets[e], expert_offsets[e+1]):
  *   dh = down_e^T dy_r (FP32);  dg = dtype(dh * u * silu'(g)),  du = dtype(dh * silu(g))
  *   grad_dispatched[r] = dtype(gate_e^T dg + up_e^T du)
  *   grad_gate[e] = sum_r dg_r x_r^T,  grad_up[e] = sum_r du_r x_r^T,
@@ -354,12 +374,13 @@ size_t rudnn_moe_experts_backward_workspace_size(const rudnn_moe_experts* ex, in
  *   grad_gate, grad_up [E, I, H] FP32, grad_down [E, H, I] FP32, every entry written (an
  *   expert without rows gets zeros); rows of grad_dispatched outside the experts' ranges are
  *   not written.  BF16/F16 on the matrix cores, F32 on v_mfma_f32_32x32x2f32.
- * workspace: at least rudnn_moe_experts_backward_workspace_size(ex, rows) bytes, 256-B aligned.
+ * workspace: at least rudnn_moe_experts_backward_workspace_size(ex, rows, cache != NULL) bytes,
+ * 256-B aligned.
  * Errors: as rudnn_moe_experts_forward; also UNSUPPORTED when H or I is not a multiple of
  * 16 / sizeof(dtype) or a pointer is not 16-byte aligned.
  */
 rudnn_moe_status rudnn_moe_experts_backward(const rudnn_moe_experts* ex, const void* dispatched,
-                                            const int32_t* expert_offsets, int64_t rows,
+                                            const int32_t* expert_offsets, int64_t rows, const float* cache,
                                             const void* grad_expert_output, void* grad_dispatched, float* grad_gate,
                                             float* grad_up, float* grad_down, void* workspace, size_t workspace_size,
                                             hipStream_t stream);

@@ -343,38 +343,57 @@ size_t rudnn_moe_experts_workspace_size(const rudnn_moe_experts* ex, int64_t row
     return experts_workspace_bytes(ex->num_experts, ex->hidden, ex->intermediate, ex->dtype, rows);
 }
 
-rudnn_moe_status rudnn_moe_experts_forward(const rudnn_moe_experts* ex, const void* dispatched, const int32_t* offsets,
-                                           int64_t rows, void* out, void* workspace, size_t workspace_size,
-                                           hipStream_t stream) {
+namespace {
+// experts_forward and its training variant (cache != NULL: [rows, 2I] FP32 pre-activations).
+rudnn_moe_status experts_forward_common(const rudnn_moe_experts* ex, const void* dispatched, const int32_t* offsets,
+                                        int64_t rows, void* out, float* cache, bool training, void* workspace,
+                                        size_t workspace_size, hipStream_t stream) {
     rudnn_moe_status st = check_experts_view(ex);
     if (st != RUDNN_MOE_OK) return st;
     if ((st = check_experts_rows(ex, rows)) != RUDNN_MOE_OK) return st;
     if (rows == 0) return RUDNN_MOE_OK;
-    if (!dispatched || !offsets || !out) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!dispatched || !offsets || !out || (training && !cache)) return RUDNN_MOE_ERR_ARGUMENT;
     if (ex->dtype != RUDNN_MOE_F32 && ((uintptr_t)dispatched % 16 || (uintptr_t)out % 16))
         return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (training && (uintptr_t)cache % 16) return RUDNN_MOE_ERR_UNSUPPORTED;
     const size_t need = rudnn_moe_experts_workspace_size(ex, rows);
     if (!workspace || workspace_size < need) return RUDNN_MOE_ERR_WORKSPACE;
     const size_t es = dtype_size(ex->dtype);
     const size_t wsz = (size_t)(ex->num_experts * ex->hidden * ex->intermediate) * es;
     const size_t xb = (size_t)rows * ex->hidden * es;
-    if (any_overlap({{out, xb}, {workspace, need}},
+    const size_t cb = training ? (size_t)rows * 2 * ex->intermediate * 4 : 0;
+    if (any_overlap({{out, xb}, {workspace, need}, {cache, cb}},
                     {{dispatched, xb}, {offsets, 4 * (size_t)(ex->num_experts + 1)}, {ex->gate, wsz}, {ex->up, wsz},
                      {ex->down, wsz}}))
         return RUDNN_MOE_ERR_ARGUMENT;
     if ((st = check_device(stream, {dispatched, offsets, out, workspace, ex->gate, ex->up, ex->down})) != RUDNN_MOE_OK)
         return st;
-    return runtime(launch_experts(ex, dispatched, offsets, rows, out, workspace, stream));
+    if (training && (st = check_device(stream, {cache})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_experts(ex, dispatched, offsets, rows, out, workspace, stream, training ? cache : nullptr));
+}
+}  // namespace
+
+rudnn_moe_status rudnn_moe_experts_forward(const rudnn_moe_experts* ex, const void* dispatched, const int32_t* offsets,
+                                           int64_t rows, void* out, void* workspace, size_t workspace_size,
+                                           hipStream_t stream) {
+    return experts_forward_common(ex, dispatched, offsets, rows, out, nullptr, false, workspace, workspace_size,
+                                  stream);
 }
 
-size_t rudnn_moe_experts_backward_workspace_size(const rudnn_moe_experts* ex, int64_t rows) {
+rudnn_moe_status rudnn_moe_experts_forward_training(const rudnn_moe_experts* ex, const void* dispatched,
+                                                    const int32_t* offsets, int64_t rows, void* out, float* cache,
+                                                    void* workspace, size_t workspace_size, hipStream_t stream) {
+    return experts_forward_common(ex, dispatched, offsets, rows, out, cache, true, workspace, workspace_size, stream);
+}
+
+size_t rudnn_moe_experts_backward_workspace_size(const rudnn_moe_experts* ex, int64_t rows, int cached) {
     if (!ex || rows < 0 || ex->num_experts < 1 || ex->intermediate < 1 || !valid_dtype(ex->dtype)) return 0;
-    return experts_backward_workspace_bytes(ex->num_experts, ex->intermediate, ex->dtype, rows);
+    return experts_backward_workspace_bytes(ex->num_experts, ex->intermediate, ex->dtype, rows, cached != 0);
 }
 
 rudnn_moe_status rudnn_moe_experts_backward(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets,
-                                            int64_t rows, const void* dy, void* dx, float* dgate, float* dup,
-                                            float* ddown, void* workspace, size_t workspace_size,
+                                            int64_t rows, const float* cache, const void* dy, void* dx, float* dgate,
+                                            float* dup, float* ddown, void* workspace, size_t workspace_size,
                                             hipStream_t stream) {
     rudnn_moe_status st = check_experts_view(ex);
     if (st != RUDNN_MOE_OK) return st;
@@ -385,20 +404,23 @@ rudnn_moe_status rudnn_moe_experts_backward(const rudnn_moe_experts* ex, const v
     if (!offsets || !dgate || !dup || !ddown) return RUDNN_MOE_ERR_ARGUMENT;
     if (rows > 0 && (!x || !dy || !dx)) return RUDNN_MOE_ERR_ARGUMENT;
     for (const void* p : {(const void*)x, dy, (const void*)dx, (const void*)dgate, (const void*)dup,
-                          (const void*)ddown, ex->gate, ex->up, ex->down})
+                          (const void*)ddown, (const void*)cache, ex->gate, ex->up, ex->down})
         if ((uintptr_t)p % 16) return RUDNN_MOE_ERR_UNSUPPORTED;
-    const size_t need = rudnn_moe_experts_backward_workspace_size(ex, rows);
+    const size_t need = rudnn_moe_experts_backward_workspace_size(ex, rows, cache != nullptr);
     if (!workspace || workspace_size < need) return RUDNN_MOE_ERR_WORKSPACE;
     const size_t wsz = (size_t)(E * H * I) * es, gsz = (size_t)(E * H * I) * 4, xb = (size_t)rows * H * es;
+    const size_t cb = cache ? (size_t)rows * 2 * I * 4 : 0;
     if (any_overlap({{dx, xb}, {dgate, gsz}, {dup, gsz}, {ddown, gsz}, {workspace, need}},
-                    {{x, xb}, {dy, xb}, {offsets, 4 * (size_t)(E + 1)}, {ex->gate, wsz}, {ex->up, wsz},
-                     {ex->down, wsz}}))
+                    {{x, xb}, {dy, xb}, {offsets, 4 * (size_t)(E + 1)}, {cache, cb}, {ex->gate, wsz},
+                     {ex->up, wsz}, {ex->down, wsz}}))
         return RUDNN_MOE_ERR_ARGUMENT;
     if ((st = check_device(stream, {offsets, dgate, dup, ddown, workspace, ex->gate, ex->up, ex->down})) !=
         RUDNN_MOE_OK)
         return st;
     if (rows > 0 && (st = check_device(stream, {x, dy, dx})) != RUDNN_MOE_OK) return st;
-    return runtime(launch_experts_backward(ex, x, offsets, rows, dy, dx, dgate, dup, ddown, workspace, stream));
+    if (rows > 0 && cache && (st = check_device(stream, {cache})) != RUDNN_MOE_OK) return st;
+    return runtime(
+        launch_experts_backward(ex, x, offsets, rows, cache, dy, dx, dgate, dup, ddown, workspace, stream));
 }
 
 rudnn_moe_status rudnn_moe_combine(const void* y, rudnn_moe_dtype dt, const int32_t* token_map, const void* w,

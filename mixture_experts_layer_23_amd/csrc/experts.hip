@@ -16,6 +16,9 @@
 // keeps the MFMA operand reads free of bank conflicts.  Two LDS stages: the copies of step k+1
 // are issued under the MFMAs of step k; one barrier per step.
 // F32: a plain FP32 FMA tile (64 x 64) on the same tile plan -- no reduced-precision step.
+// Training (section 12, forward_dispatched_training): the gate_up epilogue also stores the FP32
+// pre-activations [g | u] of every row as the backward's cache (a kernel variant of its own, so
+// the plain forward is unchanged).
 //
 // Tile order.  Tiles of expert e are enumerated in groups of GROUP_N n-tiles, all m-tiles of a
 // group together, so tiles that run side by side share both their weight columns and their
@@ -284,14 +287,16 @@ __device__ __forceinline__ void stage_slot(int slot, unsigned char* st, const St
 }
 
 // Grouped GEMM on MFMA: for the tile's expert e, C[r, n] = sum_k A[r, k] B_e[n, k] over the
-// tile's rows; DUAL computes gate and up together and stores silu(gate) * up.
-template <typename T, bool DUAL, typename Cfg>
+// tile's rows; DUAL computes gate and up together and stores silu(gate) * up.  CACHE (with DUAL)
+// also stores the FP32 pre-activations, cache[r] = [gate . x_r | up . x_r] ([rows, 2N]).
+template <typename T, bool DUAL, typename Cfg, bool CACHE = false>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(const T* __restrict__ A,
                                                                             const T* __restrict__ B0,
                                                                             const T* __restrict__ B1,
                                                                             T* __restrict__ C, int K, int N, int E,
                                                                             Plan plan, int cus,
-                                                                            float* __restrict__ partials) {
+                                                                            float* __restrict__ partials,
+                                                                            float* __restrict__ cache) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, STAGES = Cfg::STAGES;
     constexpr int BK = Cfg::BK, ROWB = Cfg::ROWB, CPR = Cfg::CPR;
     constexpr int NWAVES = WM * WN;
@@ -471,6 +476,27 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
         }
         return;
     }
+    if constexpr (DUAL && CACHE) {
+        // each lane's runs of four adjacent columns, straight from the accumulators
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * WTM + i * 32 + fr;
+            if (row >= nrows) continue;
+            float* crow = cache + (int64_t)(tile.row0 + row) * 2 * N + n0;
+#pragma unroll
+            for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = wn * WTN + j * 32 + 8 * q + 4 * fh;
+                        if (n0 + col >= N) continue;
+                        *reinterpret_cast<float4*>(crow + s * N + col) =
+                            make_float4(acc[s][i][j][4 * q], acc[s][i][j][4 * q + 1], acc[s][i][j][4 * q + 2],
+                                        acc[s][i][j][4 * q + 3]);
+                    }
+        }
+    }
     constexpr int PITCH = BN * (int)sizeof(T) + 16;  // bytes per staged output row
     constexpr int CHUNKS = BN * (int)sizeof(T) / 16;  // 16-byte pieces per row
     constexpr int LDS_MAX = 160 * 1024;
@@ -520,9 +546,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
 // Adds the S partials of every split tile in segment order and applies the epilogue (silu(g) * u
 // for gate_up).  A block takes a slab of 2048 / BN rows of one split tile (the tile is decoded
 // once per slab); a thread takes 8 output columns of one row.
-template <typename T, bool DUAL, typename Cfg>
+template <typename T, bool DUAL, typename Cfg, bool CACHE = false>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ partials, T* __restrict__ C, int K,
-                                                     int N, int E, Plan plan, int cus) {
+                                                     int N, int E, Plan plan, int cus, float* __restrict__ cache) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, NSETS = DUAL ? 2 : 1, NB = NSETS * BN;
     constexpr int CPRW = BN / 8, SLAB = 256 / CPRW;  // 8-column chunks per row, rows per slab
     constexpr int SLABS = (BM + SLAB - 1) / SLAB;     // slabs per tile
@@ -551,6 +577,13 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
             add(P + seg * seg_stride, g);
             if (DUAL) add(P + seg * seg_stride + BN, u);
         }
+        if constexpr (DUAL && CACHE) {
+            float* c = cache + (int64_t)(t.row0 + row) * 2 * N + t.n0 + col;
+            *reinterpret_cast<float4*>(c) = make_float4(g[0], g[1], g[2], g[3]);
+            *reinterpret_cast<float4*>(c + 4) = make_float4(g[4], g[5], g[6], g[7]);
+            *reinterpret_cast<float4*>(c + N) = make_float4(u[0], u[1], u[2], u[3]);
+            *reinterpret_cast<float4*>(c + N + 4) = make_float4(u[4], u[5], u[6], u[7]);
+        }
         T out[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) out[q] = from_f32<T>(DUAL ? silu_f(g[q]) * u[q] : g[q]);
@@ -568,7 +601,7 @@ constexpr int F_BM = 64, F_BN = 64, F_BK = 16;
 template <bool DUAL>
 __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict__ A, const float* __restrict__ B0,
                                                         const float* __restrict__ B1, float* __restrict__ C, int K,
-                                                        int N, int E, Plan plan) {
+                                                        int N, int E, Plan plan, float* __restrict__ cache) {
     __shared__ int s_mt[MAX_EXPERTS + 1];
     __shared__ float sA[F_BK][F_BM + 4];
     __shared__ float sB[DUAL ? 2 : 1][F_BK][F_BN + 4];
@@ -621,6 +654,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
             const int col = tx * 4 + j;
             if (tile.n0 + col >= N) continue;
             float v = acc[0][i][j];
+            if (DUAL && cache) {
+                float* c = cache + (int64_t)(tile.row0 + row) * 2 * N + tile.n0 + col;
+                c[0] = v, c[N] = acc[1][i][j];
+            }
             if (DUAL) v = (v / (1.0f + expf(-v))) * acc[1][i][j];
             Cb[(int64_t)row * N + col] = v;
         }
@@ -667,9 +704,9 @@ static size_t mfma_smem_bytes(int64_t E) {
     return bytes > out_tile ? bytes : out_tile;
 }
 
-template <typename T>
+template <typename T, bool CACHE>
 static void launch_mfma(const rudnn_moe_experts* ex, const void* disp, int64_t rows, void* out, void* h, Plan plan,
-                        float* partials, hipStream_t s) {
+                        float* partials, float* cache, hipStream_t s) {
     const int E = (int)ex->num_experts, H = (int)ex->hidden, I = (int)ex->intermediate;
     const int64_t mt = max_mtiles(rows, E, GateUpCfg::BM);
     const int cus = device_cus();
@@ -679,35 +716,35 @@ static void launch_mfma(const rudnn_moe_experts* ex, const void* disp, int64_t r
         return (unsigned)((units + 7) / 8 * 8);
     };
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
-    grouped_gemm_mfma<T, true, GateUpCfg><<<grid_for(I, GateUpCfg::BN), GateUpCfg::THREADS,
-                                            mfma_smem_bytes<GateUpCfg, true>(E), s>>>(
-        (const T*)disp, (const T*)ex->gate, (const T*)ex->up, (T*)h, H, I, E, plan, cus, partials);
+    grouped_gemm_mfma<T, true, GateUpCfg, CACHE><<<grid_for(I, GateUpCfg::BN), GateUpCfg::THREADS,
+                                                   mfma_smem_bytes<GateUpCfg, true>(E), s>>>(
+        (const T*)disp, (const T*)ex->gate, (const T*)ex->up, (T*)h, H, I, E, plan, cus, partials, cache);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE, s);
-    splitk_reduce<T, true, GateUpCfg><<<1024, 256, 0, s>>>(partials, (T*)h, H, I, E, plan, cus);
+    splitk_reduce<T, true, GateUpCfg, CACHE><<<1024, 256, 0, s>>>(partials, (T*)h, H, I, E, plan, cus, cache);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
     grouped_gemm_mfma<T, false, DownCfg><<<grid_for(H, DownCfg::BN), DownCfg::THREADS,
                                            mfma_smem_bytes<DownCfg, false>(E), s>>>(
-        (const T*)h, (const T*)ex->down, nullptr, (T*)out, I, H, E, plan, cus, partials);
+        (const T*)h, (const T*)ex->down, nullptr, (T*)out, I, H, E, plan, cus, partials, nullptr);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_DOWN_REDUCE, s);
-    splitk_reduce<T, false, DownCfg><<<1024, 256, 0, s>>>(partials, (T*)out, I, H, E, plan, cus);
+    splitk_reduce<T, false, DownCfg><<<1024, 256, 0, s>>>(partials, (T*)out, I, H, E, plan, cus, nullptr);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_DOWN_REDUCE, s);
 }
 
 static void launch_f32(const rudnn_moe_experts* ex, const void* disp, int64_t rows, void* out, void* h, Plan plan,
-                       hipStream_t s) {
+                       float* cache, hipStream_t s) {
     const int E = (int)ex->num_experts, H = (int)ex->hidden, I = (int)ex->intermediate;
     const int64_t mt = max_mtiles(rows, E, F_BM);
     auto grid_for = [&](int N) { return (unsigned)((mt * ((N + F_BN - 1) / F_BN) + 7) / 8 * 8); };
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
     grouped_gemm_f32<true><<<grid_for(I), 256, 0, s>>>((const float*)disp, (const float*)ex->gate,
-                                                       (const float*)ex->up, (float*)h, H, I, E, plan);
+                                                       (const float*)ex->up, (float*)h, H, I, E, plan, cache);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
     grouped_gemm_f32<false><<<grid_for(H), 256, 0, s>>>((const float*)h, (const float*)ex->down, nullptr,
-                                                        (float*)out, I, H, E, plan);
+                                                        (float*)out, I, H, E, plan, nullptr);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
 }
 
@@ -724,10 +761,14 @@ static void allow_large_lds() {
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<f16, false, DownCfg>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<bf16, true, GateUpCfg, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<f16, true, GateUpCfg, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
 
 hipError_t launch_experts(const rudnn_moe_experts* ex, const void* disp, const int32_t* offsets, int64_t rows,
-                          void* out, void* workspace, hipStream_t s) {
+                          void* out, void* workspace, hipStream_t s, float* cache) {
     const int64_t E = ex->num_experts, I = ex->intermediate;
     const size_t es = dtype_size(ex->dtype);
     unsigned char* ws = (unsigned char*)workspace;
@@ -742,9 +783,19 @@ hipError_t launch_experts(const rudnn_moe_experts* ex, const void* disp, const i
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_PLAN, s);
     float* partials = (float*)(ws + align_up((size_t)rows * I * es) + align_up(sizeof(int32_t) * (3 * E + 1)));
     switch (ex->dtype) {
-    case RUDNN_MOE_F32: launch_f32(ex, disp, rows, out, h, plan, s); break;
-    case RUDNN_MOE_F16: launch_mfma<f16>(ex, disp, rows, out, h, plan, partials, s); break;
-    default: launch_mfma<bf16>(ex, disp, rows, out, h, plan, partials, s); break;
+    case RUDNN_MOE_F32: launch_f32(ex, disp, rows, out, h, plan, cache, s); break;
+    case RUDNN_MOE_F16:
+        if (cache)
+            launch_mfma<f16, true>(ex, disp, rows, out, h, plan, partials, cache, s);
+        else
+            launch_mfma<f16, false>(ex, disp, rows, out, h, plan, partials, nullptr, s);
+        break;
+    default:
+        if (cache)
+            launch_mfma<bf16, true>(ex, disp, rows, out, h, plan, partials, cache, s);
+        else
+            launch_mfma<bf16, false>(ex, disp, rows, out, h, plan, partials, nullptr, s);
+        break;
     }
     return hipGetLastError();
 }

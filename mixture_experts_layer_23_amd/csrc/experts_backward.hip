@@ -1,7 +1,7 @@
 // experts_backward.hip -- backward of the bias-free SwiGLU experts on the dispatched rows (ruDNN
 // user guide, section 12 step 2: cache.backward(dexpert) -> dinput for the dispatched rows and
 // FP32 dgate, dup, ddown).  For the rows r of expert e (x = dispatched, dy = dexpert):
-//   [g | u] = x [gate_e; up_e]^T          FP32, recomputed (the forward's inputs are the cache)
+//   [g | u] = x [gate_e; up_e]^T          FP32: the training forward's cache, or recomputed
 //   dh      = dy down_e                    FP32, fused epilogue:
 //             dg = dtype(dh u silu'(g)), du = dtype(dh silu(g)), h = dtype(silu(g) u)
 //   dx      = [dg | du] [gate_e; up_e]     -> grad_dispatched (dtype)
@@ -371,10 +371,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Opnd A, Opnd B, int M, in
 
 // ---- host side ----
 
-size_t experts_backward_workspace_bytes(int64_t E, int64_t I, rudnn_moe_dtype dt, int64_t rows) {
+// Workspace: [dg | du] [rows, 2I] dtype, h [rows, I] dtype, the plan (3E + 1 ints), then (without
+// a cache) the recomputed pre-activations [g | u] [rows, 2I] FP32.
+size_t experts_backward_workspace_bytes(int64_t E, int64_t I, rudnn_moe_dtype dt, int64_t rows, bool cached) {
     const size_t es = dtype_size(dt);
-    return align_up((size_t)rows * 2 * I * 4) + align_up((size_t)rows * 2 * I * es) + align_up((size_t)rows * I * es) +
-           align_up(sizeof(int32_t) * (size_t)(3 * E + 1));
+    return align_up((size_t)rows * 2 * I * es) + align_up((size_t)rows * I * es) +
+           align_up(sizeof(int32_t) * (size_t)(3 * E + 1)) + (cached ? 0 : align_up((size_t)rows * 2 * I * 4));
 }
 
 namespace {
@@ -395,25 +397,28 @@ void gemm(bwd::Opnd A, bwd::Opnd B, int M, int N, int K, int E, bwd::Plan plan, 
 }
 
 template <typename T>
-void run(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int64_t rows, const void* dy, void* dx,
-         float* dgate, float* dup, float* ddown, void* workspace, hipStream_t s) {
+void run(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int64_t rows, const float* cache,
+         const void* dy, void* dx, float* dgate, float* dup, float* ddown, void* workspace, hipStream_t s) {
     const int E = (int)ex->num_experts, H = (int)ex->hidden, I = (int)ex->intermediate, R = (int)rows;
     const size_t es = sizeof(T);
     unsigned char* ws = (unsigned char*)workspace;
-    float* gu = (float*)ws;
-    T* dgu = (T*)(ws + align_up((size_t)rows * 2 * I * 4));
-    T* hbuf = (T*)((unsigned char*)dgu + align_up((size_t)rows * 2 * I * es));
+    T* dgu = (T*)ws;
+    T* hbuf = (T*)(ws + align_up((size_t)rows * 2 * I * es));
     int32_t* pl = (int32_t*)((unsigned char*)hbuf + align_up((size_t)rows * I * es));
+    float* gu = cache ? const_cast<float*>(cache)
+                      : (float*)((unsigned char*)pl + align_up(sizeof(int32_t) * (size_t)(3 * E + 1)));
     bwd::Plan plan{pl, pl + E, pl + 2 * E};
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_PLAN, s);
     bwd::plan_kernel<<<1, 1024, 0, s>>>(offsets, E, R, pl, pl + E, pl + 2 * E);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_PLAN, s);
     const int NOSPLIT = 0x7fffffff;
     const int64_t IH = (int64_t)I * H;
-    // [g | u] = x [gate; up]^T  (B K-major, gate rows then up rows)
-    gemm<T, bwd::ROWS, bwd::EPI_F32, true, true>({x, x, H, 0, NOSPLIT}, {ex->gate, ex->up, H, IH, I}, R, 2 * I, H, E,
-                                                 plan, offsets, R, {gu, 2 * (int64_t)I, nullptr, nullptr, nullptr},
-                                                 RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_GU, s);
+    // [g | u] = x [gate; up]^T  (B K-major, gate rows then up rows), unless the forward cached it
+    if (!cache)
+        gemm<T, bwd::ROWS, bwd::EPI_F32, true, true>({x, x, H, 0, NOSPLIT}, {ex->gate, ex->up, H, IH, I}, R, 2 * I, H,
+                                                     E, plan, offsets, R,
+                                                     {gu, 2 * (int64_t)I, nullptr, nullptr, nullptr},
+                                                     RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_GU, s);
     // dh = dy down_e (B(n = i, k = c) = down[e, c, i]: X-major), epilogue -> dg | du, h
     gemm<T, bwd::ROWS, bwd::EPI_SWIGLU, true, false>({dy, dy, H, 0, NOSPLIT}, {ex->down, ex->down, I, IH, NOSPLIT}, R, I,
                                                      H, E, plan, offsets, R, {nullptr, 0, gu, dgu, hbuf},
@@ -439,12 +444,12 @@ void run(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int
 }  // namespace
 
 hipError_t launch_experts_backward(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int64_t rows,
-                                   const void* dy, void* dx, float* dgate, float* dup, float* ddown, void* workspace,
-                                   hipStream_t s) {
+                                   const float* cache, const void* dy, void* dx, float* dgate, float* dup,
+                                   float* ddown, void* workspace, hipStream_t s) {
     switch (ex->dtype) {
-    case RUDNN_MOE_F32: run<float>(ex, x, offsets, rows, dy, dx, dgate, dup, ddown, workspace, s); break;
-    case RUDNN_MOE_F16: run<f16>(ex, x, offsets, rows, dy, dx, dgate, dup, ddown, workspace, s); break;
-    default: run<bf16>(ex, x, offsets, rows, dy, dx, dgate, dup, ddown, workspace, s); break;
+    case RUDNN_MOE_F32: run<float>(ex, x, offsets, rows, cache, dy, dx, dgate, dup, ddown, workspace, s); break;
+    case RUDNN_MOE_F16: run<f16>(ex, x, offsets, rows, cache, dy, dx, dgate, dup, ddown, workspace, s); break;
+    default: run<bf16>(ex, x, offsets, rows, cache, dy, dx, dgate, dup, ddown, workspace, s); break;
     }
     return hipGetLastError();
 }

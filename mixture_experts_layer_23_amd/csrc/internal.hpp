@@ -86,13 +86,15 @@ hipError_t launch_combine(const void* y, rudnn_moe_dtype dt, const int32_t* toke
 
 // Expert GEMMs.  Workspace layout is owned by experts.hip.
 size_t experts_workspace_bytes(int64_t E, int64_t H, int64_t I, rudnn_moe_dtype dt, int64_t rows);
+// cache: NULL, or [rows, 2I] FP32 that receives the pre-activations [gate . x | up . x].
 hipError_t launch_experts(const rudnn_moe_experts* ex, const void* dispatched, const int32_t* offsets, int64_t rows,
-                          void* out, void* workspace, hipStream_t s);
+                          void* out, void* workspace, hipStream_t s, float* cache = nullptr);
 
-// Experts backward (experts_backward.hip).
-size_t experts_backward_workspace_bytes(int64_t E, int64_t I, rudnn_moe_dtype dt, int64_t rows);
+// Experts backward (experts_backward.hip).  cached: the pre-activations come from the forward's
+// cache (no room for them in the workspace); cache NULL recomputes them.
+size_t experts_backward_workspace_bytes(int64_t E, int64_t I, rudnn_moe_dtype dt, int64_t rows, bool cached);
 hipError_t launch_experts_backward(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int64_t rows,
-                                   const void* dy, void* dx, float* dgate, float* dup, float* ddown, void* workspace,
-                                   hipStream_t s);
+                                   const float* cache, const void* dy, void* dx, float* dgate, float* dup,
+                                   float* ddown, void* workspace, hipStream_t s);
 
 }  // namespace rudnn

@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
         L.rudnn_moe_experts_workspace_size.argtypes = [EXP, I64]
         L.rudnn_moe_experts_workspace_size.restype = SZ
         L.rudnn_moe_experts_forward.argtypes = [EXP, P, P, I64, P, P, SZ, P]
+        L.rudnn_moe_experts_forward_training.argtypes = [EXP, P, P, I64, P, P, P, SZ, P]
         L.rudnn_moe_combine.argtypes = [P, I32, P, P, I32, I64, I64, I64, P, P]
         L.rudnn_moe_forward_workspace_size.argtypes = [EXP, I64, I64, I32]
         L.rudnn_moe_forward_workspace_size.restype = SZ
@@ -103,9 +104,9 @@ def lib() -> ctypes.CDLL:
         L.rudnn_moe_selected_router_backward.argtypes = [P, I32, I64, I64, P, I32, I64, RouterWeightOptions, P, P, P]
         L.rudnn_moe_combine_backward.argtypes = [P, I32, P, P, I32, P, I64, I64, I64, P, P, P]
         L.rudnn_moe_dispatch_backward.argtypes = [P, I32, P, I64, I64, I64, P, P]
-        L.rudnn_moe_experts_backward_workspace_size.argtypes = [EXP, I64]
+        L.rudnn_moe_experts_backward_workspace_size.argtypes = [EXP, I64, I32]
         L.rudnn_moe_experts_backward_workspace_size.restype = SZ
-        L.rudnn_moe_experts_backward.argtypes = [EXP, P, P, I64, P, P, P, P, P, P, SZ, P]
+        L.rudnn_moe_experts_backward.argtypes = [EXP, P, P, I64, P, P, P, P, P, P, P, SZ, P]
         L.rudnn_moe_status_string.argtypes = [I32]
         L.rudnn_moe_status_string.restype = ctypes.c_char_p
         L.rudnn_moe_time_next_launch.argtypes = [I32, P, P]
@@ -113,7 +114,8 @@ def lib() -> ctypes.CDLL:
                   "rudnn_moe_forward", "rudnn_moe_time_next_launch", "rudnn_moe_route_sigmoid_grouped",
                   "rudnn_moe_forward_sigmoid_grouped", "rudnn_moe_route_projected", "rudnn_moe_forward_projected",
                   "rudnn_moe_selected_router_weights", "rudnn_moe_selected_router_backward",
-                  "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward", "rudnn_moe_experts_backward"):
+                  "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward", "rudnn_moe_experts_backward",
+                  "rudnn_moe_experts_forward_training"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -202,8 +204,28 @@ class SwiGluExperts:
 
     def backward_dispatched(self, d: "Dispatched", grad_expert_output: torch.Tensor, workspace=None):
         """Backward of forward_dispatched (user guide section 12, step 2): ``(grad_dispatched,
-        dgate, dup, ddown)``, the weight gradients FP32."""
+        dgate, dup, ddown)``, the weight gradients FP32; the gate and up products are recomputed."""
         return experts_backward(self, d.dispatched, d.expert_offsets, grad_expert_output, workspace=workspace)
+
+    def forward_dispatched_training(self, d: "Dispatched", out=None, workspace=None):
+        """User guide section 12: ``(output, cache)``; ``cache.backward(dexpert)`` gives
+        ``(grad_dispatched, dgate, dup, ddown)``.  The dispatched rows must stay unchanged until then."""
+        out, pre = experts_forward_training(self, d.dispatched, d.expert_offsets, out=out, workspace=workspace)
+        return out, ExpertsCache(self, d.dispatched, d.expert_offsets, pre)
+
+
+class ExpertsCache:
+    """What the experts backward reads: the forward's dispatched rows and offsets and the FP32
+    pre-activations [gate . x | up . x] [rows, 2I] it stored."""
+
+    def __init__(self, experts: SwiGluExperts, dispatched: torch.Tensor, expert_offsets: torch.Tensor,
+                 preactivations: torch.Tensor):
+        self.experts, self.dispatched, self.expert_offsets = experts, dispatched, expert_offsets
+        self.preactivations = preactivations
+
+    def backward(self, grad_expert_output: torch.Tensor, workspace=None):
+        return experts_backward(self.experts, self.dispatched, self.expert_offsets, grad_expert_output,
+                                cache=self.preactivations, workspace=workspace)
 
 
 def route(logits: torch.Tensor, top_k: int, renormalize: bool):
@@ -312,6 +334,24 @@ def experts_forward(experts: SwiGluExperts, dispatched: torch.Tensor, expert_off
         ctypes.byref(experts.view), _ptr(dispatched), _ptr(expert_offsets), rows, _ptr(out), _ptr(workspace),
         workspace.numel(), _stream(dispatched)))
     return out
+
+
+def experts_forward_training(experts: SwiGluExperts, dispatched: torch.Tensor, expert_offsets: torch.Tensor,
+                             out=None, cache=None, workspace=None):
+    """``experts_forward`` that also returns the FP32 pre-activations [rows, 2I] (the backward's cache)."""
+    dispatched = _contig(dispatched, "dispatched")
+    rows = dispatched.shape[0]
+    if out is None:
+        out = torch.empty_like(dispatched)
+    if cache is None:
+        cache = torch.empty(rows, 2 * experts.I, dtype=torch.float32, device=dispatched.device)
+    if workspace is None:
+        workspace = torch.empty(max(experts_workspace_size(experts, rows), 1), dtype=torch.uint8,
+                                device=dispatched.device)
+    _check("rudnn_moe_experts_forward_training", lib().rudnn_moe_experts_forward_training(
+        ctypes.byref(experts.view), _ptr(dispatched), _ptr(expert_offsets), rows, _ptr(out), _ptr(_contig(cache, "cache")),
+        _ptr(workspace), workspace.numel(), _stream(dispatched)))
+    return out, cache
 
 
 def combine(expert_output: torch.Tensor, token_map: torch.Tensor, weights: torch.Tensor, out=None) -> torch.Tensor:
@@ -465,14 +505,15 @@ def dispatch_backward(grad_dispatched: torch.Tensor, token_map: torch.Tensor, ou
     return out
 
 
-def experts_backward_workspace_size(experts: SwiGluExperts, rows: int) -> int:
-    return lib().rudnn_moe_experts_backward_workspace_size(ctypes.byref(experts.view), rows)
+def experts_backward_workspace_size(experts: SwiGluExperts, rows: int, cached: bool = False) -> int:
+    return lib().rudnn_moe_experts_backward_workspace_size(ctypes.byref(experts.view), rows, int(bool(cached)))
 
 
 def experts_backward(experts: SwiGluExperts, dispatched: torch.Tensor, expert_offsets: torch.Tensor,
-                     grad_expert_output: torch.Tensor, workspace=None):
+                     grad_expert_output: torch.Tensor, cache=None, workspace=None):
     """Returns ``(grad_dispatched [rows, H] (rows outside the experts' ranges zero), dgate, dup [E, I, H],
-    ddown [E, H, I] FP32)``."""
+    ddown [E, H, I] FP32)``.  ``cache``: the pre-activations from ``experts_forward_training``, or None
+    to recompute them."""
     dispatched = _contig(dispatched, "dispatched")
     grad_expert_output = _contig(grad_expert_output, "grad_expert_output")
     rows = dispatched.shape[0]
@@ -482,10 +523,15 @@ def experts_backward(experts: SwiGluExperts, dispatched: torch.Tensor, expert_of
     dg = torch.empty(E, I, H, dtype=torch.float32, device=dev)
     du = torch.empty(E, I, H, dtype=torch.float32, device=dev)
     dd = torch.empty(E, H, I, dtype=torch.float32, device=dev)
+    if cache is not None:
+        cache = _contig(cache, "cache")
+        if cache.dtype != torch.float32 or tuple(cache.shape) != (rows, 2 * I):
+            raise ValueError("cache must be FP32 [rows, 2I]")
     if workspace is None:
-        workspace = torch.empty(max(experts_backward_workspace_size(experts, rows), 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(experts_backward_workspace_size(experts, rows, cache is not None), 1),
+                                dtype=torch.uint8, device=dev)
     _check("rudnn_moe_experts_backward", lib().rudnn_moe_experts_backward(
         ctypes.byref(experts.view), _ptr(dispatched), _ptr(_contig(expert_offsets, "expert_offsets")), rows,
-        _ptr(grad_expert_output), _ptr(dx), _ptr(dg), _ptr(du), _ptr(dd), _ptr(workspace), workspace.numel(),
+        _ptr(cache), _ptr(grad_expert_output), _ptr(dx), _ptr(dg), _ptr(du), _ptr(dd), _ptr(workspace), workspace.numel(),
         _stream(dispatched)))
     return dx, dg, du, dd

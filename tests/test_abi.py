@@ -28,14 +28,14 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
     for required in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
                      "rudnn_moe_forward", "rudnn_moe_route_sigmoid_grouped", "rudnn_moe_forward_sigmoid_grouped",
                      "rudnn_moe_route_projected", "rudnn_moe_forward_projected", "rudnn_moe_selected_router_weights",
                      "rudnn_moe_selected_router_backward", "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward",
-                     "rudnn_moe_experts_backward"):
+                     "rudnn_moe_experts_backward", "rudnn_moe_experts_forward_training"):
         assert required in names
 
 
@@ -117,6 +117,27 @@ def test_experts_validation(L):
     # f32 experts have no alignment or multiple-of-8 requirement
     ex32 = _experts(dt=0, H=60, I=52, up=FAKE + 2**30 + 4)
     assert L.rudnn_moe_experts_workspace_size(ctypes.byref(ex32), 10) >= 10 * 52 * 4
+
+
+def test_experts_forward_training_validation(L):
+    f = L.rudnn_moe_experts_forward_training
+    ex = _experts()
+    need = L.rudnn_moe_experts_workspace_size(ctypes.byref(ex), 256)
+    x, offs, out, cache, ws = FAKE + 2**33, FAKE + 2**34, FAKE + 2**35, FAKE + 2**37, FAKE + 2**36
+
+    def call(rows=256, **kw):
+        a = dict(x=x, offs=offs, out=out, cache=cache, ws=ws, wsz=need)
+        a.update(kw)
+        return f(ctypes.byref(ex), a["x"], a["offs"], rows, a["out"], a["cache"], a["ws"], a["wsz"], None)
+
+    assert call(cache=None) == ARGUMENT                 # the cache is the point of the call
+    assert call(cache=cache + 4) == UNSUPPORTED         # unaligned
+    assert call(cache=x + 64) == ARGUMENT               # overlaps the dispatched rows
+    assert call(cache=out + 256 * 64 * 2 - 16) == ARGUMENT  # overlaps the output
+    assert call(cache=ws + 16) == ARGUMENT              # overlaps the workspace
+    assert call(wsz=need - 1) == WORKSPACE
+    assert call(rows=-1) == SHAPE
+    assert call(rows=0, x=None, offs=None, out=None, cache=None, ws=None, wsz=0) == OK
 
 
 def test_combine_validation(L):
@@ -357,16 +378,18 @@ def test_combine_and_dispatch_backward_validation(L):
 def test_experts_backward_validation(L):
     f = L.rudnn_moe_experts_backward
     ex = _experts()
-    need = L.rudnn_moe_experts_backward_workspace_size(ctypes.byref(ex), 256)
+    need = L.rudnn_moe_experts_backward_workspace_size(ctypes.byref(ex), 256, 0)
     assert need >= 256 * 96 * 4 * 2 and need % 256 == 0
+    need_cached = L.rudnn_moe_experts_backward_workspace_size(ctypes.byref(ex), 256, 1)
+    assert need - need_cached == 256 * 96 * 2 * 4        # the recomputed FP32 [g | u] is left out
     x, offs, dy, dx = FAKE + 2**33, FAKE + 2**34, FAKE + 2**35, FAKE + 2**36
     dg, du, dd, ws = FAKE + 2**37, FAKE + 2**38, FAKE + 2**39, FAKE + 2**40
 
     def call(exv=ex, rows=256, **kw):
-        a = dict(x=x, offs=offs, dy=dy, dx=dx, dg=dg, du=du, dd=dd, ws=ws, wsz=need)
+        a = dict(x=x, offs=offs, cache=None, dy=dy, dx=dx, dg=dg, du=du, dd=dd, ws=ws, wsz=need)
         a.update(kw)
-        return f(ctypes.byref(exv), a["x"], a["offs"], rows, a["dy"], a["dx"], a["dg"], a["du"], a["dd"], a["ws"],
-                 a["wsz"], None)
+        return f(ctypes.byref(exv), a["x"], a["offs"], rows, a["cache"], a["dy"], a["dx"], a["dg"], a["du"], a["dd"],
+                 a["ws"], a["wsz"], None)
 
     assert call(exv=_experts(E=0)) == SHAPE
     assert call(exv=_experts(dt=9)) == DTYPE
@@ -379,5 +402,10 @@ def test_experts_backward_validation(L):
     assert call(wsz=need - 1) == WORKSPACE
     assert call(dx=x + 64) == ARGUMENT                          # grad_dispatched overlaps the input rows
     assert call(dd=FAKE + 2**30 + 64) == ARGUMENT               # a weight gradient overlaps the up weights
+    cache = FAKE + 2**41
+    assert call(cache=cache + 8) == UNSUPPORTED                 # unaligned cache
+    assert call(cache=cache, dx=cache + 64) == ARGUMENT         # an output overlaps the cache
+    assert call(cache=cache, ws=cache + 256) == ARGUMENT        # the workspace overlaps the cache
+    assert call(cache=None, wsz=need_cached) == WORKSPACE       # recomputing needs the larger workspace
     # no rows: only the (zero) weight gradients are written, the row buffers may be NULL
-    assert L.rudnn_moe_experts_backward_workspace_size(ctypes.byref(ex), 0) > 0
+    assert L.rudnn_moe_experts_backward_workspace_size(ctypes.byref(ex), 0, 0) > 0

@@ -187,15 +187,43 @@ def test_experts_backward_parity(name):
     dx, dgate, dup, ddown = ex.backward_dispatched(d, dy)
     rdx, rdg, rdu, rdd = oracle.experts_backward(d.dispatched.cpu(), d.expert_offsets.cpu().numpy(), gate.cpu(),
                                                  up.cpu(), down.cpu(), dy.cpu())
-    assert_close(dx, rdx, w.dtype, "grad_dispatched")
-    # weight gradients: FP32 sums over the expert's rows of products of dtype operands
-    tol = "f32" if w.dtype == "f32" else w.dtype
-    assert_close(dgate, rdg, tol, "dgate")
-    assert_close(dup, rdu, tol, "dup")
-    assert_close(ddown, rdd, tol, "ddown")
+    # the training forward: same output bits as the forward, plus the FP32 pre-activation cache
+    y_plain = ex.forward_dispatched(d)
+    y, cache = ex.forward_dispatched_training(d)
+    assert torch.equal(y, y_plain)
+    _check_preactivations(cache.preactivations, d.dispatched, d.expert_offsets, gate, up, range(d.dispatched.shape[0]))
+    cached = cache.backward(dy)
+    for tag, (gx, gg, gu_, gd) in (("recomputed", (dx, dgate, dup, ddown)), ("cached", cached)):
+        assert_close(gx, rdx, w.dtype, f"grad_dispatched ({tag})")
+        # weight gradients: FP32 sums over the expert's rows of products of dtype operands
+        tol = "f32" if w.dtype == "f32" else w.dtype
+        assert_close(gg, rdg, tol, f"dgate ({tag})")
+        assert_close(gu_, rdu, tol, f"dup ({tag})")
+        assert_close(gd, rdd, tol, f"ddown ({tag})")
     # repeatable bit for bit
     dx2, dg2, du2, dd2 = ex.backward_dispatched(d, dy)
     assert torch.equal(dx2, dx) and torch.equal(dg2, dgate) and torch.equal(du2, dup) and torch.equal(dd2, ddown)
+    again = cache.backward(dy)
+    assert all(torch.equal(a, b) for a, b in zip(again, cached))
+
+
+def _check_preactivations(pre, dispatched, offsets, gate, up, rows):
+    """cache[r] = [gate_e . x_r | up_e . x_r] for the listed rows: float64 products of the same
+    operands, within the FP32 accumulation bound (H + 2) 2^-24 sum_h |x_h w_h| (per element; the
+    two extra units cover FP32 operands, whose products round)."""
+    offs = offsets.cpu().numpy()
+    rows = np.asarray(list(rows))
+    xs = dispatched[torch.from_numpy(rows).to(dispatched.device)].cpu().double()
+    got = pre[torch.from_numpy(rows).to(pre.device)].cpu().double()
+    H = xs.shape[1]
+    for n, r in enumerate(rows):
+        e = int(np.searchsorted(offs, r, side="right") - 1)
+        for half, wt in enumerate((gate, up)):
+            W = wt[e].cpu().double()
+            ref = W @ xs[n]
+            bound = (H + 2) * 2.0**-24 * (W.abs() @ xs[n].abs()) + 1e-30
+            err = (got[n, half * W.shape[0]:(half + 1) * W.shape[0]] - ref).abs()
+            assert (err <= bound).all(), f"pre-activation row {r} half {half}: max err {err.max():.3g}"
 
 
 def test_experts_backward_no_rows():
@@ -224,10 +252,14 @@ def test_experts_backward_mixtral_sampled():
     g = torch.Generator(device=DEV).manual_seed(4)
     dy = (torch.randn(d.dispatched.shape, generator=g, device=DEV) * 0.05).bfloat16()
     dx, dgate, dup, ddown = ex.backward_dispatched(d, dy)
+    y, cache = ex.forward_dispatched_training(d)
+    cdx, cdgate, cdup, cddown = cache.backward(dy)
     torch.cuda.synchronize()
     offs = d.expert_offsets.cpu().numpy()
     rng = np.random.default_rng(11)
     rows = np.sort(rng.choice(int(offs[-1]), size=6, replace=False))
+    _check_preactivations(cache.preactivations, d.dispatched, d.expert_offsets, gate, up, rows)
+    del y
     gate_c, up_c, down_c = gate.cpu(), up.cpu(), down.cpu()
     for r in rows:
         e = int(np.searchsorted(offs, r, side="right") - 1)
@@ -235,6 +267,7 @@ def test_experts_backward_mixtral_sampled():
         rdx, _, _, _ = oracle.experts_backward(d.dispatched[r:r + 1].cpu(), np.array([0, 1], np.int32),
                                                gate_c[e:e + 1], up_c[e:e + 1], down_c[e:e + 1], dy[r:r + 1].cpu())
         assert_close(dx[r:r + 1], rdx, "bf16", f"grad_dispatched row {r}")
+        assert_close(cdx[r:r + 1], rdx, "bf16", f"grad_dispatched row {r} (cached)")
     units = torch.from_numpy(np.sort(rng.choice(w.I, size=16, replace=False))).to(DEV)
     for e in (0, w.E - 1):
         a, b = int(offs[e]), int(offs[e + 1])
@@ -243,6 +276,70 @@ def test_experts_backward_mixtral_sampled():
         d1 = down_c[e:e + 1][:, :, uc].contiguous()
         _, rdg, rdu, rdd = oracle.experts_backward(d.dispatched[a:b].cpu(), np.array([0, b - a], np.int32), g1, u1, d1,
                                                    dy[a:b].cpu())
-        assert_close(dgate[e, units].cpu(), rdg[0], "bf16", f"dgate expert {e}")
-        assert_close(dup[e, units].cpu(), rdu[0], "bf16", f"dup expert {e}")
-        assert_close(ddown[e][:, units].cpu(), rdd[0], "bf16", f"ddown expert {e}")
+        for tag, (gg, gu_, gd) in (("", (dgate, dup, ddown)), (" (cached)", (cdgate, cdup, cddown))):
+            assert_close(gg[e, units].cpu(), rdg[0], "bf16", f"dgate expert {e}{tag}")
+            assert_close(gu_[e, units].cpu(), rdu[0], "bf16", f"dup expert {e}{tag}")
+            assert_close(gd[e][:, units].cpu(), rdd[0], "bf16", f"ddown expert {e}{tag}")
+
+
+# ------------------------------------------------------------------------------------------
+# the whole first-order chain of section 12
+# ------------------------------------------------------------------------------------------
+
+CHAIN_CASES = {
+    # name: (layer, scoring, renormalize, scale)
+    "bf16_softmax_renorm": (BWD_LAYERS["bf16_small"], "softmax", True, 1.0),
+    "f16_softmax_plain": (BWD_LAYERS["f16_ragged"], "softmax", False, 1.0),
+    "f32_sigmoid_scaled": (BWD_LAYERS["f32_tiny"], "sigmoid", True, 2.5),
+}
+
+
+@pytest.mark.parametrize("name", list(CHAIN_CASES))
+def test_training_chain(name):
+    """Route, keep the selection and recompute its FP32 weights, dispatch, the experts forward with
+    its cache, combine; then combine_backward -> cache.backward -> dispatch_backward ->
+    selected_router_backward.  The oracle runs the same chain from the same inputs with its own
+    routing, dispatch and intermediate values; the selection and the map must agree exactly, every
+    gradient within the dtype tolerance."""
+    w, scoring, renorm, scale = CHAIN_CASES[name]
+    say("training chain", name)
+    logits, _ = make_logits(w)
+    x = make_tokens(w, DEV)
+    gate, up, down = make_experts(w, DEV)
+    ex = moe.SwiGluExperts(gate, up, down)
+    lg = logits.to(DEV)
+    idx, _ = moe.route(lg, w.top_k, renorm)
+    wts = moe.selected_router_weights(lg, idx, scoring, renorm, scale)
+    d = moe.dispatch(idx, x, w.E)
+    y, cache = ex.forward_dispatched_training(d)
+    out = moe.combine(y, d.token_map, wts)
+    g = torch.Generator(device=DEV).manual_seed(w.seed + 7)
+    dout = (torch.randn(w.T, w.H, generator=g, device=DEV) * 0.1).to(DTYPES[w.dtype])
+    dexp, dw = moe.combine_backward(y, d.token_map, wts, dout)
+    dxd, dgate, dup, ddown = cache.backward(dexp)
+    dx = moe.dispatch_backward(dxd, d.token_map)
+    dlogits = moe.selected_router_backward(lg, idx, dw, scoring, renorm, scale)
+    torch.cuda.synchronize()
+
+    ridx, _, _ = oracle.route(logits, w.top_k, renorm)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ridx)
+    rw, _ = oracle.selected_router_weights(logits, ridx, scoring, renorm, scale)
+    rdisp, roffs, rmap, _ = oracle.dispatch(ridx, x.cpu(), w.E)
+    assert np.array_equal(d.token_map.cpu().numpy(), rmap)
+    ry = oracle.experts_forward(rdisp, roffs, gate, up, down)
+    rout = oracle.combine(ry, rmap, rw)
+    rdexp, rdw = oracle.combine_backward(ry, rmap, rw, dout.cpu())
+    rdxd, rdg, rdu, rdd = oracle.experts_backward(rdisp, roffs, gate, up, down, rdexp)
+    rdx = oracle.dispatch_backward(rdxd, rmap)
+    rdl = oracle.selected_router_backward(logits, ridx, rdw, scoring, renorm, scale)
+
+    assert_close(wts, rw, "f32", "router weights")
+    assert_close(out, rout, w.dtype, "output")
+    assert_close(dexp, rdexp, w.dtype, "dexpert")
+    assert_close(dw, rdw, w.dtype, "dweights")
+    assert_close(dx, rdx, w.dtype, "dinput")
+    tol = "f32" if w.dtype == "f32" else w.dtype
+    assert_close(dgate, rdg, tol, "dgate")
+    assert_close(dup, rdu, tol, "dup")
+    assert_close(ddown, rdd, tol, "ddown")
+    assert_close(dlogits, rdl, w.dtype, "dlogits")
