@@ -90,7 +90,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
-                    help="target CPU time of the oracle baseline sample (sized from an 8-token probe)")
+                    help="target CPU time of the oracle baseline sample (sized from 8- and 64-token probes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-stages", action="store_true")
     ap.add_argument("--no-sigmoid", action="store_true",
@@ -226,12 +226,16 @@ def main():
         from oracle import oracle
         g_c, u_c, d_c = gate.cpu(), up.cpu(), down.cpu()
         x_c = x.cpu()
-        probe = 8
-        t0 = time.perf_counter()
-        oracle.forward(x_c[:probe], logits_cpu[:probe], k, renorm, g_c, u_c, d_c)
-        per_token = (time.perf_counter() - t0) / probe
-        n = int(min(T, max(probe, args.cpu_seconds / per_token)))
-        log(f"cpu baseline: {n} tokens through the oracle (probe: {per_token * 1e3:.1f} ms/token)")
+        # two probes give a fixed cost (weight rows decoded once per block) and a cost per token
+        times = {}
+        for probe in (8, 64):
+            t0 = time.perf_counter()
+            oracle.forward(x_c[:probe], logits_cpu[:probe], k, renorm, g_c, u_c, d_c)
+            times[probe] = time.perf_counter() - t0
+        per_token = max((times[64] - times[8]) / 56, 1e-6)
+        fixed = max(times[8] - 8 * per_token, 0.0)
+        n = int(min(T, max(64, (args.cpu_seconds - fixed) / per_token)))
+        log(f"cpu baseline: {n} tokens through the oracle (probes: {per_token * 1e3:.2f} ms/token + {fixed:.2f} s)")
         t0 = time.perf_counter()
         oracle.forward(x_c[:n], logits_cpu[:n], k, renorm, g_c, u_c, d_c)
         dt = time.perf_counter() - t0

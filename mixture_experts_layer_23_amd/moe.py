@@ -475,6 +475,32 @@ def selected_router_backward(logits: torch.Tensor, indices: torch.Tensor, grad_w
     return g
 
 
+class RouterTrainingPlan:
+    """User guide section 12 (RoutingPlan::into_training): the selection ``indices`` is kept and
+    its FP32 weights are recomputed from ``logits``; ``routing()`` gives (indices, weights) for
+    dispatch and combine, ``backward(grad_weights)`` the logits gradient.  The logits and indices
+    must stay unchanged until then."""
+
+    def __init__(self, logits: torch.Tensor, indices: torch.Tensor, scoring: str = "softmax",
+                 renormalize: bool = False, scale: float = 1.0, unsigned: bool = True):
+        self.logits, self.indices = logits, indices
+        self.scoring, self.renormalize, self.scale, self.unsigned = scoring, renormalize, scale, unsigned
+        self.weights = selected_router_weights(logits, indices, scoring, renormalize, scale, unsigned)
+
+    def routing(self):
+        return self.indices, self.weights
+
+    def backward(self, grad_weights: torch.Tensor) -> torch.Tensor:
+        return selected_router_backward(self.logits, self.indices, grad_weights, self.scoring, self.renormalize,
+                                        self.scale, self.unsigned)
+
+
+def into_training(logits: torch.Tensor, indices: torch.Tensor, scoring: str = "softmax", renormalize: bool = False,
+                  scale: float = 1.0) -> RouterTrainingPlan:
+    """A routing result (``indices`` as ``route`` returns them) turned into a training plan."""
+    return RouterTrainingPlan(logits, indices, scoring, renormalize, scale, unsigned=True)
+
+
 def combine_backward(expert_output: torch.Tensor, token_map: torch.Tensor, weights: torch.Tensor,
                      grad_output: torch.Tensor, grad_expert_output: torch.Tensor | None = None):
     """Returns ``(grad_expert_output [T*k, H], grad_weights [T, k] FP32)`` (user guide section 12, step 1).

@@ -308,8 +308,8 @@ def test_training_chain(name):
     gate, up, down = make_experts(w, DEV)
     ex = moe.SwiGluExperts(gate, up, down)
     lg = logits.to(DEV)
-    idx, _ = moe.route(lg, w.top_k, renorm)
-    wts = moe.selected_router_weights(lg, idx, scoring, renorm, scale)
+    plan = moe.into_training(lg, moe.route(lg, w.top_k, renorm)[0], scoring, renorm, scale)
+    idx, wts = plan.routing()
     d = moe.dispatch(idx, x, w.E)
     y, cache = ex.forward_dispatched_training(d)
     out = moe.combine(y, d.token_map, wts)
@@ -318,7 +318,7 @@ def test_training_chain(name):
     dexp, dw = moe.combine_backward(y, d.token_map, wts, dout)
     dxd, dgate, dup, ddown = cache.backward(dexp)
     dx = moe.dispatch_backward(dxd, d.token_map)
-    dlogits = moe.selected_router_backward(lg, idx, dw, scoring, renorm, scale)
+    dlogits = plan.backward(dw)
     torch.cuda.synchronize()
 
     ridx, _, _ = oracle.route(logits, w.top_k, renorm)
