@@ -8,17 +8,20 @@
 //   dgate_e = dg^T x,  dup_e = du^T x,  ddown_e = dy^T h     (FP32, sums over the expert's rows)
 // silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z).
 //
-// One MFMA kernel serves all five products: C[m, n] = sum_k A(m, k) B(n, k), 128 x 128 tiles,
-// K staged 128 bytes per row, four wavefronts of 64 x 64 (v_mfma_f32_32x32x16 for BF16/F16,
-// 32x32x2f32 for FP32).  An operand is either "K-major" (k contiguous: staged as 16-byte pieces)
-// or "X-major" (its row/column index contiguous): a thread then loads a block of CE rows of k by
-// CE consecutive x (CE = elements per 16 bytes), transposes it in registers and stores CE
-// 16-byte pieces of the [x][k] LDS tile.  The operand tiles go through registers: step k+1 is
-// loaded while step k computes, then written to the other LDS stage.
+// One MFMA kernel serves all five products: C[m, n] = sum_k A(m, k) B(n, k) on BM x BN tiles
+// (256 x 256, eight wavefronts of 128 x 64), K staged 128 bytes per row (v_mfma_f32_32x32x16 for
+// BF16/F16, 32x32x2f32 for FP32).  An operand is either "K-major" (k contiguous: staged as 16-byte pieces)
+// or "X-major" (its row/column index contiguous): a thread then loads 4 rows of k by CE
+// consecutive x (CE = elements per 16 bytes), transposes them in registers and stores CE runs
+// of 4 k values into the [x][k] LDS tile.  The operand tiles go through registers (two sets): the
+// loads of step k+2 are issued while step k computes; step k+1, loaded during step k-1, is written
+// to the other LDS stage after step k's MFMAs.
 // Two operand sources may be stacked along the operand's outer index (gate over up).
 // Grouping: ROWS tiles the expert's rows along M (a device-side plan of m-tiles per expert);
 // KROWS uses the expert's rows as the contraction axis, every (expert, m, n) tile (an expert
 // without rows gets zeros).
+#include <type_traits>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -29,8 +32,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, ROWB = 128, THREADS = 256;
-constexpr int LDS_BYTES = 2 * (BM + BN) * ROWB;  // two stages
+constexpr int ROWB = 128;  // bytes of K per staged row and step
+
+// Block tile BM x BN, WM x WN wavefronts (each (BM / WM) x (BN / WN), whole 32 x 32 MFMA blocks).
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, THREADS = 64 * WM_ * WN_;
+    static constexpr int LDS_BYTES = 2 * (BM_ + BN_) * ROWB;  // two stages
+};
 
 template <typename T>
 struct Mma;
@@ -63,21 +72,22 @@ struct Mma<float> {  // four 32x32x2 steps over one 16-byte chunk per lane half 
 // (one chunk from each of 32 consecutive rows) then spread over all LDS banks.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// CE x CE block transpose of 16-byte rows (CE elements each): out[x] holds element x of in[0..CE).
-__device__ __forceinline__ void transpose_block(const uint4 (&in)[8], uint4 (&out)[8]) {  // 16-bit elements
+// 4 rows of 8 16-bit elements -> 8 runs of 4: out[x] holds element x of in[0..4).
+__device__ __forceinline__ void transpose_quad(const uint4 (&in)[4], uint2 (&out)[8]) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-        uint32_t d[4];
+        uint32_t d[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
             const uint32_t a = reinterpret_cast<const uint32_t*>(&in[2 * j])[x >> 1];
             const uint32_t b = reinterpret_cast<const uint32_t*>(&in[2 * j + 1])[x >> 1];
             d[j] = (x & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
         }
-        out[x] = make_uint4(d[0], d[1], d[2], d[3]);
+        out[x] = make_uint2(d[0], d[1]);
     }
 }
-__device__ __forceinline__ void transpose_block(const uint4 (&in)[4], uint4 (&out)[4]) {  // 32-bit elements
+// 4 x 4 transpose of 32-bit elements: out[x] holds element x of in[0..4).
+__device__ __forceinline__ void transpose_block(const uint4 (&in)[4], uint4 (&out)[4]) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         uint32_t d[4];
@@ -127,7 +137,7 @@ struct Plan {
     const int32_t* mt_begin;   // [E + 1]
 };
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int rows,
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int rows, int BM,
                                                     int32_t* __restrict__ row_begin, int32_t* __restrict__ row_count,
                                                     int32_t* __restrict__ mt_begin) {
     __shared__ int scratch[17];
@@ -158,17 +168,25 @@ struct Epi {
     void* h;              // EPI_SWIGLU: [rows, I] dtype
 };
 
-// C = A B^T on 128 x 128 tiles; see the file comment.
-template <typename T, int MODE, int EPI, bool AK, bool BK>
-__global__ __launch_bounds__(THREADS) void gemm_kernel(Opnd A, Opnd B, int M, int N, int K, int E, Plan plan,
-                                                       const int32_t* __restrict__ offsets, int rows, int NT, int MT,
-                                                       Epi ep) {
+// C = A B^T on BM x BN tiles; see the file comment.
+template <typename T, typename C, int MODE, int EPI, bool AK, bool BK>
+__global__ __launch_bounds__(C::THREADS) void gemm_kernel(Opnd A, Opnd B, int M, int N, int K, int E, Plan plan,
+                                                          const int32_t* __restrict__ offsets, int rows, int NT,
+                                                          int MT, Epi ep) {
+    constexpr int BM = C::BM, BN = C::BN, THREADS = C::THREADS;
+    constexpr int TM = BM / C::WM, TN = BN / C::WN;  // wavefront tile
+    constexpr int FM = TM / 32, FN = TN / 32;        // 32 x 32 MFMA blocks per wavefront
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wavefront tiles are whole MFMA blocks");
     constexpr int CE = 16 / (int)sizeof(T);     // elements per 16-byte chunk
     constexpr int BKE = ROWB / (int)sizeof(T);  // K elements per step
     constexpr int NCH = ROWB / 16;              // chunks per staged row
-    constexpr int KQ = BM * NCH / THREADS;      // K-major pieces per thread
-    constexpr int NB = (BKE / CE) * (BM / CE);  // X-major CE x CE blocks per operand tile
-    static_assert(NB == 128 || NB == 256, "at most one X-major block per thread and operand");
+    constexpr int KQA = BM * NCH / THREADS, KQB = BN * NCH / THREADS;  // K-major pieces per thread
+    static_assert(BM * NCH % THREADS == 0 && BN * NCH % THREADS == 0, "K-major pieces split evenly");
+    // X-major pieces: 4 rows of k x CE consecutive x
+    constexpr int NKQ = BKE / 4;                                     // k quads per step
+    constexpr int NPA = NKQ * (BM / CE), NPB = NKQ * (BN / CE);      // pieces per operand tile
+    constexpr int XQA = (NPA + THREADS - 1) / THREADS, XQB = (NPB + THREADS - 1) / THREADS;  // per thread
+    static_assert(NKQ % 8 == 0 && (BM / CE) % 8 == 0 && (BN / CE) % 8 == 0, "pieces come in 8 x 8 groups");
     typedef typename Mma<T>::frag frag;
     extern __shared__ __align__(1024) unsigned char lds[];
 
@@ -205,16 +223,17 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Opnd A, Opnd B, int M, in
     const int nlim = min(BN, N - n0);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C::WN, wn = wave % C::WN;
 
     // The outer index of an operand's tile row x (A: a dispatched row or m, B: n).
     auto x_outer = [&](bool is_a, int x) -> int64_t {
         return is_a ? (MODE == ROWS ? row0 + x : (int64_t)(m0 + x)) : (int64_t)(n0 + x);
     };
     // K-major staging: piece c -> row x = c / NCH, chunk c % NCH.
-    auto load_k = [&](const Opnd& o, bool is_a, int xlim, int k0, uint4 (&r)[KQ]) __attribute__((always_inline)) {
+    auto load_k = [&](const Opnd& o, bool is_a, int xlim, int k0, auto& r) __attribute__((always_inline)) {
+        constexpr int NQ = sizeof(r) / sizeof(uint4);
 #pragma unroll
-        for (int q = 0; q < KQ; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int c = tid + q * THREADS, x = c / NCH, k = k0 + (c % NCH) * CE;
             r[q] = make_uint4(0, 0, 0, 0);
             if (x < xlim && k < kn)
@@ -222,118 +241,180 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(Opnd A, Opnd B, int M, in
                     opnd_row<T>(o, MODE == ROWS && is_a ? 0 : e, x_outer(is_a, x)) + kb + k);
         }
     };
-    auto store_k = [&](unsigned char* st, const uint4 (&r)[KQ]) __attribute__((always_inline)) {
+    auto store_k = [&](unsigned char* st, const auto& r) __attribute__((always_inline)) {
+        constexpr int NQ = sizeof(r) / sizeof(uint4);
 #pragma unroll
-        for (int q = 0; q < KQ; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const int c = tid + q * THREADS, x = c / NCH, kc = c % NCH;
             *reinterpret_cast<uint4*>(st + x * ROWB + ((kc ^ swz(x)) * 16)) = r[q];
         }
     };
-    // X-major staging: block b -> k group b / (BM / CE) (CE rows of k), x group b % (BM / CE).
-    // A takes block tid, B block (tid + 128) mod 256: with 128 blocks per operand (16-bit
-    // elements) the two operands occupy different threads; with 256 (FP32) every thread takes
-    // one block of each.
-    auto block_of = [&](bool is_a) { return (tid + (is_a ? 0 : 128)) & (THREADS - 1); };
-    auto load_x = [&](const Opnd& o, bool is_a, int xlim, int k0, uint4 (&r)[CE]) __attribute__((always_inline)) {
+    // X-major staging.  Piece p covers k rows 4 kq .. 4 kq + 3 of the step and x group xg (CE
+    // consecutive x): lanes take x groups fastest in runs of 8, then 8 k quads, so one load
+    // instruction of a wavefront reads eight full 128-byte lines, and each store step writes 4 k
+    // values (8 bytes; 16 for FP32) to rows x whose swizzled positions cover every LDS bank.
+    // Thread tid takes pieces tid + j THREADS.
+    auto piece = [&](int p, int& kq, int& xg) __attribute__((always_inline)) {
+        constexpr int KH = NKQ / 8;
+        const int rest = p >> 6;
+        kq = ((p >> 3) & 7) + 8 * (rest % KH);
+        xg = (p & 7) + 8 * (rest / KH);
+    };
+    auto load_x = [&](const Opnd& o, bool is_a, int xlim, int k0, auto& r) __attribute__((always_inline)) {
+        constexpr int NQ = sizeof(r) / sizeof(r[0]);
 #pragma unroll
-        for (int i = 0; i < CE; ++i) r[i] = make_uint4(0, 0, 0, 0);
-        const int bb = block_of(is_a);
-        if (bb >= NB) return;
-        const int kg = bb / (BM / CE), x = (bb % (BM / CE)) * CE;
-        if (x >= xlim) return;
-        const int64_t xo = x_outer(is_a, x);
+        for (int j = 0; j < NQ; ++j) {
+            const int p = tid + j * THREADS;
+            if ((is_a ? NPA : NPB) % THREADS != 0 && p >= (is_a ? NPA : NPB)) continue;
 #pragma unroll
-        for (int i = 0; i < CE; ++i) {
-            const int k = k0 + kg * CE + i;
-            if (k < kn) r[i] = *reinterpret_cast<const uint4*>(opnd_row<T>(o, MODE == KROWS ? 0 : e, kb + k) + xo);
+            for (int i = 0; i < 4; ++i) r[j][i] = make_uint4(0, 0, 0, 0);
+            int kq, xg;
+            piece(p, kq, xg);
+            const int x = xg * CE;
+            if (x >= xlim) continue;
+            const int64_t xo = x_outer(is_a, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = k0 + kq * 4 + i;
+                if (k < kn)
+                    r[j][i] = *reinterpret_cast<const uint4*>(opnd_row<T>(o, MODE == KROWS ? 0 : e, kb + k) + xo);
+            }
         }
     };
-    auto store_x = [&](unsigned char* st, bool is_a, const uint4 (&r)[CE]) __attribute__((always_inline)) {
-        const int bb = block_of(is_a);
-        if (bb >= NB) return;
-        const int kg = bb / (BM / CE), x0 = (bb % (BM / CE)) * CE;
-        uint4 t[CE];
-        transpose_block(r, t);
+    auto store_x = [&](unsigned char* st, bool is_a, const auto& r) __attribute__((always_inline)) {
+        constexpr int NQ = sizeof(r) / sizeof(r[0]);
 #pragma unroll
-        for (int i = 0; i < CE; ++i) {
-            const int x = x0 + i;
-            *reinterpret_cast<uint4*>(st + x * ROWB + ((kg ^ swz(x)) * 16)) = t[i];
+        for (int j = 0; j < NQ; ++j) {
+            const int p = tid + j * THREADS;
+            if ((is_a ? NPA : NPB) % THREADS != 0 && p >= (is_a ? NPA : NPB)) continue;
+            int kq, xg;
+            piece(p, kq, xg);
+            const int x0 = xg * CE;
+            if constexpr (CE == 8) {
+                uint2 t[8];
+                transpose_quad(r[j], t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int x = x0 + i;
+                    *reinterpret_cast<uint2*>(st + x * ROWB + (((kq >> 1) ^ swz(x)) * 16) + (kq & 1) * 8) = t[i];
+                }
+            } else {
+                uint4 t[4];
+                transpose_block(r[j], t);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int x = x0 + i;
+                    *reinterpret_cast<uint4*>(st + x * ROWB + ((kq ^ swz(x)) * 16)) = t[i];
+                }
+            }
         }
     };
 
-    uint4 ka[AK ? KQ : 1], kbr[BK ? KQ : 1];
-    uint4 xa[AK ? 1 : CE], xb[BK ? 1 : CE];
-    auto load_step = [&](int kt) __attribute__((always_inline)) {
-        const int k0 = kt * BKE;
-        if constexpr (AK)
-            load_k(A, true, mlim, k0, ka);
-        else
-            load_x(A, true, mlim, k0, xa);
-        if constexpr (BK)
-            load_k(B, false, nlim, k0, kbr);
-        else
-            load_x(B, false, nlim, k0, xb);
+    // One step's operand pieces in registers; two sets, so that the loads of a step are issued
+    // two steps before they are written to LDS.
+    struct Regs {
+        uint4 ka[AK ? KQA : 1], kb[BK ? KQB : 1];
+        uint4 xa[AK ? 1 : XQA][4], xb[BK ? 1 : XQB][4];
     };
-    auto store_step = [&](int kt) __attribute__((always_inline)) {
+    auto load_a = [&](int kt, Regs& r) __attribute__((always_inline)) {
+        if constexpr (AK)
+            load_k(A, true, mlim, kt * BKE, r.ka);
+        else
+            load_x(A, true, mlim, kt * BKE, r.xa);
+    };
+    auto load_b = [&](int kt, Regs& r) __attribute__((always_inline)) {
+        if constexpr (BK)
+            load_k(B, false, nlim, kt * BKE, r.kb);
+        else
+            load_x(B, false, nlim, kt * BKE, r.xb);
+    };
+    auto store_a = [&](int kt, const Regs& r) __attribute__((always_inline)) {
         unsigned char* st = lds + (kt & 1) * (BM + BN) * ROWB;
         if constexpr (AK)
-            store_k(st, ka);
+            store_k(st, r.ka);
         else
-            store_x(st, true, xa);
+            store_x(st, true, r.xa);
+    };
+    auto store_b = [&](int kt, const Regs& r) __attribute__((always_inline)) {
+        unsigned char* st = lds + (kt & 1) * (BM + BN) * ROWB + BM * ROWB;
         if constexpr (BK)
-            store_k(st + BM * ROWB, kbr);
+            store_k(st, r.kb);
         else
-            store_x(st + BM * ROWB, false, xb);
+            store_x(st, false, r.xb);
+    };
+    auto load_step = [&](int kt, Regs& r) __attribute__((always_inline)) {
+        load_a(kt, r);
+        load_b(kt, r);
+    };
+    auto store_step = [&](int kt, const Regs& r) __attribute__((always_inline)) {
+        store_a(kt, r);
+        store_b(kt, r);
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
     const int fr = lane & 31, fh = lane >> 5;
     const int KT = (kn + BKE - 1) / BKE;
+    Regs even, odd;  // steps 0, 2, 4, ... and 1, 3, 5, ...
     if (KT > 0) {
-        load_step(0);
-        store_step(0);
+        load_step(0, even);
+        store_step(0, even);
     }
+    if (KT > 1) load_step(1, odd);
+    if (KT > 2) load_step(2, even);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) load_step(kt + 1);  // into registers, under this step's MFMAs
+    // Step kt: MFMAs from LDS stage kt & 1; step kt + 1 (in `next`, loaded two steps ago) goes to
+    // the other stage (last read in step kt - 1) between the MFMA groups -- A after the first, B
+    // after the second -- each followed by the loads of step kt + 3 into the registers it freed,
+    // so that the staging work overlaps the matrix cores instead of following them.
+    auto step = [&](int kt, Regs& next) __attribute__((always_inline)) {
         const unsigned char* st = lds + (kt & 1) * (BM + BN) * ROWB;
-        const unsigned char* sa = st + (wm * 64 + fr) * ROWB;
-        const unsigned char* sb = st + BM * ROWB + (wn * 64 + fr) * ROWB;
+        const unsigned char* sa = st + (wm * TM + fr) * ROWB;
+        const unsigned char* sb = st + BM * ROWB + (wn * TN + fr) * ROWB;
 #pragma unroll
         for (int ks = 0; ks < NCH / 2; ++ks) {
             const int off = ((ks * 2 + fh) ^ swz(fr)) * 16;
-            frag fa[2], fb[2];
+            frag fa[FM], fb[FN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const frag*>(sa + i * 32 * ROWB + off);
+            for (int i = 0; i < FM; ++i) fa[i] = *reinterpret_cast<const frag*>(sa + i * 32 * ROWB + off);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const frag*>(sb + j * 32 * ROWB + off);
+            for (int j = 0; j < FN; ++j) fb[j] = *reinterpret_cast<const frag*>(sb + j * 32 * ROWB + off);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = Mma<T>::run(fb[j], fa[i], acc[i][j]);
+                for (int j = 0; j < FN; ++j) acc[i][j] = Mma<T>::run(fb[j], fa[i], acc[i][j]);
+            if (ks == 0) {
+                if (kt + 1 < KT) store_a(kt + 1, next);
+                if (kt + 3 < KT) load_a(kt + 3, next);
+            } else if (ks == 1) {
+                if (kt + 1 < KT) store_b(kt + 1, next);
+                if (kt + 3 < KT) load_b(kt + 3, next);
+            }
         }
-        if (kt + 1 < KT) store_step(kt + 1);  // the other stage: last read in step kt - 1
         __syncthreads();
+    };
+    for (int kt = 0; kt < KT; kt += 2) {
+        step(kt, odd);
+        if (kt + 1 < KT) step(kt + 1, even);
     }
 
     // ---- epilogue: lane holds row m = fr of each 32-row block, columns 8 (v / 4) + 4 fh + v % 4 ----
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int ml = wm * 64 + i * 32 + fr;
+    for (int i = 0; i < FM; ++i) {
+        const int ml = wm * TM + i * 32 + fr;
         if (ml >= mlim) continue;
         const int64_t crow = MODE == ROWS ? row0 + ml : (int64_t)e * M + m0 + ml;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int nl = wn * 64 + j * 32 + 8 * q + 4 * fh;
+                const int nl = wn * TN + j * 32 + 8 * q + 4 * fh;
                 if (nl >= nlim) continue;  // N is a multiple of 4: a run of 4 is wholly in or out
                 const int n = n0 + nl;
                 const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
@@ -381,17 +462,28 @@ size_t experts_backward_workspace_bytes(int64_t E, int64_t I, rudnn_moe_dtype dt
 
 namespace {
 
+// Tiles: products over the dispatched rows (ROWS) and the weight gradients (KROWS).
+#ifndef RUDNN_BWD_ROWS_TILE
+#define RUDNN_BWD_ROWS_TILE 256, 256, 2, 4
+#endif
+#ifndef RUDNN_BWD_KROWS_TILE
+#define RUDNN_BWD_KROWS_TILE 256, 256, 2, 4
+#endif
+typedef bwd::Cfg<RUDNN_BWD_ROWS_TILE> RowsCfg;
+typedef bwd::Cfg<RUDNN_BWD_KROWS_TILE> KRowsCfg;
+
 template <typename T, int MODE, int EPI, bool AK, bool BK>
 void gemm(bwd::Opnd A, bwd::Opnd B, int M, int N, int K, int E, bwd::Plan plan, const int32_t* offsets, int rows,
           bwd::Epi ep, rudnn_moe_kernel kid, hipStream_t s) {
-    const int NT = (N + bwd::BN - 1) / bwd::BN, MT = (M + bwd::BM - 1) / bwd::BM;
-    const int64_t blocks = MODE == bwd::ROWS ? ((int64_t)rows / bwd::BM + E) * NT : (int64_t)E * MT * NT;
+    typedef typename std::conditional<MODE == bwd::ROWS, RowsCfg, KRowsCfg>::type C;
+    const int NT = (N + C::BN - 1) / C::BN, MT = (M + C::BM - 1) / C::BM;
+    const int64_t blocks = MODE == bwd::ROWS ? ((int64_t)rows / C::BM + E) * NT : (int64_t)E * MT * NT;
     if (blocks <= 0) return;
-    static const hipError_t attr = hipFuncSetAttribute((const void*)bwd::gemm_kernel<T, MODE, EPI, AK, BK>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, bwd::LDS_BYTES);
+    static const hipError_t attr = hipFuncSetAttribute((const void*)bwd::gemm_kernel<T, C, MODE, EPI, AK, BK>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     (void)attr;
     timing_before(kid, s);
-    bwd::gemm_kernel<T, MODE, EPI, AK, BK><<<dim3((unsigned)blocks), dim3(bwd::THREADS), bwd::LDS_BYTES, s>>>(
+    bwd::gemm_kernel<T, C, MODE, EPI, AK, BK><<<dim3((unsigned)blocks), dim3(C::THREADS), C::LDS_BYTES, s>>>(
         A, B, M, N, K, E, plan, offsets, rows, NT, MT, ep);
     timing_after(kid, s);
 }
@@ -409,7 +501,7 @@ void run(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int
                       : (float*)((unsigned char*)pl + align_up(sizeof(int32_t) * (size_t)(3 * E + 1)));
     bwd::Plan plan{pl, pl + E, pl + 2 * E};
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_PLAN, s);
-    bwd::plan_kernel<<<1, 1024, 0, s>>>(offsets, E, R, pl, pl + E, pl + 2 * E);
+    bwd::plan_kernel<<<1, 1024, 0, s>>>(offsets, E, R, RowsCfg::BM, pl, pl + E, pl + 2 * E);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_PLAN, s);
     const int NOSPLIT = 0x7fffffff;
     const int64_t IH = (int64_t)I * H;
