@@ -10,12 +10,12 @@
 //
 // One MFMA kernel serves all five products: C[m, n] = sum_k A(m, k) B(n, k) on BM x BN tiles
 // (256 x 256, eight wavefronts of 128 x 64), K staged 128 bytes per row (v_mfma_f32_32x32x16 for
-// BF16/F16, 32x32x2f32 for FP32).  An operand is either "K-major" (k contiguous: staged as 16-byte pieces)
-// or "X-major" (its row/column index contiguous): a thread then loads 4 rows of k by CE
-// consecutive x (CE = elements per 16 bytes), transposes them in registers and stores CE runs
-// of 4 k values into the [x][k] LDS tile.  The operand tiles go through registers (two sets): the
-// loads of step k+2 are issued while step k computes; step k+1, loaded during step k-1, is written
-// to the other LDS stage after step k's MFMAs.
+// BF16/F16, 32x32x2f32 for FP32).  An operand is either "K-major" (k contiguous: staged as
+// 16-byte pieces) or "X-major" (its row/column index contiguous): a thread then loads 4 rows of k
+// by CE consecutive x (CE = elements per 16 bytes), transposes them in registers and stores CE
+// runs of 4 k values into the [x][k] LDS tile.  The operand tiles go through registers (two
+// sets): during step k, step k+1 (loaded during step k-1) is written to the other LDS stage
+// between the first MFMA groups, and the loads of step k+3 go out into the registers it freed.
 // Two operand sources may be stacked along the operand's outer index (gate over up).
 // Grouping: ROWS tiles the expert's rows along M (a device-side plan of m-tiles per expert);
 // KROWS uses the expert's rows as the contraction axis, every (expert, m, n) tile (an expert
