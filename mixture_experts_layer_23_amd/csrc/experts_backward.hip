@@ -14,7 +14,7 @@
 // 16-byte pieces) or "X-major" (its row/column index contiguous): a thread then loads 4 rows of k
 // by CE consecutive x (CE = elements per 16 bytes), transposes them in registers and stores CE
 // runs of 4 k values into the [x][k] LDS tile.  The operand tiles go through registers (two
-// sets): during step k, step k+1 (loaded during step k-1) is written to the other LDS stage
+// sets): during step k, step k+1 (loaded during step k-2) is written to the other LDS stage
 // between the first MFMA groups, and the loads of step k+3 go out into the registers it freed.
 // Two operand sources may be stacked along the operand's outer index (gate over up).
 // Grouping: ROWS tiles the expert's rows along M (a device-side plan of m-tiles per expert);
