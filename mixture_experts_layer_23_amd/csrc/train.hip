@@ -15,8 +15,9 @@
 //
 // combine_backward (one wavefront per token): dexpert[map[t,j]] = dtype(w[t,j] * dout[t]) and
 // dweights[t,j] = sum_h dout[t,h] * y[map[t,j],h] in FP32 (lane partial sums, then a wavefront
-// sum).  A token with a map entry outside [0, rows) gets NaN dweights and no dexpert row for
-// that entry.  HBM per token: k*H*s (y) + H*s (dout) read, k*H*s written.
+// sum; for k <= 8 every lane issues the dout vector and all k row vectors of an iteration before
+// the arithmetic).  A token with a map entry outside [0, rows) gets NaN dweights and no dexpert
+// row for that entry.  HBM per token: k*H*s (y) + H*s (dout) read, k*H*s written.
 //
 // dispatch_backward (one wavefront per token and 1 KiB piece of the row): dinput[t] =
 // dtype(sum_j ddispatched[map[t,j]]), FP32, j ascending, no weights; NaN row for an invalid
@@ -160,7 +161,10 @@ __device__ __forceinline__ u32x4 pack16(const float (&f)[N]) {
     return v;
 }
 
-template <typename T, typename WT>
+// KMAX > 0: k <= KMAX known at compile time, so each lane issues the dout vector and all k expert
+// row vectors of an iteration before the arithmetic (the rows read once, streamed past the
+// caches); KMAX == 0: any k, one slot at a time.
+template <typename T, typename WT, int KMAX>
 __global__ __launch_bounds__(256) void combine_backward_kernel(const u32x4* __restrict__ y,
                                                                const int32_t* __restrict__ map,
                                                                const WT* __restrict__ w,
@@ -180,32 +184,70 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const u32x4* __re
     const bool ok_me = my_row >= 0 && my_row < rows;
     const bool bad = __ballot(lane < k && !ok_me) != 0;
     float part = 0.f;  // lane j < k ends with dweights[t, j]
-    for (int j = 0; j < k; ++j) {
-        const int r = readlane(my_row, j);
-        const float wj = readlane(my_w, j);
-        const bool ok = r >= 0 && r < rows;  // wave-uniform
-        float acc = 0.f;
+    if constexpr (KMAX > 0) {
+        float acc[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) acc[j] = 0.f;
         for (int64_t i = lane; i < row_vecs; i += 64) {
-            float g[N], o[N];
-            unpack16<T, N>(dout[t * row_vecs + i], g);
-            if (ok) {
-                float yy[N];
-                unpack16<T, N>(y[(int64_t)r * row_vecs + i], yy);
+            const u32x4 gv = dout[t * row_vecs + i];
+            u32x4 v[KMAX];
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                const int r = readlane(my_row, j);  // wave-uniform
+                if (j < k && r >= 0 && r < rows) v[j] = __builtin_nontemporal_load(y + (int64_t)r * row_vecs + i);
+            }
+            float g[N];
+            unpack16<T, N>(gv, g);
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                const int r = readlane(my_row, j);
+                if (!(j < k && r >= 0 && r < rows)) continue;
+                const float wj = readlane(my_w, j);
+                float yy[N], o[N];
+                unpack16<T, N>(v[j], yy);
 #pragma unroll
                 for (int q = 0; q < N; ++q) {
-                    acc += g[q] * yy[q];
+                    acc[j] += g[q] * yy[q];
                     o[q] = wj * g[q];
                 }
                 dexp[(int64_t)r * row_vecs + i] = pack16<T, N>(o);
             }
         }
-        acc = wave_sum(acc);
-        if (lane == j) part = acc;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (j >= k) break;
+            const float sj = wave_sum(acc[j]);
+            if (lane == j) part = sj;
+        }
+    } else {
+        for (int j = 0; j < k; ++j) {
+            const int r = readlane(my_row, j);
+            const float wj = readlane(my_w, j);
+            const bool ok = r >= 0 && r < rows;  // wave-uniform
+            float acc = 0.f;
+            for (int64_t i = lane; i < row_vecs; i += 64) {
+                float g[N], o[N];
+                unpack16<T, N>(dout[t * row_vecs + i], g);
+                if (ok) {
+                    float yy[N];
+                    unpack16<T, N>(y[(int64_t)r * row_vecs + i], yy);
+#pragma unroll
+                    for (int q = 0; q < N; ++q) {
+                        acc += g[q] * yy[q];
+                        o[q] = wj * g[q];
+                    }
+                    dexp[(int64_t)r * row_vecs + i] = pack16<T, N>(o);
+                }
+            }
+            acc = wave_sum(acc);
+            if (lane == j) part = acc;
+        }
     }
     if (lane < k) dw[t * k + lane] = bad ? __builtin_nanf("") : part;
 }
 
-template <typename T>
+// KMAX as in combine_backward_kernel: all k row vectors loaded before the sum.
+template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void dispatch_backward_kernel(const u32x4* __restrict__ d,
                                                                 const int32_t* __restrict__ map, int64_t T_, int k,
                                                                 int64_t rows, int64_t row_vecs, int pieces,
@@ -222,12 +264,26 @@ __global__ __launch_bounds__(256) void dispatch_backward_kernel(const u32x4* __r
     float acc[N];
 #pragma unroll
     for (int q = 0; q < N; ++q) acc[q] = bad ? __builtin_nanf("") : 0.f;
-    if (!bad) {
-        for (int j = 0; j < k; ++j) {
-            float v[N];
-            unpack16<T, N>(d[(int64_t)readlane(my_row, j) * row_vecs + i], v);
+    if (!bad && KMAX > 0) {
+        u32x4 v[KMAX > 0 ? KMAX : 1];
 #pragma unroll
-            for (int q = 0; q < N; ++q) acc[q] += v[q];
+        for (int j = 0; j < (KMAX > 0 ? KMAX : 1); ++j)
+            if (j < k) v[j] = __builtin_nontemporal_load(d + (int64_t)readlane(my_row, j) * row_vecs + i);
+#pragma unroll
+        for (int j = 0; j < (KMAX > 0 ? KMAX : 1); ++j) {
+            if (j < k) {
+                float f[N];
+                unpack16<T, N>(v[j], f);
+#pragma unroll
+                for (int q = 0; q < N; ++q) acc[q] += f[q];
+            }
+        }
+    } else if (!bad) {
+        for (int j = 0; j < k; ++j) {
+            float f[N];
+            unpack16<T, N>(d[(int64_t)readlane(my_row, j) * row_vecs + i], f);
+#pragma unroll
+            for (int q = 0; q < N; ++q) acc[q] += f[q];
         }
     }
     out[t * row_vecs + i] = pack16<T, N>(acc);
@@ -237,8 +293,19 @@ template <typename DT, typename WT>
 static void launch_cb(const void* y, const int32_t* map, const void* w, const void* dout, int64_t T, int64_t k,
                       int64_t H, int64_t rows, void* dexp, float* dw, hipStream_t s) {
     const int64_t row_vecs = H * (int64_t)sizeof(DT) / 16;
-    combine_backward_kernel<DT, WT><<<(unsigned)((T + 3) / 4), 256, 0, s>>>(
-        (const u32x4*)y, map, (const WT*)w, (const u32x4*)dout, T, (int)k, rows, row_vecs, (u32x4*)dexp, dw);
+    const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+    const u32x4 *yv = (const u32x4*)y, *gv = (const u32x4*)dout;
+    const WT* wt = (const WT*)w;
+    u32x4* ov = (u32x4*)dexp;
+    const int ki = (int)k;
+    if (k <= 2)
+        combine_backward_kernel<DT, WT, 2><<<grid, block, 0, s>>>(yv, map, wt, gv, T, ki, rows, row_vecs, ov, dw);
+    else if (k <= 4)
+        combine_backward_kernel<DT, WT, 4><<<grid, block, 0, s>>>(yv, map, wt, gv, T, ki, rows, row_vecs, ov, dw);
+    else if (k <= 8)
+        combine_backward_kernel<DT, WT, 8><<<grid, block, 0, s>>>(yv, map, wt, gv, T, ki, rows, row_vecs, ov, dw);
+    else
+        combine_backward_kernel<DT, WT, 0><<<grid, block, 0, s>>>(yv, map, wt, gv, T, ki, rows, row_vecs, ov, dw);
 }
 
 template <typename DT>
@@ -270,8 +337,18 @@ static void launch_db(const void* d, const int32_t* map, int64_t T, int64_t k, i
     const int64_t row_vecs = H * (int64_t)sizeof(DT) / 16;
     const int pieces = (int)((row_vecs + 63) / 64);
     const int64_t waves = T * pieces;
-    dispatch_backward_kernel<DT><<<(unsigned)((waves + 3) / 4), 256, 0, s>>>((const u32x4*)d, map, T, (int)k, rows,
-                                                                          row_vecs, pieces, (u32x4*)out);
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    const u32x4* dv = (const u32x4*)d;
+    u32x4* ov = (u32x4*)out;
+    const int ki = (int)k;
+    if (k <= 2)
+        dispatch_backward_kernel<DT, 2><<<grid, block, 0, s>>>(dv, map, T, ki, rows, row_vecs, pieces, ov);
+    else if (k <= 4)
+        dispatch_backward_kernel<DT, 4><<<grid, block, 0, s>>>(dv, map, T, ki, rows, row_vecs, pieces, ov);
+    else if (k <= 8)
+        dispatch_backward_kernel<DT, 8><<<grid, block, 0, s>>>(dv, map, T, ki, rows, row_vecs, pieces, ov);
+    else
+        dispatch_backward_kernel<DT, 0><<<grid, block, 0, s>>>(dv, map, T, ki, rows, row_vecs, pieces, ov);
 }
 
 hipError_t launch_dispatch_backward(const void* d, rudnn_moe_dtype dt, const int32_t* map, int64_t T, int64_t k,

@@ -291,6 +291,12 @@ CHAIN_CASES = {
     "bf16_softmax_renorm": (BWD_LAYERS["bf16_small"], "softmax", True, 1.0),
     "f16_softmax_plain": (BWD_LAYERS["f16_ragged"], "softmax", False, 1.0),
     "f32_sigmoid_scaled": (BWD_LAYERS["f32_tiny"], "sigmoid", True, 2.5),
+    # one expert, top_k 1: a dense SwiGLU MLP whose router weight is 1 (renormalised softmax)
+    "bf16_one_expert": (Workload("ch_dense", 130, 128, 256, 1, 1, "bf16", "bf16", (True,), None, 1005), "softmax",
+                        True, 1.0),
+    # top_k = E: every expert takes every token
+    "bf16_all_experts": (Workload("ch_all", 70, 128, 128, 4, 4, "bf16", "bf16", (False,), None, 1006), "softmax",
+                         False, 1.0),
 }
 
 
@@ -343,3 +349,6 @@ def test_training_chain(name):
     assert_close(dup, rdu, tol, "dup")
     assert_close(ddown, rdd, tol, "ddown")
     assert_close(dlogits, rdl, w.dtype, "dlogits")
+    if w.E == 1 and renorm:
+        # a lone selected expert under renormalisation: weight exactly scale, zero logits gradient
+        assert torch.all(wts == scale) and not dlogits.float().any()
