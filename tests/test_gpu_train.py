@@ -294,6 +294,9 @@ CHAIN_CASES = {
     # one expert, top_k 1: a dense SwiGLU MLP whose router weight is 1 (renormalised softmax)
     "bf16_one_expert": (Workload("ch_dense", 130, 128, 256, 1, 1, "bf16", "bf16", (True,), None, 1005), "softmax",
                         True, 1.0),
+    # NaN, +inf and all -inf logit rows (NaN weights) and tied rows, through every backward step
+    "bf16_special_rows": (Workload("ch_special", 200, 128, 256, 8, 2, "bf16", "bf16", (True,), None, 1007,
+                                   special=(1, 1, 1, 1, 2, 2, 2)), "softmax", True, 1.0),
     # top_k = E: every expert takes every token
     "bf16_all_experts": (Workload("ch_all", 70, 128, 128, 4, 4, "bf16", "bf16", (False,), None, 1006), "softmax",
                          False, 1.0),
