@@ -388,7 +388,8 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(Opnd A, Opnd B, int M,
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = Mma<T>::run(fb[j], fa[i], acc[i][j]);
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = MODE == ROWS ? Mma<T>::run(fb[j], fa[i], acc[i][j]) : Mma<T>::run(fa[i], fb[j], acc[i][j]);
             if (ks == 0) {
                 if (kt + 1 < KT) store_a(kt + 1, next);
                 if (kt + 3 < KT) load_a(kt + 3, next);
@@ -404,6 +405,26 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(Opnd A, Opnd B, int M,
         if (kt + 1 < KT) step(kt + 1, even);
     }
 
+    if constexpr (MODE == KROWS) {
+        // Weight gradients (FP32): the operands went in token fragment first, so lane l holds
+        // column l % 32 and rows 8 (v / 4) + 4 fh + v % 4 of each block; a store instruction writes
+        // two whole 128-byte row pieces.
+        static_assert(EPI == EPI_F32, "weight gradients are FP32");
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int nl = wn * TN + j * 32 + fr;
+                if (nl >= nlim) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int ml = wm * TM + i * 32 + 8 * (v / 4) + 4 * fh + v % 4;
+                    if (ml < mlim)
+                        reinterpret_cast<float*>(ep.c)[((int64_t)e * M + m0 + ml) * ep.ldc + n0 + nl] = acc[i][j][v];
+                }
+            }
+        return;
+    }
     // ---- epilogue: lane holds row m = fr of each 32-row block, columns 8 (v / 4) + 4 fh + v % 4 ----
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
