@@ -11,10 +11,11 @@
 //   down     grouped GEMM, N = H, K = I.
 // BF16/F16: v_mfma_f32_32x32x16_{bf16,f16} with FP32 accumulators.  A block of eight wavefronts
 // (4 along M x 2 along N, two per SIMD) owns a 256-row tile: gate_up 192 columns of gate + 192 of
-// up (384 accumulator columns, 192 registers per lane), down 256 columns.  K is staged 64 at a time: tokens and weight rows go straight from global memory
-// into LDS with global_load_lds_dwordx4 (no register staging), in an XOR-swizzled layout that
-// keeps the MFMA operand reads free of bank conflicts.  Two LDS stages: the copies of step k+1
-// are issued under the MFMAs of step k; one barrier per step.
+// up (384 accumulator columns, 192 registers per lane), down 256 columns.  K is staged 64 at a
+// time: tokens and weight rows go straight from global memory into LDS with buffer_load_dwordx4
+// ... lds (no register staging), in an XOR-swizzled layout that keeps the MFMA operand reads
+// free of bank conflicts.  Two LDS stages: the copies of step k+1 are issued under the MFMAs of
+// step k; one barrier per step.
 // F32: a plain FP32 FMA tile (64 x 64) on the same tile plan -- no reduced-precision step.
 // Training (section 12, forward_dispatched_training): the gate_up epilogue also stores the FP32
 // pre-activations [g | u] of every row as the backward's cache (a kernel variant of its own, so
@@ -22,8 +23,11 @@
 //
 // Tile order.  Tiles of expert e are enumerated in groups of GROUP_N n-tiles, all m-tiles of a
 // group together, so tiles that run side by side share both their weight columns and their
-// token rows; block i takes tile i.  (Dealing contiguous shares of the list to the 8 XCDs
-// measured slower on the Mixtral-shaped layer.)  The grid is sized for the worst case
+// token rows.  Workgroups reach the 8 XCDs round-robin (block b on XCD b % 8); within each
+// round of CUs blocks, XCD x takes the contiguous eighth x of the round's units, so the tiles
+// that share operands meet in one XCD's L2 (on the Mixtral-shaped layer this cut the gate/up
+// fetches from L2 misses by 14% and the down ones by 36%).  (Dealing each XCD a contiguous share
+// of the whole list instead measured slower.)  The grid is sized for the worst case
 // (floor(rows / BM) + min(E, rows) m-tiles, plus the split units below); blocks beyond the real
 // count exit at once.
 //
@@ -152,7 +156,18 @@ __device__ __forceinline__ bool find_unit(const Plan& plan, int E, int N, int KT
     const int NT = (N + BN - 1) / BN;
     const int64_t tiles = load_plan(plan, E, NT, s_mt);
     const Split sp = split_plan(tiles, KT, cus);
-    const int64_t U = blockIdx.x;
+    int64_t U = blockIdx.x;
+    {
+        // XCD x runs blocks x, x + 8, ...; within each full round of `cus` blocks it takes the
+        // contiguous slice [x * cus/8, (x+1) * cus/8) of the round's units (a bijection on the
+        // round; a last, partial round keeps block order).
+        const int64_t units = sp.full + (int64_t)sp.R * sp.S;
+        if (cus % 8 == 0 && U < units / cus * cus) {
+            const int64_t r = U / cus;
+            const int j = (int)(U - r * cus);
+            U = r * cus + (int64_t)(j % 8) * (cus / 8) + j / 8;
+        }
+    }
     int64_t L;
     if (U < sp.full) {
         L = U, u.kb = 0, u.ke = KT, u.slot = -1;
@@ -239,17 +254,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Staging.  A tile step copies BM rows of tokens and NB = NSETS * BN weight rows, BK elements
-// each, straight from global memory into swizzled LDS (global_load_lds_dwordx4: lane i of a
+// each, straight from global memory into swizzled LDS (buffer_load_dwordx4 ... lds: lane i of a
 // wave writes 16 bytes at the wave's LDS base + 16 i, so one wave instruction fills 1 KiB =
-// 1024 / ROWB rows).  The copies of one step are numbered as slots (token groups first, then
+// 1024 / ROWB rows).  The buffer form, not global_load_lds, because the compiler counts the
+// global form against the LDS-read counter as well and then waits for every outstanding LDS
+// read (lgkmcnt 0) before each MFMA group; with buffer copies it waits for exactly the operand
+// fragments each MFMA needs.  The copies of one step are numbered as slots (token groups first, then
 // weight groups) and dealt to the wavefronts round-robin, so each wave owns SLOTS copies.
 // A row past the end of its matrix re-reads the last row (such rows are never stored); in the
 // last step of a K that is not a multiple of BK, chunks at k >= K are zeroed instead of copied.
 // Offsets from a tile's base pointers are 32-bit: a tile spans at most a few MB of a matrix.
 struct StageSrc {
-    const unsigned char* a;   // token rows of the tile
-    const unsigned char* b0;  // weight rows (gate, or down)
-    const unsigned char* b1;  // up weight rows (gate_up only)
+    __amdgpu_buffer_rsrc_t ra;   // token rows of the tile
+    __amdgpu_buffer_rsrc_t rb0;  // weight rows (gate, or down)
+    __amdgpu_buffer_rsrc_t rb1;  // up weight rows (gate_up only)
     int ld_bytes, last_a, last_b, K, esize;
 };
 
@@ -261,14 +279,14 @@ __device__ __forceinline__ void stage_slot(int slot, unsigned char* st, const St
     static_assert(GA % NWAVES == 0 && GB % NWAVES == 0, "each region splits evenly over the wavefronts");
     const int gi = wave + slot * NWAVES;  // global group index over A, B0, B1
     // the region depends on the slot only (a constant once the slot loop is unrolled)
-    const unsigned char* base;
+    __amdgpu_buffer_rsrc_t rs;
     int g, last;
     if (slot < GA / NWAVES) {
-        base = src.a, g = gi, last = src.last_a;
+        rs = src.ra, g = gi, last = src.last_a;
     } else if (NSETS == 1 || slot < (GA + GB) / NWAVES) {
-        base = src.b0, g = gi - GA, last = src.last_b;
+        rs = src.rb0, g = gi - GA, last = src.last_b;
     } else {
-        base = src.b1, g = gi - GA - GB, last = src.last_b;
+        rs = src.rb1, g = gi - GA - GB, last = src.last_b;
     }
     // A group of token rows wholly past the tile's last row is not copied: those LDS rows only
     // feed output rows that are never stored (each output row depends on its own token row).
@@ -280,8 +298,8 @@ __device__ __forceinline__ void stage_slot(int slot, unsigned char* st, const St
     const int rr = r < last ? r : last;
     unsigned char* dst = st + gi * 1024;
     if (!TAIL || kk < src.K)
-        __builtin_amdgcn_global_load_lds((const void*)(base + (uint32_t)(rr * src.ld_bytes + kk * src.esize)),
-                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16,
+                                                 rr * src.ld_bytes + kk * src.esize, 0, 0, 0);
     else
         *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
 }
@@ -302,6 +320,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     constexpr int NWAVES = WM * WN;
     constexpr int NSETS = DUAL ? 2 : 1;
     constexpr int NB = NSETS * BN;          // weight rows staged per tile
+    constexpr bool ROLL = DUAL;             // weight-fragment-outer MFMA order (see step)
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int KS = BK / 16;             // MFMA steps per staged tile
@@ -328,14 +347,23 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     const int wm = wave / WN, wn = wave % WN;
     const int nrows = tile.nrows, n0 = tile.n0;
     StageSrc src;
-    src.a = reinterpret_cast<const unsigned char*>(A + (int64_t)tile.row0 * K);
-    src.b0 = reinterpret_cast<const unsigned char*>(B0 + ((int64_t)tile.e * N + n0) * K);
-    src.b1 = DUAL ? reinterpret_cast<const unsigned char*>(B1 + ((int64_t)tile.e * N + n0) * K) : nullptr;
     src.ld_bytes = K * (int)sizeof(T);
     src.last_a = nrows - 1;
     src.last_b = N - 1 - n0;
     src.K = K;
     src.esize = (int)sizeof(T);
+    {
+        // raw buffers over exactly the rows a tile may read (the copies clamp to them anyway)
+        constexpr int GFX9_RSRC_WORD3 = 0x00020000;  // 32-bit data format, no swizzle
+        const int b_bytes = min(src.last_b + 1, BN) * src.ld_bytes;
+        src.ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)tile.row0 * K), (short)0,
+                                                   nrows * src.ld_bytes, GFX9_RSRC_WORD3);
+        src.rb0 = __builtin_amdgcn_make_buffer_rsrc((void*)(B0 + ((int64_t)tile.e * N + n0) * K), (short)0, b_bytes,
+                                                    GFX9_RSRC_WORD3);
+        src.rb1 = DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)(B1 + ((int64_t)tile.e * N + n0) * K), (short)0,
+                                                           b_bytes, GFX9_RSRC_WORD3)
+                       : src.rb0;
+    }
     const bool ragged_k = (K % BK) != 0;
 
     // all copies of step kt (the tail form zeroes chunks past K)
@@ -369,12 +397,63 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
 
     // The MFMAs of one staged step.  Operand fragments of MFMA step ks+1 are read from LDS while
     // the MFMAs of step ks run; with ISSUE, the copies of step kt_next are spread over the MFMA
-    // steps.  A scheduling fence after each MFMA step keeps at most two fragment sets live.
+    // steps.  gate_up (ROLL) has no registers left for a second set of weight fragments: its
+    // MFMAs run weight-fragment-outer and each weight fragment is reloaded for step ks+1 right
+    // after its FM MFMAs (a fence after each group keeps that order).  down double-buffers all
+    // fragments, with a fence after each MFMA step.
     auto step = [&](int kt, auto with_mfma, auto with_issue, int kt_next) __attribute__((always_inline)) {
         const unsigned char* st = smem_raw + (kt % STAGES) * STAGE_BYTES;
         unsigned char* st_next = smem_raw + (kt_next % STAGES) * STAGE_BYTES;
         const unsigned char* a = st + (wm * WTM) * ROWB;
         const unsigned char* b = st + A_BYTES + (wn * WTN) * ROWB;
+        if constexpr (ROLL) {
+        // Weight-fragment-outer order: each weight fragment feeds its FM MFMAs and its register is
+        // then reloaded with the next MFMA step's fragment at once, so every LDS read has about a
+        // whole MFMA step to land while only the token fragments are double-buffered (the
+        // accumulators leave no room for a second set of weight fragments).
+        frag fa[2][FM], fb[NSETS][FN];
+        auto fetch_a = [&](int ks, int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[buf][i] = *reinterpret_cast<const frag*>(a + i * 32 * ROWB + lane_off[ks]);
+        };
+        auto fetch_b = [&](int ks, int s, int j) __attribute__((always_inline)) {
+            fb[s][j] = *reinterpret_cast<const frag*>(b + (s * BN + j * 32) * ROWB + lane_off[ks]);
+        };
+        if constexpr (decltype(with_mfma)::value) {
+            fetch_a(0, 0);
+#pragma unroll
+            for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) fetch_b(0, s, j);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (decltype(with_issue)::value) {
+                // copies for the next step go out early: spread over the first DMA_SPREAD MFMA steps
+                constexpr int SP = RUDNN_DMA_SPREAD < KS ? RUDNN_DMA_SPREAD : KS;
+                if (ks < SP) {
+#pragma unroll
+                    for (int q = ks * SLOTS / SP; q < (ks + 1) * SLOTS / SP; ++q)
+                        stage_slot<Cfg, NSETS, NWAVES, false>(q, st_next, src, kt_next * BK, wave, lane);
+                }
+            }
+            if constexpr (decltype(with_mfma)::value) {
+                if (ks + 1 < KS) fetch_a(ks + 1, (ks + 1) & 1);
+#pragma unroll
+                for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                        for (int i = 0; i < FM; ++i)
+                            acc[s][i][j] = Mfma<T>::run(fb[s][j], fa[ks & 1][i], acc[s][i][j]);
+                        if (ks + 1 < KS) fetch_b(ks + 1, s, j);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        } else {
         frag fa[2][FM], fb[2][NSETS][FN];
         auto fetch = [&](int ks, int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -409,6 +488,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
                             acc[s][i][j] = Mfma<T>::run(fb[ks & 1][s][j], fa[ks & 1][i], acc[s][i][j]);
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
         }
     };
 
