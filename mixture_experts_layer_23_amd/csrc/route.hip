@@ -3,7 +3,8 @@
 // A group of G adjacent lanes owns one row of logits [T, E] (G = 1 .. 64, a power of two, so a
 // wavefront covers 64 / G rows); lane l of the group holds experts [l * NPER, (l + 1) * NPER),
 // so a wavefront's loads cover 64 / G consecutive rows contiguously.  The selection itself
-// (exact top-k on the logits, FP32 softmax of the winners) is route_row in route_select.hpp.
+// (exact top-k on the logits, FP32 softmax of the winners) is route_row in route_select.hpp, or
+// route_row_sorted (same results, less VALU work) for 16-bit logits in whole 16-byte lane chunks.
 // HBM traffic per row: E * sizeof(logits) read, k * (4 + sizeof(logits)) written.
 #include <type_traits>
 
@@ -45,7 +46,15 @@ __global__ __launch_bounds__(ROUTE_THREADS) void route_kernel(const LT* __restri
 #pragma unroll
         for (int s = 0; s < NPER; ++s) raw[s] = (live && e0 + s < E) ? x[s] : (R)0;
     }
-    route_row<LT, NPER, G>(raw, E, k, renorm, live, row, si, se, idx, w);
+    if constexpr (VEC && sizeof(R) == 2) {
+        // whole 16-byte lane chunks (E % NPER == 0): sorted per-lane lists (k is block-uniform)
+        if (NPER == 16 && k <= 8)
+            route_row_sorted<LT, NPER, G, (NPER == 16 ? 8 : NPER)>(raw, E, k, renorm, live, row, si, se, idx, w);
+        else
+            route_row_sorted<LT, NPER, G, NPER>(raw, E, k, renorm, live, row, si, se, idx, w);
+    } else {
+        route_row<LT, NPER, G>(raw, E, k, renorm, live, row, si, se, idx, w);
+    }
 }
 
 template <typename LT, int NPER, int G>

@@ -170,4 +170,139 @@ __device__ __forceinline__ void route_row(const typename RouteBits<LT>::raw (&ra
     }
 }
 
+// The same routing for 16-bit logits whose lanes hold whole NPER-element chunks (E % NPER == 0),
+// with less VALU work per row:
+//   * codes: ord = 0x8000 + |x| for x >= +0 and 0x8000 - |x| for x <= -0 (both zeros 0x8000),
+//     built two logits at a time with packed 16-bit integer operations; key = ord << 16 above
+//     the complemented id, as in make_key (ord differs from make_key's by a constant for
+//     negatives, which leaves the order unchanged);
+//   * NaN-row test from the lane's largest and smallest code: +inf or +NaN give ord >= 0x8000 +
+//     EXP, -NaN ord < 0x8000 - EXP, -inf exactly 0x8000 - EXP;
+//   * selection: each lane sorts its L largest keys once (a bitonic network; L = 8 takes the top
+//     8 of 16 by sorting both halves and merging), then every round takes the group maximum of
+//     the lanes' heads and the winning lane shifts its list by one.  Since keys are unique in a
+//     row, this yields the same k winners in the same order as the k rounds of route_row.
+template <typename LT>
+__device__ __forceinline__ float ord_logit(uint32_t key) {
+    const uint32_t ord = key >> 16;
+    const uint16_t b = ord >= 0x8000u ? (uint16_t)(ord - 0x8000u) : (uint16_t)(0x8000u | (0x8000u - ord));
+    LT v;
+    __builtin_memcpy(&v, &b, sizeof(v));
+    return to_f32(v);
+}
+
+// key[a] >= key[b] afterwards
+__device__ __forceinline__ void key_order(uint32_t& a, uint32_t& b) {
+    const uint32_t x = a, y = b;
+    a = max(x, y);
+    b = min(x, y);
+}
+
+// Bitonic sort, descending, of key[B .. B + N) (N a power of two).
+template <int B, int N, int NPER>
+__device__ __forceinline__ void key_sort(uint32_t (&key)[NPER]) {
+#pragma unroll
+    for (int kk = 2; kk <= N; kk <<= 1)
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    if ((i & kk) == 0)
+                        key_order(key[B + i], key[B + l]);
+                    else
+                        key_order(key[B + l], key[B + i]);
+                }
+            }
+}
+
+template <typename LT, int NPER, int G, int L>
+__device__ __forceinline__ void route_row_sorted(const uint16_t (&raw)[NPER], int E, int k, int renorm, bool live,
+                                                 int64_t row, uint32_t* si, float* se, uint32_t* __restrict__ idx,
+                                                 LT* __restrict__ w) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    typedef short ss2 __attribute__((ext_vector_type(2)));
+    static_assert(NPER % 2 == 0 && (L == NPER || (L == 8 && NPER == 16)), "list of the whole chunk or top 8 of 16");
+    constexpr uint32_t EXP = RouteBits<LT>::EXP, POS = 0x8000u + EXP, NEG = 0x8000u - EXP;
+    const int lane = lane_id(), l = lane % G, e0 = l * NPER;
+    const bool lane_in = e0 < E;  // whole chunks: a lane's entries are all in or all out
+    uint32_t key[NPER];
+    us2 omax = {0, 0}, omin = {0xffff, 0xffff};
+#pragma unroll
+    for (int p = 0; p < NPER / 2; ++p) {
+        us2 v;
+        __builtin_memcpy(&v, &raw[2 * p], sizeof(v));
+        const us2 neg = (us2)(((ss2)v) >> (ss2)15);  // 0xffff where the sign bit is set
+        const us2 mag = v & (us2)0x7fff;
+        const us2 ord = (us2)0x8000 + ((mag ^ neg) - neg);
+        omax = __builtin_elementwise_max(omax, ord);
+        omin = __builtin_elementwise_min(omin, ord);
+        key[2 * p] = lane_in ? (((uint32_t)ord.x << 16) | (0xffffu - (uint32_t)(e0 + 2 * p))) : 0u;
+        key[2 * p + 1] = lane_in ? (((uint32_t)ord.y << 16) | (0xffffu - (uint32_t)(e0 + 2 * p + 1))) : 0u;
+    }
+    const uint32_t hi = max((uint32_t)omax.x, (uint32_t)omax.y), lo = min((uint32_t)omin.x, (uint32_t)omin.y);
+    const bool nan_or_posinf = lane_in && (hi >= POS || lo < NEG);
+    const bool not_neginf = lane_in && !(hi == NEG && lo == NEG);
+    const int gshift = lane - l;  // first lane of the group
+    const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull);
+    const bool nan_row =
+        ((__ballot(nan_or_posinf) >> gshift) & gmask) != 0 || ((__ballot(not_neginf) >> gshift) & gmask) == 0;
+
+    if constexpr (L == NPER) {
+        key_sort<0, NPER>(key);
+    } else {  // top 8 of 16: sort both halves, keep the larger of key[i] and key[15 - i], merge
+        key_sort<0, 8>(key);
+        key_sort<8, 8>(key);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) key[i] = max(key[i], key[15 - i]);
+#pragma unroll
+        for (int j = 4; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((i ^ j) > i) key_order(key[i], key[i ^ j]);
+    }
+
+    float m = 0.f, den = 0.f;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t win = group_max_key<G>(key[0]);
+        const bool hit = key[0] == win;
+#pragma unroll
+        for (int p = 0; p < L - 1; ++p) key[p] = hit ? key[p + 1] : key[p];
+        key[L - 1] = hit ? 0u : key[L - 1];
+        const float xw = ord_logit<LT>(win);
+        if (j == 0) m = xw;
+        const float e = expf(xw - m);  // -inf logits give 0 exactly
+        den += e;
+        if (live && l == 0) {
+            si[j] = 0xffffu - (win & 0xffffu);
+            se[j] = e;
+        }
+    }
+    if (!renorm) {  // denominator over all experts
+        float sum = 0.f;
+        if (lane_in) {
+#pragma unroll
+            for (int s = 0; s < NPER; ++s) {
+                LT v;
+                __builtin_memcpy(&v, &raw[s], sizeof(v));
+                sum += expf(to_f32(v) - m);
+            }
+        }
+        den = group_sum<G>(sum);
+    }
+    __syncthreads();
+    if (live) {
+        for (int j = l; j < k; j += G) {
+            if (nan_row) {
+                idx[row * k + j] = (uint32_t)j;
+                w[row * k + j] = from_f32<LT>(__builtin_nanf(""));
+            } else {
+                idx[row * k + j] = si[j];
+                w[row * k + j] = from_f32<LT>(se[j] / den);
+            }
+        }
+    }
+}
+
 }  // namespace rudnn
