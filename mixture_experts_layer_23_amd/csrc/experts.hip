@@ -7,6 +7,8 @@
 // Both products contract over a contiguous axis of both operands ("TN" GEMMs).  Three kernels:
 //   plan     one block: clamps the device-side expert offsets to [0, rows], counts BM-row
 //            tiles per expert and their exclusive prefix (no host round trip, no sync);
+//   skinny   experts with at most SMALL_ROWS rows when a batch has few rows per expert
+//            (decode): weight rows streamed whole, FP32 FMAs (see skinny_gemm);
 //   gate_up  grouped GEMM, N = I, fused epilogue silu(g) * u (two accumulator sets per tile);
 //   down     grouped GEMM, N = H, K = I.
 // BF16/F16: v_mfma_f32_32x32x16_{bf16,f16} with FP32 accumulators.  A block of eight wavefronts
@@ -70,7 +72,7 @@ struct Plan {
 };
 
 __global__ __launch_bounds__(1024) void experts_plan_kernel(const int32_t* __restrict__ offsets, int E, int rows,
-                                                            int BM, Plan plan) {
+                                                            int BM, int small_rows, Plan plan) {
     __shared__ int scratch[17];
     const int e = threadIdx.x;
     int tiles = 0;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(1024) void experts_plan_kernel(const int32_t* __res
         const int n = max(b - a, 0);
         plan.row_begin[e] = a;
         plan.row_count[e] = n;
-        tiles = (n + BM - 1) / BM;
+        tiles = n > small_rows ? (n + BM - 1) / BM : 0;  // experts of <= small_rows rows: skinny_gemm
     }
     int total;
     const int excl = block_exclusive_scan(tiles, scratch, &total);
@@ -745,6 +747,125 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------
+// Experts with few rows (decode-shaped batches)
+// ---------------------------------------------------------------------------------------
+// With one to SMALL_ROWS rows per expert the products are a stream of weight rows.  The MFMA
+// tiles read them in 128-byte pieces, one piece per K step from each of hundreds of rows at
+// once; here a wavefront reads a weight row 1 KiB at a time (lane l: elements [512 c + 8 l, +8)
+// of chunk c), every chunk of its FR rows (per weight set) in flight together, and forms the dot
+// products with the expert's n token rows, staged once per block in LDS, in FP32 FMAs.  A
+// wavefront sum gives each (token row, output column); lane r stores token row r's value.  A
+// block covers FPB = 8 wavefronts x FR x IT output columns of one expert; blocks of other
+// experts exit at once.
+constexpr int SMALL_ROWS = 4;
+
+template <typename T>
+__device__ __forceinline__ void unpack8(uint4 q, float (&v)[8]) {
+    T t[8];
+    __builtin_memcpy(t, &q, sizeof(q));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = to_f32(t[i]);
+}
+
+template <typename T, bool DUAL, int JMAX, int FR, int IT>
+__global__ __launch_bounds__(512) void skinny_gemm(const T* __restrict__ A, const T* __restrict__ B0,
+                                                   const T* __restrict__ B1, T* __restrict__ C, int K, int N, int E,
+                                                   Plan plan, int blocks_per_expert) {
+    constexpr int NSETS = DUAL ? 2 : 1, NW = 8, FPB = NW * FR * IT;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    const int e = blockIdx.x / blocks_per_expert, b = blockIdx.x % blocks_per_expert;
+    if (e >= E) return;
+    const int n = plan.row_count[e];
+    if (n <= 0 || n > SMALL_ROWS) return;  // block-uniform
+    const int r0 = plan.row_begin[e];
+    const int kv = K / 8;  // 16-byte vectors per row (K is a multiple of 8)
+    uint4* xs = reinterpret_cast<uint4*>(smem_raw);  // [n][kv]
+    for (int q = threadIdx.x; q < n * kv; q += blockDim.x) {
+        const int r = q / kv, c = q - r * kv;
+        xs[q] = reinterpret_cast<const uint4*>(A + (int64_t)(r0 + r) * K)[c];
+    }
+    __syncthreads();
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int J = (K + 511) / 512;  // chunks per row, <= JMAX (checked by the host)
+    const T* Bs[2] = {B0, B1};
+    for (int it = 0; it < IT; ++it) {
+        const int f0 = b * FPB + (it * NW + wave) * FR;  // this wavefront's FR output columns
+        if (f0 >= N) break;                             // wave-uniform
+        uint4 wv[NSETS][FR][JMAX];
+#pragma unroll
+        for (int st = 0; st < NSETS; ++st)
+#pragma unroll
+            for (int fr = 0; fr < FR; ++fr)
+#pragma unroll
+                for (int j = 0; j < JMAX; ++j) {
+                    const int kk = j * 512 + lane * 8;
+                    wv[st][fr][j] = make_uint4(0, 0, 0, 0);
+                    if (j < J && kk < K && f0 + fr < N)
+                        wv[st][fr][j] = *reinterpret_cast<const uint4*>(Bs[st] + ((int64_t)e * N + f0 + fr) * K + kk);
+                }
+        float acc[NSETS][FR][SMALL_ROWS] = {};
+#pragma unroll
+        for (int j = 0; j < JMAX; ++j) {
+            const int kk = j * 512 + lane * 8;
+            if (j >= J) break;
+            if (kk >= K) continue;  // this lane's chunk is past the row's end (zero)
+            float wf[NSETS][FR][8];
+#pragma unroll
+            for (int st = 0; st < NSETS; ++st)
+#pragma unroll
+                for (int fr = 0; fr < FR; ++fr) unpack8<T>(wv[st][fr][j], wf[st][fr]);
+#pragma unroll
+            for (int r = 0; r < SMALL_ROWS; ++r) {
+                if (r >= n) break;
+                float x[8];
+                unpack8<T>(xs[r * kv + kk / 8], x);
+#pragma unroll
+                for (int st = 0; st < NSETS; ++st)
+#pragma unroll
+                    for (int fr = 0; fr < FR; ++fr)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) acc[st][fr][r] = fmaf(wf[st][fr][i], x[i], acc[st][fr][r]);
+            }
+        }
+#pragma unroll
+        for (int fr = 0; fr < FR; ++fr) {
+            if (f0 + fr >= N) break;
+#pragma unroll
+            for (int r = 0; r < SMALL_ROWS; ++r) {
+                if (r >= n) break;
+                const float g = wave_sum(acc[0][fr][r]);
+                const float v = DUAL ? silu_f(g) * wave_sum(acc[NSETS - 1][fr][r]) : g;
+                if (lane == r) C[(int64_t)(r0 + r) * N + f0 + fr] = from_f32<T>(v);
+            }
+        }
+    }
+}
+
+// Launch shapes: gate_up reads one row per set (two sets) with up to 16 chunks (K <= 8192);
+// down reads four rows with up to 4 chunks (K <= 2048) or one row with up to 16.
+constexpr int SKINNY_MAX_K = 8192;
+
+template <typename T, bool DUAL, int JMAX, int FR, int IT>
+static void launch_skinny_t(const T* A, const T* B0, const T* B1, T* C, int K, int N, int E, Plan plan,
+                            hipStream_t s) {
+    constexpr int FPB = 8 * FR * IT;
+    const int bpe = (N + FPB - 1) / FPB;
+    const size_t lds = (size_t)SMALL_ROWS * K * sizeof(T);
+    skinny_gemm<T, DUAL, JMAX, FR, IT><<<(unsigned)((int64_t)E * bpe), 512, lds, s>>>(A, B0, B1, C, K, N, E, plan, bpe);
+}
+
+template <typename T>
+static void launch_skinny(bool dual, const T* A, const T* B0, const T* B1, T* C, int K, int N, int E, Plan plan,
+                          hipStream_t s) {
+    if (dual)
+        launch_skinny_t<T, true, 16, 1, 4>(A, B0, B1, C, K, N, E, plan, s);
+    else if (K <= 2048)
+        launch_skinny_t<T, false, 4, 4, 2>(A, B0, nullptr, C, K, N, E, plan, s);
+    else
+        launch_skinny_t<T, false, 16, 1, 8>(A, B0, nullptr, C, K, N, E, plan, s);
+}
+
+// ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
 static int64_t max_mtiles(int64_t rows, int64_t E, int BM) { return rows / BM + (E < rows ? E : rows); }
@@ -786,7 +907,7 @@ static size_t mfma_smem_bytes(int64_t E) {
 
 template <typename T, bool CACHE>
 static void launch_mfma(const rudnn_moe_experts* ex, const void* disp, int64_t rows, void* out, void* h, Plan plan,
-                        float* partials, float* cache, hipStream_t s) {
+                        float* partials, float* cache, bool skinny, hipStream_t s) {
     const int E = (int)ex->num_experts, H = (int)ex->hidden, I = (int)ex->intermediate;
     const int64_t mt = max_mtiles(rows, E, GateUpCfg::BM);
     const int cus = device_cus();
@@ -796,6 +917,7 @@ static void launch_mfma(const rudnn_moe_experts* ex, const void* disp, int64_t r
         return (unsigned)((units + 7) / 8 * 8);
     };
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP, s);
+    if (skinny) launch_skinny<T>(true, (const T*)disp, (const T*)ex->gate, (const T*)ex->up, (T*)h, H, I, E, plan, s);
     grouped_gemm_mfma<T, true, GateUpCfg, CACHE><<<grid_for(I, GateUpCfg::BN), GateUpCfg::THREADS,
                                                    mfma_smem_bytes<GateUpCfg, true>(E), s>>>(
         (const T*)disp, (const T*)ex->gate, (const T*)ex->up, (T*)h, H, I, E, plan, cus, partials, cache);
@@ -804,6 +926,7 @@ static void launch_mfma(const rudnn_moe_experts* ex, const void* disp, int64_t r
     splitk_reduce<T, true, GateUpCfg, CACHE><<<1024, 256, 0, s>>>(partials, (T*)h, H, I, E, plan, cus, cache);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_GATE_UP_REDUCE, s);
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_DOWN, s);
+    if (skinny) launch_skinny<T>(false, (const T*)h, (const T*)ex->down, nullptr, (T*)out, I, H, E, plan, s);
     grouped_gemm_mfma<T, false, DownCfg><<<grid_for(H, DownCfg::BN), DownCfg::THREADS,
                                            mfma_smem_bytes<DownCfg, false>(E), s>>>(
         (const T*)h, (const T*)ex->down, nullptr, (T*)out, I, H, E, plan, cus, partials, nullptr);
@@ -858,23 +981,28 @@ hipError_t launch_experts(const rudnn_moe_experts* ex, const void* disp, const i
     std::call_once(g_smem_once, allow_large_lds);
     static_assert(GateUpCfg::BM == DownCfg::BM, "both expert GEMMs share one tile plan");
     const int BM = ex->dtype == RUDNN_MOE_F32 ? F_BM : GateUpCfg::BM;
+    // Few rows per expert on average (decode-shaped batches): experts with at most SMALL_ROWS rows
+    // stream their weights through skinny_gemm and get no MFMA tiles.  Not with the training
+    // cache (skinny_gemm does not store the pre-activations).
+    const bool skinny = !cache && ex->dtype != RUDNN_MOE_F32 && ex->hidden <= SKINNY_MAX_K && I <= SKINNY_MAX_K &&
+                        rows <= SMALL_ROWS * E;
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_PLAN, s);
-    experts_plan_kernel<<<1, 1024, 0, s>>>(offsets, (int)E, (int)rows, BM, plan);
+    experts_plan_kernel<<<1, 1024, 0, s>>>(offsets, (int)E, (int)rows, BM, skinny ? SMALL_ROWS : 0, plan);
     timing_after(RUDNN_MOE_KERNEL_EXPERTS_PLAN, s);
     float* partials = (float*)(ws + align_up((size_t)rows * I * es) + align_up(sizeof(int32_t) * (3 * E + 1)));
     switch (ex->dtype) {
     case RUDNN_MOE_F32: launch_f32(ex, disp, rows, out, h, plan, cache, s); break;
     case RUDNN_MOE_F16:
         if (cache)
-            launch_mfma<f16, true>(ex, disp, rows, out, h, plan, partials, cache, s);
+            launch_mfma<f16, true>(ex, disp, rows, out, h, plan, partials, cache, false, s);
         else
-            launch_mfma<f16, false>(ex, disp, rows, out, h, plan, partials, nullptr, s);
+            launch_mfma<f16, false>(ex, disp, rows, out, h, plan, partials, nullptr, skinny, s);
         break;
     default:
         if (cache)
-            launch_mfma<bf16, true>(ex, disp, rows, out, h, plan, partials, cache, s);
+            launch_mfma<bf16, true>(ex, disp, rows, out, h, plan, partials, cache, false, s);
         else
-            launch_mfma<bf16, false>(ex, disp, rows, out, h, plan, partials, nullptr, s);
+            launch_mfma<bf16, false>(ex, disp, rows, out, h, plan, partials, nullptr, skinny, s);
         break;
     }
     return hipGetLastError();

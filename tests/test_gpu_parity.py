@@ -218,6 +218,11 @@ SMALL_LAYERS = {
     "long_k": Workload("long_k", 64, 4096, 2048, 4, 2, "bf16", "bf16", (True,), None, 207),
     # a long K that is not a multiple of the 64-element step, fp16
     "long_ragged_k": Workload("long_ragged_k", 40, 4104, 1032, 3, 1, "f16", "f16", (True,), None, 208),
+    # few rows per expert (at most 4 on average): experts of 1-4 rows take the weight-streaming
+    # path, the others MFMA tiles; K = 1000 and 520 are not multiples of the 512-element chunk
+    "bf16_few_rows": Workload("bf16_few_rows", 24, 1000, 520, 16, 2, "bf16", "bf16", (True,), None, 209),
+    # the same in fp16 with a down K above 2048 (the one-row-per-wavefront down variant)
+    "f16_few_rows": Workload("f16_few_rows", 30, 776, 2056, 32, 4, "f16", "f16", (False,), None, 210),
 }
 
 
