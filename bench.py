@@ -7,8 +7,9 @@ H=4096, I=14336, E=8, top_k=2, renormalised, bf16), all inputs resident in HBM. 
 JSON line with tokens/s, the roofline of the dominant kernel (the gate/up expert GEMM, timed
 with HIP events on its launch stream during the timed steps), a per-kernel breakdown, the HBM
 rates of route / dispatch / combine on the routing+dispatch workload (T=65536, E=128, k=8,
-H=2048, bf16, identity experts), the fused gate projection + routing on the same token shapes,
-and the CPU oracle timed on a bounded sample of the same layer.  HBM-bound stages start from a
+H=2048, bf16, identity experts), the forward of the decode-shaped, skewed and tiny layers
+(`forward_other`, not part of `value`), the fused gate projection + routing on the same token
+shapes, and the CPU oracle timed on a bounded sample of the same layer.  HBM-bound stages start from a
 cold cache: 512 MiB are read (not written) before each timed launch, so that the caches hold
 neither the inputs nor dirty lines whose write-back would land in the timed kernel.
 
@@ -28,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer tokens/s (1 GPU); expert-GEMM MFMA %; route/dispatch/combine GB/s"
 HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, 8 TB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # dense; fp32 = vector FMA peak
+DTYPE_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["mixture_experts_layer_23_amd/csrc/experts.hip", "mixture_experts_layer_23_amd/csrc/device.hpp",
                   "mixture_experts_layer_23_amd/csrc/internal.hpp"]
@@ -99,6 +101,8 @@ def main():
                     help="skip the fused gate projection + routing measurements")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the first-order training (backward chain) measurements")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the forward of the decode-shaped, skewed and tiny layers")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -360,6 +364,12 @@ def main():
                                  "hbm_frac": wbytes / (msd / 1e3) / 1e9 / HBM_PEAK_GBS}
         del gd, ud, dd, exd, wsd
 
+    # ---------------- the forward on the other layers of the workload set ----------------
+    other = None
+    if not args.no_other:
+        torch.cuda.empty_cache()
+        other = measure_other_forwards(moe, hip, stream, dev)
+
     # ---------------- gate projection fused with routing ----------------
     proj = None
     if not args.no_projection:
@@ -395,11 +405,60 @@ def main():
         "cpu_baseline": cpu,
         "stages": stages,
         "hbm_stages": hbm,
+        "forward_other": other,
         "sigmoid_routing": sig,
         "projection": proj,
         "training": train,
     }
     print(json.dumps(result), flush=True)
+
+
+def measure_other_forwards(moe, hip, stream, dev, steps=20):
+    """rudnn_moe_forward on the decode-shaped, skewed and tiny layers (inputs resident in HBM,
+    back-to-back steps): ms per forward, tokens/s, and the expert weights streamed per second
+    (active experts' 3*H*I elements) or the expert GEMMs' flops per second."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_23_amd.inputs import WORKLOADS, make_experts, make_logits, make_tokens
+
+    res = {}
+    for name in ("decode", "skewed", "tiny"):
+        w = WORKLOADS[name]
+        log("forward", name)
+        lg_cpu, _ = make_logits(w)
+        lg = lg_cpu.to(dev)
+        x = make_tokens(w, dev)
+        g, u, d = make_experts(w, dev)
+        ex = moe.SwiGluExperts(g, u, d)
+        out = torch.empty_like(x)
+        ws = torch.empty(moe.forward_workspace_size(ex, w.T, w.top_k, lg.dtype), dtype=torch.uint8, device=dev)
+        renorm = w.renormalize[0]
+        for _ in range(3):
+            ex.forward(x, lg, w.top_k, renorm, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        a, b = hip.event(), hip.event()
+        hip.record(a, stream)
+        for _ in range(steps):
+            ex.forward(x, lg, w.top_k, renorm, out=out, workspace=ws)
+        hip.record(b, stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(a, b) / steps
+        s = DTYPE_BYTES[w.dtype]
+        active = int(np.count_nonzero(np.bincount(moe.route(lg, w.top_k, renorm)[0].cpu().numpy().ravel(),
+                                                  minlength=w.E)))
+        wbytes = active * 3 * w.H * w.I * s
+        flops = 6.0 * w.T * w.top_k * w.H * w.I
+        ent = {"workload": f"T={w.T} H={w.H} I={w.I} E={w.E} k={w.top_k} {w.dtype}, {active} active experts",
+               "ms": ms, "tokens_per_s": w.T / (ms / 1e3),
+               "expert_weight_GBps": wbytes / (ms / 1e3) / 1e9, "hbm_frac": wbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+               "expert_TFLOPps": flops / (ms / 1e3) / 1e12}
+        if w.dtype != "f32":  # the FP32 layer runs on the vector FMAs, not the matrix cores
+            ent["mfma_frac"] = ent["expert_TFLOPps"] / MFMA_PEAK_TFLOPS[w.dtype]
+        res[name] = ent
+        del lg, x, g, u, d, ex, out, ws
+        torch.cuda.empty_cache()
+    return res
 
 
 def measure_projection(args, moe, hip, stream, flush, dev, ex, wmix, out_shape):
