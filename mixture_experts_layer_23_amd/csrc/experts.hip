@@ -968,6 +968,19 @@ static void allow_large_lds() {
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     (void)hipFuncSetAttribute((const void*)grouped_gemm_mfma<f16, true, GateUpCfg, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    // skinny_gemm stages SMALL_ROWS rows of up to SKINNY_MAX_K elements (64 KiB at the limit)
+    (void)hipFuncSetAttribute((const void*)skinny_gemm<bf16, true, 16, 1, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              lds);
+    (void)hipFuncSetAttribute((const void*)skinny_gemm<bf16, false, 4, 4, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              lds);
+    (void)hipFuncSetAttribute((const void*)skinny_gemm<bf16, false, 16, 1, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              lds);
+    (void)hipFuncSetAttribute((const void*)skinny_gemm<f16, true, 16, 1, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              lds);
+    (void)hipFuncSetAttribute((const void*)skinny_gemm<f16, false, 4, 4, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              lds);
+    (void)hipFuncSetAttribute((const void*)skinny_gemm<f16, false, 16, 1, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              lds);
 }
 
 hipError_t launch_experts(const rudnn_moe_experts* ex, const void* disp, const int32_t* offsets, int64_t rows,

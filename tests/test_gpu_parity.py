@@ -223,6 +223,8 @@ SMALL_LAYERS = {
     "bf16_few_rows": Workload("bf16_few_rows", 24, 1000, 520, 16, 2, "bf16", "bf16", (True,), None, 209),
     # the same in fp16 with a down K above 2048 (the one-row-per-wavefront down variant)
     "f16_few_rows": Workload("f16_few_rows", 30, 776, 2056, 32, 4, "f16", "f16", (False,), None, 210),
+    # the widest rows the weight-streaming path takes (H = 8192: 64 KiB of staged token rows)
+    "bf16_few_rows_wide": Workload("bf16_few_rows_wide", 8, 8192, 264, 8, 2, "bf16", "bf16", (True,), None, 211),
 }
 
 
