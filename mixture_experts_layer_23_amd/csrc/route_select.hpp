@@ -28,20 +28,38 @@ __device__ __forceinline__ float group_sum(float v) {
     for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
     return v;
 }
-template <int G>
-__device__ __forceinline__ uint32_t group_max_key(uint32_t key) {
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) key = max(key, (uint32_t)__shfl_xor(key, m, 64));
-    return key;
+// Lane permutations inside the 16-lane rows of a wavefront, as DPP moves (no LDS round trip):
+// STEP 0 swaps lanes 2i and 2i + 1, STEP 1 swaps the pairs of each quad, STEP 2 mirrors each
+// 8-lane half row, STEP 3 each 16-lane row.  Taking a maximum with STEP 0, 1, .. in turn leaves
+// every aligned group of 2, 4, 8, 16 lanes holding its group's maximum (a mirror pairs each lane
+// with one in the other half of its group, which by then holds that half's maximum).
+template <int STEP>
+__device__ __forceinline__ uint32_t row_perm(uint32_t v) {
+    constexpr int CTRL = STEP == 0 ? 0xb1 : STEP == 1 ? 0x4e : STEP == 2 ? 0x141 : 0x140;  // quad_perm / mirrors
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
-template <int G>
-__device__ __forceinline__ uint64_t group_max_key(uint64_t key) {
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)key, m, 64), hi = __shfl_xor((uint32_t)(key >> 32), m, 64);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        key = o > key ? o : key;
+template <int STEP>
+__device__ __forceinline__ uint64_t row_perm(uint64_t v) {
+    return ((uint64_t)row_perm<STEP>((uint32_t)(v >> 32)) << 32) | row_perm<STEP>((uint32_t)v);
+}
+template <typename K>
+__device__ __forceinline__ K xor_lanes(K v, int m) {
+    if constexpr (sizeof(K) == 4) {
+        return (K)__shfl_xor((uint32_t)v, m, 64);
+    } else {
+        const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+        return ((K)hi << 32) | lo;
     }
+}
+// The largest key of each aligned group of G lanes, in every lane of the group.
+template <int G, typename K>
+__device__ __forceinline__ K group_max_key(K key) {
+    if constexpr (G >= 2) key = max(key, row_perm<0>(key));
+    if constexpr (G >= 4) key = max(key, row_perm<1>(key));
+    if constexpr (G >= 8) key = max(key, row_perm<2>(key));
+    if constexpr (G >= 16) key = max(key, row_perm<3>(key));
+    if constexpr (G >= 32) key = max(key, xor_lanes(key, 16));
+    if constexpr (G >= 64) key = max(key, xor_lanes(key, 32));
     return key;
 }
 

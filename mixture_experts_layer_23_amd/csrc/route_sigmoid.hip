@@ -17,21 +17,12 @@
 //      times scale, rounded once to the logits dtype.
 #include "device.hpp"
 #include "internal.hpp"
+#include "route_select.hpp"  // group_max_key: the group maximum by DPP row permutations
 
 namespace rudnn {
 
 constexpr int SIG_THREADS = 256;
 
-template <int G>
-__device__ __forceinline__ uint64_t sig_group_max(uint64_t key) {
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)key, m, 64), hi = __shfl_xor((uint32_t)(key >> 32), m, 64);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        key = o > key ? o : key;
-    }
-    return key;
-}
 
 // FP32 value -> order-preserving 32 bits (-0 taken as +0), above the complement of an id.
 __device__ __forceinline__ uint64_t sig_key(float v, uint32_t id) {
@@ -141,7 +132,7 @@ __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __
         uint64_t best = 0;
 #pragma unroll
         for (int q = 0; q < GPL; ++q) best = max(best, gkey[q] < prev ? gkey[q] : (uint64_t)0);
-        const uint64_t win = sig_group_max<G>(best);
+        const uint64_t win = group_max_key<G>(best);
         prev = win;
         const uint32_t g = 0xffffffffu - (uint32_t)win;
 #pragma unroll
@@ -167,7 +158,7 @@ __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __
         uint64_t best = 0;
 #pragma unroll
         for (int s = 0; s < NPER; ++s) best = max(best, key[s] < prev ? key[s] : (uint64_t)0);
-        const uint64_t win = sig_group_max<G>(best);
+        const uint64_t win = group_max_key<G>(best);
         prev = win;
         const uint32_t id = 0xffffffffu - (uint32_t)win;
         const uint32_t idc = id < (uint32_t)E ? id : 0u;  // NaN rows may pick nothing valid
