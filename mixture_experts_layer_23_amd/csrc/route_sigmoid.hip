@@ -32,7 +32,9 @@ __device__ __forceinline__ uint64_t sig_key(float v, uint32_t id) {
     return ((uint64_t)ord << 32) | (uint32_t)(0xffffffffu - id);
 }
 
-template <typename LT, int NPER, int G>
+// VEC: every lane's NPER logits (and bias entries) are whole, 16-byte aligned vectors inside the
+// row (E % NPER == 0): one vector load each, and the scores go to LDS as 16-byte stores.
+template <typename LT, int NPER, int G, bool VEC>
 __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __restrict__ logits,
                                                                     const float* __restrict__ bias, int64_t T, int E,
                                                                     int k, int groups, int nsel, int top_two,
@@ -54,18 +56,57 @@ __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __
     // 1. sigmoid and corrected scores (slots past E are computed on a clamped id, then masked)
     float c[NPER];
     bool bad = false;
+    if constexpr (VEC) {
+        float xv[NPER], bv[NPER] = {};
+        const bool in = e0 < E;  // whole chunks: a lane's entries are all in or all out
+        {
+            constexpr int PER16 = 16 / (int)sizeof(LT);
+            LT t[NPER];
 #pragma unroll
-    for (int s = 0; s < NPER; ++s) {
-        const int e = e0 + s;
-        const int ec = e < E ? e : E - 1;
-        const float xv = to_f32(x[ec]);
-        const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-xv));  // +inf -> 1, -inf -> 0, NaN -> NaN
-        const float cv = bias ? sg + bias[ec] : sg;
-        c[s] = cv;
-        if (e < E) {
-            bad |= cv != cv;
-            sc[e] = cv;
-            ss[e] = sg;
+            for (int q = 0; q < NPER / PER16; ++q) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (in) v = *reinterpret_cast<const uint4*>(x + e0 + q * PER16);
+                __builtin_memcpy(t + q * PER16, &v, 16);
+            }
+#pragma unroll
+            for (int i = 0; i < NPER; ++i) xv[i] = to_f32(t[i]);
+            if (bias && in) {
+#pragma unroll
+                for (int q = 0; q < NPER / 4; ++q) {
+                    const float4 b4 = *reinterpret_cast<const float4*>(bias + e0 + q * 4);
+                    bv[4 * q] = b4.x, bv[4 * q + 1] = b4.y, bv[4 * q + 2] = b4.z, bv[4 * q + 3] = b4.w;
+                }
+            }
+        }
+        float sgv[NPER];
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+            sgv[i] = __builtin_amdgcn_rcpf(1.0f + expf(-xv[i]));  // +inf -> 1, -inf -> 0, NaN -> NaN
+            c[i] = bias ? sgv[i] + bv[i] : sgv[i];
+            bad |= in && c[i] != c[i];
+        }
+        if (in) {
+#pragma unroll
+            for (int q = 0; q < NPER / 4; ++q) {
+                *reinterpret_cast<float4*>(sc + e0 + q * 4) = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+                *reinterpret_cast<float4*>(ss + e0 + q * 4) =
+                    make_float4(sgv[4 * q], sgv[4 * q + 1], sgv[4 * q + 2], sgv[4 * q + 3]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < NPER; ++s) {
+            const int e = e0 + s;
+            const int ec = e < E ? e : E - 1;
+            const float xv = to_f32(x[ec]);
+            const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-xv));  // +inf -> 1, -inf -> 0, NaN -> NaN
+            const float cv = bias ? sg + bias[ec] : sg;
+            c[s] = cv;
+            if (e < E) {
+                bad |= cv != cv;
+                sc[e] = cv;
+                ss[e] = sg;
+            }
         }
     }
     __syncthreads();
@@ -188,8 +229,13 @@ static void launch_sig_g(const LT* l, const float* bias, int64_t T, int E, int k
     constexpr int RPB = SIG_THREADS / G;
     const dim3 grid((unsigned)((T + RPB - 1) / RPB)), block(SIG_THREADS);
     const size_t smem = (size_t)RPB * (2 * E + k) * 4;
-    route_sigmoid_kernel<LT, NPER, G><<<grid, block, smem, s>>>(l, bias, T, E, k, groups, nsel, top_two, renorm,
-                                                                scale, idx, w);
+    const bool vec = E % NPER == 0 && ((uintptr_t)l % 16) == 0 && ((uintptr_t)bias % 16) == 0;
+    if (vec)
+        route_sigmoid_kernel<LT, NPER, G, true><<<grid, block, smem, s>>>(l, bias, T, E, k, groups, nsel, top_two,
+                                                                          renorm, scale, idx, w);
+    else
+        route_sigmoid_kernel<LT, NPER, G, false><<<grid, block, smem, s>>>(l, bias, T, E, k, groups, nsel, top_two,
+                                                                           renorm, scale, idx, w);
 }
 
 template <typename LT>
