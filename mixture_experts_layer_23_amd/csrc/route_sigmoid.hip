@@ -3,7 +3,7 @@
 // group_top_two, renormalize, scale, and an optional FP32 correction bias [E]).
 //
 // A group of G adjacent lanes owns one row of logits [T, E] (the lane layout of the softmax
-// router: lane l of the group holds experts [l * NPER, (l + 1) * NPER)).  Per row, in FP32:
+// router: lane l of the group holds experts [l * NPER, (l + 1) * NPER), NPER = 16).  Per row, in FP32:
 //   1. s_e = 1 / (1 + exp(-x_e)); corrected score c_e = s_e + bias_e (the bias only steers the
 //      choice).  s and c go to LDS.
 //   2. Group scores from LDS, lane l taking groups l, l + G, ...: the largest c of the group,
@@ -247,21 +247,20 @@ static hipError_t launch_sig_t(const void* logits, const float* bias, int64_t T,
     const int Ei = (int)E, ki = (int)k, gi = (int)groups, ni = (int)nsel, t2 = top_two ? 1 : 0, r = renorm ? 1 : 0;
     const float sc = (float)scale;
     timing_before(RUDNN_MOE_KERNEL_ROUTE_SIGMOID_GROUPED, s);
-    // lanes per row: the smallest power of two G with 8 G >= E (16 G >= E once G reaches 64)
-    if (E <= 8)
-        launch_sig_g<LT, 8, 1>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
-    else if (E <= 16)
-        launch_sig_g<LT, 8, 2>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+    // lanes per row: the smallest power of two G with 16 G >= E (16 experts per lane: fewer lanes
+    // per row means fewer cross-lane steps in every selection round)
+    if (E <= 16)
+        launch_sig_g<LT, 16, 1>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 32)
-        launch_sig_g<LT, 8, 4>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 16, 2>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 64)
-        launch_sig_g<LT, 8, 8>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 16, 4>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 128)
-        launch_sig_g<LT, 8, 16>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 16, 8>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 256)
-        launch_sig_g<LT, 8, 32>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 16, 16>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else if (E <= 512)
-        launch_sig_g<LT, 8, 64>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
+        launch_sig_g<LT, 16, 32>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     else
         launch_sig_g<LT, 16, 64>(l, bias, T, Ei, ki, gi, ni, t2, r, sc, idx, wo, s);
     timing_after(RUDNN_MOE_KERNEL_ROUTE_SIGMOID_GROUPED, s);
