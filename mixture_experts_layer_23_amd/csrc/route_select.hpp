@@ -210,15 +210,22 @@ __device__ __forceinline__ float ord_logit(uint32_t key) {
 }
 
 // key[a] >= key[b] afterwards
-__device__ __forceinline__ void key_order(uint32_t& a, uint32_t& b) {
-    const uint32_t x = a, y = b;
-    a = max(x, y);
-    b = min(x, y);
+template <typename K>
+__device__ __forceinline__ void key_order(K& a, K& b) {
+    const K x = a, y = b;
+    if constexpr (sizeof(K) == 4) {
+        a = max(x, y);
+        b = min(x, y);
+    } else {
+        const bool gt = x > y;
+        a = gt ? x : y;
+        b = gt ? y : x;
+    }
 }
 
 // Bitonic sort, descending, of key[B .. B + N) (N a power of two).
-template <int B, int N, int NPER>
-__device__ __forceinline__ void key_sort(uint32_t (&key)[NPER]) {
+template <int B, int N, typename K, int NPER>
+__device__ __forceinline__ void key_sort(K (&key)[NPER]) {
 #pragma unroll
     for (int kk = 2; kk <= N; kk <<= 1)
 #pragma unroll
@@ -233,6 +240,42 @@ __device__ __forceinline__ void key_sort(uint32_t (&key)[NPER]) {
                         key_order(key[B + l], key[B + i]);
                 }
             }
+}
+
+// The L largest of the NPER keys, sorted descending, in key[0 .. L): the whole chunk (L == NPER)
+// or the top 8 of 16 (sort both halves, keep the larger of key[i] and key[15 - i], which leaves
+// the top 8 as one bitonic sequence, and merge it).
+template <int L, typename K, int NPER>
+__device__ __forceinline__ void sort_top(K (&key)[NPER]) {
+    static_assert(L == NPER || (L == 8 && NPER == 16), "the whole chunk or the top 8 of 16");
+    if constexpr (L == NPER) {
+        key_sort<0, NPER>(key);
+    } else {
+        key_sort<0, 8>(key);
+        key_sort<8, 8>(key);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) key[i] = key[i] > key[15 - i] ? key[i] : key[15 - i];  // max
+#pragma unroll
+        for (int j = 4; j > 0; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((i ^ j) > i) key_order(key[i], key[i ^ j]);
+    }
+}
+
+// k rounds over per-lane lists sorted by sort_top<L>: the group maximum of the lists' heads wins
+// and its lane shifts its list by one (keys are unique in a row, so exactly one lane holds it).
+// Calls on_win(j, win) for round j.
+template <int G, int L, typename K, int NPER, typename F>
+__device__ __forceinline__ void select_sorted(K (&key)[NPER], int k, F on_win) {
+    for (int j = 0; j < k; ++j) {
+        const K win = group_max_key<G>(key[0]);
+        const bool hit = key[0] == win;
+#pragma unroll
+        for (int p = 0; p < L - 1; ++p) key[p] = hit ? key[p + 1] : key[p];
+        key[L - 1] = hit ? (K)0 : key[L - 1];
+        on_win(j, win);
+    }
 }
 
 template <typename LT, int NPER, int G, int L>
@@ -267,27 +310,10 @@ __device__ __forceinline__ void route_row_sorted(const uint16_t (&raw)[NPER], in
     const bool nan_row =
         ((__ballot(nan_or_posinf) >> gshift) & gmask) != 0 || ((__ballot(not_neginf) >> gshift) & gmask) == 0;
 
-    if constexpr (L == NPER) {
-        key_sort<0, NPER>(key);
-    } else {  // top 8 of 16: sort both halves, keep the larger of key[i] and key[15 - i], merge
-        key_sort<0, 8>(key);
-        key_sort<8, 8>(key);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) key[i] = max(key[i], key[15 - i]);
-#pragma unroll
-        for (int j = 4; j > 0; j >>= 1)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if ((i ^ j) > i) key_order(key[i], key[i ^ j]);
-    }
+    sort_top<L>(key);
 
     float m = 0.f, den = 0.f;
-    for (int j = 0; j < k; ++j) {
-        const uint32_t win = group_max_key<G>(key[0]);
-        const bool hit = key[0] == win;
-#pragma unroll
-        for (int p = 0; p < L - 1; ++p) key[p] = hit ? key[p + 1] : key[p];
-        key[L - 1] = hit ? 0u : key[L - 1];
+    select_sorted<G, L>(key, k, [&](int j, uint32_t win) __attribute__((always_inline)) {
         const float xw = ord_logit<LT>(win);
         if (j == 0) m = xw;
         const float e = expf(xw - m);  // -inf logits give 0 exactly
@@ -296,7 +322,7 @@ __device__ __forceinline__ void route_row_sorted(const uint16_t (&raw)[NPER], in
             si[j] = 0xffffu - (win & 0xffffu);
             se[j] = e;
         }
-    }
+    });
     if (!renorm) {  // denominator over all experts
         float sum = 0.f;
         if (lane_in) {

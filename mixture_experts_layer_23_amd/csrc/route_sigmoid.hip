@@ -12,7 +12,8 @@
 //   3. selected_groups rounds over order-preserving keys (score bits above the complemented
 //      group id) choose the groups, ties to the lower group.
 //   4. k rounds over the experts of the chosen groups (keys: c bits above the complemented
-//      expert id; experts of other groups have key 0) choose the experts, ties to the lower id.
+//      expert id; experts of other groups have key 0) choose the experts, ties to the lower id:
+//      each lane sorts its largest keys once and a round takes the largest of the lanes' heads.
 //   5. w_j = s_j, divided by the FP32 sum of the selected s (j ascending) when renormalising,
 //      times scale, rounded once to the logits dtype.
 #include "device.hpp"
@@ -193,18 +194,25 @@ __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __
             if ((wv >> (g & 31)) & 1u) key[s] = sig_key(c[s], (uint32_t)e);
         }
     }
-    prev = ~0ull;
+    // each lane's largest keys sorted once; a round compares only the lists' heads
     float den = 0.f;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
-#pragma unroll
-        for (int s = 0; s < NPER; ++s) best = max(best, key[s] < prev ? key[s] : (uint64_t)0);
-        const uint64_t win = group_max_key<G>(best);
-        prev = win;
+    auto take = [&](int j, uint64_t win) __attribute__((always_inline)) {
         const uint32_t id = 0xffffffffu - (uint32_t)win;
         const uint32_t idc = id < (uint32_t)E ? id : 0u;  // NaN rows may pick nothing valid
         den += ss[idc];
         if (l == 0) swin[j] = idc;
+    };
+    if constexpr (NPER == 16) {
+        if (k <= 8) {  // block-uniform
+            sort_top<8>(key);
+            select_sorted<G, 8>(key, k, take);
+        } else {
+            sort_top<16>(key);
+            select_sorted<G, 16>(key, k, take);
+        }
+    } else {
+        sort_top<NPER>(key);
+        select_sorted<G, NPER>(key, k, take);
     }
     __syncthreads();
 
