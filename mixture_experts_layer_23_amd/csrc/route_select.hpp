@@ -303,27 +303,11 @@ __device__ __forceinline__ void route_row_sorted(const uint16_t (&raw)[NPER], in
         key[2 * p + 1] = lane_in ? (((uint32_t)ord.y << 16) | (0xffffu - (uint32_t)(e0 + 2 * p + 1))) : 0u;
     }
     const uint32_t hi = max((uint32_t)omax.x, (uint32_t)omax.y), lo = min((uint32_t)omin.x, (uint32_t)omin.y);
-    const bool nan_or_posinf = lane_in && (hi >= POS || lo < NEG);
-    const bool not_neginf = lane_in && !(hi == NEG && lo == NEG);
-    const int gshift = lane - l;  // first lane of the group
-    const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull);
-    const bool nan_row =
-        ((__ballot(nan_or_posinf) >> gshift) & gmask) != 0 || ((__ballot(not_neginf) >> gshift) & gmask) == 0;
-
-    sort_top<L>(key);
-
-    float m = 0.f, den = 0.f;
-    select_sorted<G, L>(key, k, [&](int j, uint32_t win) __attribute__((always_inline)) {
-        const float xw = ord_logit<LT>(win);
-        if (j == 0) m = xw;
-        const float e = expf(xw - m);  // -inf logits give 0 exactly
-        den += e;
-        if (live && l == 0) {
-            si[j] = 0xffffu - (win & 0xffffu);
-            se[j] = e;
-        }
-    });
-    if (!renorm) {  // denominator over all experts
+    // the row maximum (the first winner's logit) and, without renormalisation, the denominator over
+    // all experts, before the sort: the raw logits are then dead during the selection
+    const float m = ord_logit<LT>(group_max_key<G>(lane_in ? hi : 0u) << 16);
+    float den = 0.f;
+    if (!renorm) {
         float sum = 0.f;
         if (lane_in) {
 #pragma unroll
@@ -335,6 +319,23 @@ __device__ __forceinline__ void route_row_sorted(const uint16_t (&raw)[NPER], in
         }
         den = group_sum<G>(sum);
     }
+    const bool nan_or_posinf = lane_in && (hi >= POS || lo < NEG);
+    const bool not_neginf = lane_in && !(hi == NEG && lo == NEG);
+    const int gshift = lane - l;  // first lane of the group
+    const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1ull);
+    const bool nan_row =
+        ((__ballot(nan_or_posinf) >> gshift) & gmask) != 0 || ((__ballot(not_neginf) >> gshift) & gmask) == 0;
+
+    sort_top<L>(key);
+
+    select_sorted<G, L>(key, k, [&](int j, uint32_t win) __attribute__((always_inline)) {
+        const float e = expf(ord_logit<LT>(win) - m);  // -inf logits give 0 exactly
+        if (renorm) den += e;
+        if (live && l == 0) {
+            si[j] = 0xffffu - (win & 0xffffu);
+            se[j] = e;
+        }
+    });
     __syncthreads();
     if (live) {
         for (int j = l; j < k; j += G) {
