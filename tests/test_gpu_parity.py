@@ -72,6 +72,9 @@ ROUTE_EDGE = [
     # (T, E, k, dtype)
     (1, 1, 1, "f32"), (5, 3, 3, "bf16"), (333, 64, 64, "f16"), (97, 65, 7, "bf16"), (70, 1000, 64, "f32"),
     (129, 1024, 64, "f16"), (1000, 1024, 1, "f16"), (257, 200, 16, "f32"), (64, 8, 8, "bf16"),
+    # 16-bit logits in whole 16-element lane chunks with lanes past the row's end (E = 48: 4 lanes,
+    # 3 in use; E = 96: 8 lanes, 6 in use), top 8 and whole-chunk lists (k > 8)
+    (300, 48, 8, "bf16"), (211, 48, 12, "f16"), (150, 96, 16, "bf16"), (99, 96, 5, "f16"), (400, 128, 12, "bf16"),
 ]
 
 
