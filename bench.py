@@ -35,6 +35,18 @@ KERNEL_SOURCES = ["mixture_experts_layer_23_amd/csrc/experts.hip", "mixture_expe
                   "mixture_experts_layer_23_amd/csrc/internal.hpp"]
 
 
+
+def _cpu_model() -> str:
+    """The host CPU's model name as /proc/cpuinfo gives it (empty when unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -244,6 +256,7 @@ def main():
         oracle.forward(x_c[:n], logits_cpu[:n], k, renorm, g_c, u_c, d_c)
         dt = time.perf_counter() - t0
         cpu = {"value": n / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "cpu_model": _cpu_model(),
                "sample": f"first {n} of the {T} tokens of the Mixtral-shaped layer, whole forward "
                          f"(route, dispatch, SwiGLU experts, combine) in the fp64 oracle; {dt:.1f} s"}
         del g_c, u_c, d_c, x_c

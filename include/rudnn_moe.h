@@ -36,15 +36,25 @@
 extern "C" {
 #endif
 
+/* The enumerations below travel as 32-bit ints, and a C caller may pass any int.  C++ gives
+ * them int as their fixed underlying type, so such a value is still a value of the type and the
+ * entry points can reject it with an error (without it, an int outside the enumerators would be
+ * undefined behaviour on the library's side). */
+#ifdef __cplusplus
+#define RUDNN_MOE_ENUM enum : int
+#else
+#define RUDNN_MOE_ENUM enum
+#endif
+
 /* Floating-point storage types (section 4: unquantised F32, F16 or BF16). */
-typedef enum {
+typedef RUDNN_MOE_ENUM {
     RUDNN_MOE_F32 = 0,
     RUDNN_MOE_F16 = 1,
     RUDNN_MOE_BF16 = 2
 } rudnn_moe_dtype;
 
 /* Result of every entry point; the counterpart of the guide's MoeError (sections 3 and 6). */
-typedef enum {
+typedef RUDNN_MOE_ENUM {
     RUDNN_MOE_OK = 0,
     RUDNN_MOE_ERR_SHAPE = 1,       /* a size < 1 where one is required; E/H/I disagree */
     RUDNN_MOE_ERR_DTYPE = 2,       /* not F32/F16/BF16; tokens and expert weights differ */
@@ -83,8 +93,10 @@ typedef struct {
 /*
  * route -- section 4 "Routing contract" (RoutingPlan, expert_indices(), weights()).
  * For each row t of logits [T, E]: p = softmax over all E experts, computed in FP32; the k
- * largest p are selected, equal p favouring the lower expert id, and listed by descending
- * p (equal p: ascending id).  weights[t, j] = p of the j-th selected expert, divided by the
+ * largest p are selected and listed by descending p.  Softmax is strictly increasing, so the
+ * selection is made on the exact logits: equal logits (a true tie) favour the lower expert
+ * id, and of two distinct logits the larger wins even where their FP32 probabilities round
+ * (or underflow) to the same value.  weights[t, j] = p of the j-th selected expert, divided by the
  * sum of the k selected p when opt.renormalize, then cast (round to nearest even) to the
  * logits dtype.  A row holding a NaN, a +inf, or nothing but -inf gets weights NaN and
  * indices 0..k-1.
@@ -268,7 +280,7 @@ rudnn_moe_status rudnn_moe_forward_projected(const rudnn_moe_experts* ex, const 
 /* ---- First-order training (section 12 "MoE-Training erster Ordnung") ---- */
 
 /* Integer type of caller-provided expert indices (section 12: U32, I32 or I64). */
-typedef enum { RUDNN_MOE_U32 = 0, RUDNN_MOE_I32 = 1, RUDNN_MOE_I64 = 2 } rudnn_moe_index_type;
+typedef RUDNN_MOE_ENUM { RUDNN_MOE_U32 = 0, RUDNN_MOE_I32 = 1, RUDNN_MOE_I64 = 2 } rudnn_moe_index_type;
 
 /* RouterWeightOptions of section 12: RouterScoring::Softmax (0) or Sigmoid (1), optional
  * renormalisation of the selected weights, then a finite positive scale. */
@@ -392,7 +404,7 @@ const char* rudnn_moe_status_string(rudnn_moe_status s);
  * Optional timing hook (measurement only; not part of the method).  The library's kernels,
  * as launched by the entry points above:
  */
-typedef enum {
+typedef RUDNN_MOE_ENUM {
     RUDNN_MOE_KERNEL_ROUTE = 0,
     RUDNN_MOE_KERNEL_DISPATCH_COUNT = 1,
     RUDNN_MOE_KERNEL_DISPATCH_SCAN = 2,

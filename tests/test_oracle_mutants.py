@@ -15,6 +15,7 @@ PINS = "test_oracle_pins.py"
 SIG = "test_oracle_sigmoid_pins.py"
 PROJ = "test_oracle_projection_pins.py"
 BWD = "test_oracle_backward_pins.py"
+FWD = "test_oracle_forward_pins.py"
 
 MUTANTS = {
     "tie_to_higher_id": ("if (best < 0 || p[e] > p[best]) best = e;", "if (best < 0 || p[e] >= p[best]) best = e;"),
@@ -66,6 +67,15 @@ MUTANTS = {
     "bwd_dweights_from_weight": ("dw += go * load_val(expert_output, dt, r * H + c);", "dw += go * w;", BWD),
     "bwd_dispatch_skips_last": ("for (int64_t j = 0; j < k; ++j) s += load_val(grad_dispatched",
                                 "for (int64_t j = 0; j + 1 < k; ++j) s += load_val(grad_dispatched", BWD),
+    # the composed forwards with sigmoid routing and with the gate projection, checked against
+    # their own pins
+    "fwd_routed_weights_in_token_dtype": ("rc = oracle_combine(y, dt, map, w, ldt, T, k, H, output);\n    if (gate) free(y);\n    free(disp);\n    free(map);\n    free(offs);\n    return rc;",
+                                          "rc = oracle_combine(y, dt, map, w, dt, T, k, H, output);\n    if (gate) free(y);\n    free(disp);\n    free(map);\n    free(offs);\n    return rc;", FWD),
+    "fwd_routed_combines_the_inputs": ("rc = oracle_combine(y, dt, map, w, ldt, T, k, H, output);\n    if (gate) free(y);\n    free(disp);\n    free(map);\n    free(offs);\n    return rc;",
+                                       "rc = oracle_combine(disp, dt, map, w, ldt, T, k, H, output);\n    if (gate) free(y);\n    free(disp);\n    free(map);\n    free(offs);\n    return rc;", FWD),
+    "fwd_sigmoid_scale_dropped": ("scale, idx, w, NULL);", "1.0, idx, w, NULL);", FWD),
+    "fwd_projected_renorm_dropped": ("oracle_route_projected(input, dt, router, T, H, E, k, renormalize, idx, w, NULL);",
+                                     "oracle_route_projected(input, dt, router, T, H, E, k, 0, idx, w, NULL);", FWD),
 }
 
 
