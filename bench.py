@@ -76,6 +76,34 @@ class Hip:
         assert self.L.hipEventElapsedTime(ctypes.byref(v), a, b) == 0
         return float(v.value)
 
+    def ms_if_recorded(self, a, b):
+        """Elapsed time, or None when the pair was never recorded (its kernel did not launch)."""
+        v = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(v), a, b) != 0:
+            return None
+        return float(v.value)
+
+
+class ProfilerRegion:
+    """roctx resume/pause around the timed steps: under ``rocprofv3 --selected-regions`` the kernel
+    trace then holds exactly the timed launches (outside rocprofv3 these calls do nothing)."""
+
+    def __init__(self):
+        try:
+            self.L = ctypes.CDLL("librocprofiler-sdk-roctx.so.1")
+            self.L.roctxProfilerResume.argtypes = [ctypes.c_uint64]
+            self.L.roctxProfilerPause.argtypes = [ctypes.c_uint64]
+        except OSError:
+            self.L = None
+
+    def resume(self):
+        if self.L is not None:
+            self.L.roctxProfilerResume(0)
+
+    def pause(self):
+        if self.L is not None:
+            self.L.roctxProfilerPause(0)
+
 
 def kernel_source_hash():
     h = hashlib.sha256()
@@ -178,23 +206,33 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps back to back; HIP events around every gate/up GEMM launch
+    # timed region: K steps back to back; HIP events around every gate/up GEMM launch and around
+    # its split-K reduce (the epilogue of the K-split tail tiles), when that launches
     K = args.steps
     gu_ev = [(hip.event(), hip.event()) for _ in range(K)]
+    gur_ev = [(hip.event(), hip.event()) for _ in range(K)]
     t_start, t_stop = hip.event(), hip.event()
+    region = ProfilerRegion()
     torch.cuda.synchronize()
+    region.resume()
     wall0 = time.perf_counter()
     hip.record(t_start, stream)
     for i in range(K):
         moe.time_next_launch("experts_gate_up", *gu_ev[i])
+        moe.time_next_launch("experts_gate_up_reduce", *gur_ev[i])
         step()
+        moe.time_next_launch("experts_gate_up_reduce", None, None)  # clear it if it did not launch
     hip.record(t_stop, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    region.pause()
     ms_total = hip.ms(t_start, t_stop)
     ms_per_step = ms_total / K
     tokens_per_s = w.T / (ms_per_step / 1e3)
-    gu_ms = float(np.mean([hip.ms(a, b) for a, b in gu_ev]))
+    gu_main_ms = float(np.mean([hip.ms(a, b) for a, b in gu_ev]))
+    gur = [hip.ms_if_recorded(a, b) for a, b in gur_ev]
+    gu_reduce_ms = float(np.mean([v for v in gur if v is not None])) if any(v is not None for v in gur) else 0.0
+    gu_ms = gu_main_ms + gu_reduce_ms
     log(f"{K} steps: {ms_per_step:.3f} ms/step (host wall {wall / K * 1e3:.3f} ms), gate/up {gu_ms:.3f} ms")
 
     T, H, I, E, k = w.T, w.H, w.I, w.E, w.top_k
@@ -414,7 +452,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "experts_gate_up", "achieved": gu_tflops,
                      "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
                      "frac": gu_tflops / MFMA_PEAK_TFLOPS[w.dtype], "traffic": traffic,
-                     "algorithmic_per_launch": gu_flops, "avg_launch_ms": gu_ms},
+                     "algorithmic_per_launch": gu_flops, "avg_launch_ms": gu_ms,
+                     "avg_launch_ms_parts": {"experts_gate_up": gu_main_ms, "experts_gate_up_reduce": gu_reduce_ms}},
         "cpu_baseline": cpu,
         "stages": stages,
         "hbm_stages": hbm,

@@ -37,21 +37,23 @@ def assert_close(got: torch.Tensor, ref: torch.Tensor, dt: str, what: str = ""):
                            f"max abs err {d.max():.3g}, max rel {(d / ra.clamp_min(1e-30)).max():.3g}")
 
 
-def sampled_oracle_forward(x, logits, rows, k, renorm, gate, up, down):
-    """The oracle's forward on the given tokens only: route, each selected expert on the
-    token's row (only the experts used are copied to the host), combine."""
-    xs, ls = x[rows].cpu(), logits[rows].cpu()
-    ridx, rw, _ = oracle.route(ls, k, renorm)
+def full_oracle_forward(x, logits, k, renorm, gate, up, down):
+    """The oracle's staged forward over every token: route, dispatch, the SwiGLU experts, combine.
+    Only the experts that receive rows are copied to the host (ids renumbered in increasing
+    order, so the dispatched row order is the same as with all E experts)."""
+    ridx, rw, _ = oracle.route(logits.cpu(), k, renorm)
+    E = gate.shape[0]
     used = np.unique(ridx)
-    remap = {int(e): i for i, e in enumerate(used)}
+    remap = np.full(E, -1, np.int64)
+    remap[used] = np.arange(len(used))
     sel = torch.from_numpy(used.astype(np.int64)).to(gate.device)
     g, u, dn = gate[sel].cpu(), up[sel].cpu(), down[sel].cpu()
-    n = len(rows)
-    order = np.argsort(ridx.ravel(), kind="stable")  # group rows by expert
-    xr = xs.repeat_interleave(k, 0)[torch.from_numpy(order)]
-    eor = np.array([remap[int(e)] for e in ridx.ravel()[order]], np.int32)
-    yr = oracle.expert_rows(xr, eor, g, u, dn)
-    y = torch.empty_like(yr)
-    y[torch.from_numpy(order)] = yr
-    tmap = np.arange(n * k, dtype=np.int32).reshape(n, k)
-    return oracle.combine(y, tmap, rw)
+    say("oracle dispatch", len(used), "active experts")
+    rdisp, roffs_c, rmap, _ = oracle.dispatch(remap[ridx].astype(np.uint32), x.cpu(), len(used))
+    say("oracle experts", rdisp.shape[0], "rows")
+    ry = oracle.experts_forward(rdisp, roffs_c, g, u, dn)
+    say("oracle combine")
+    rout = oracle.combine(ry, rmap, rw)
+    counts = np.bincount(ridx.ravel().astype(np.int64), minlength=E)
+    roffs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return ridx, rdisp, roffs, ry, rout

@@ -3,8 +3,8 @@ inputs.  Indices, dispatch counts and maps are compared bit for bit; floating-po
 within the stated tolerances (FP32: 1e-4 relative + 1e-5; BF16/F16: 2e-2 relative with a
 floor of 2e-2 times the RMS of the reference, see ``assert_close``); NaN positions exactly.
 
-Small cases run the whole oracle; the full-size workloads compare sampled tokens, which the
-oracle computes one by one (each token's output depends only on its own row)."""
+Every workload, the full-size ones included, is compared element by element with the whole
+oracle."""
 import math
 import sys
 
@@ -16,7 +16,7 @@ from mixture_experts_layer_23_amd import moe
 from mixture_experts_layer_23_amd.inputs import DTYPES, WORKLOADS, Workload, make_experts, make_tokens
 from mixture_experts_layer_23_amd.inputs import make_logits as _make_logits
 from oracle import oracle
-from parity_util import assert_close, sampled_oracle_forward, say
+from parity_util import assert_close, full_oracle_forward, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -271,25 +271,31 @@ def test_forward_parity_small(name):
         assert torch.isnan(out[int(t)]).all()
 
 
-@pytest.mark.parametrize("name,nsample", [("decode", 16), ("skewed", 64), ("mixtral", 24)])
-def test_forward_parity_full_size_sampled(name, nsample):
+@pytest.mark.parametrize("name", ["decode", "skewed", "mixtral"])
+def test_forward_parity_full_size(name):
+    """Every output element of the full-size layers against the oracle: the routing indices bit
+    for bit, the expert GEMMs on the oracle's dispatched rows (every row of every expert,
+    including the ragged last m-tile of each expert and the K-split tail tiles), and the forward
+    itself.  Outputs start as NaN, so a tile that is never written cannot pass."""
     w = WORKLOADS[name]
-    say("forward-full", name, "T", w.T, "H", w.H, "I", w.I, "E", w.E, "k", w.top_k, "sample", nsample)
+    say("forward-full", name, "T", w.T, "H", w.H, "I", w.I, "E", w.E, "k", w.top_k)
     logits, _ = make_logits(w)
     x = make_tokens(w, DEV)
     gate, up, down = make_experts(w, DEV)
     ex = moe.SwiGluExperts(gate, up, down)
     renorm = w.renormalize[0]
-    out = ex.forward(x, logits.to(DEV), w.top_k, renorm)
+    out = torch.full((w.T, w.H), float("nan"), dtype=DTYPES[w.dtype], device=DEV)
+    ex.forward(x, logits.to(DEV), w.top_k, renorm, out=out)
+    idx, _ = moe.route(logits.to(DEV), w.top_k, renorm)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(w.seed)
-    rows = np.sort(rng.choice(w.T, size=min(nsample, w.T), replace=False))
-    # the hottest and the coldest tokens' experts are covered by taking first/last rows too
-    rows = np.unique(np.concatenate([rows, [0, w.T - 1]]))
-    say("oracle on", len(rows), "tokens")
-    ref = sampled_oracle_forward(x, logits, rows, w.top_k, renorm, gate, up, down)
-    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, w.dtype, "forward (sampled)")
-    # every output row is finite (no NaN rows in these workloads) and no row was left unwritten
+    ridx, rdisp, roffs, ry, rout = full_oracle_forward(x, logits, w.top_k, renorm, gate, up, down)
+    assert np.array_equal(idx.cpu().numpy().astype(np.int64), ridx.astype(np.int64))
+    y = torch.full(tuple(rdisp.shape), float("nan"), dtype=DTYPES[w.dtype], device=DEV)
+    moe.experts_forward(ex, rdisp.to(DEV), torch.from_numpy(roffs).to(DEV), out=y)
+    torch.cuda.synchronize()
+    say("compare", name)
+    assert_close(y, ry, w.dtype, "expert output (all rows)")
+    assert_close(out, rout, w.dtype, "forward (all tokens)")
     assert torch.isfinite(out).all()
 
 

@@ -20,7 +20,7 @@ import torch
 from mixture_experts_layer_23_amd import moe
 from mixture_experts_layer_23_amd.inputs import WORKLOADS, Workload, make_experts, make_projection_inputs
 from oracle import oracle
-from parity_util import assert_close, sampled_oracle_forward, say
+from parity_util import assert_close, full_oracle_forward, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -192,20 +192,22 @@ def test_forward_projected_small(name):
     assert_close(out, ref, w.dtype, "forward_projected")
 
 
-@pytest.mark.parametrize("name,nsample", [("mixtral", 24), ("decode", 16)])
-def test_forward_projected_full_size_sampled(name, nsample):
+@pytest.mark.parametrize("name", ["mixtral", "decode"])
+def test_forward_projected_full_size(name):
+    """Every logit and every output element of the full-size layers: the forward's output starts
+    as NaN and is compared with the oracle's forward on the logits the kernel routed."""
     w = WORKLOADS[name]
     renorm = w.renormalize[0]
-    say("forward-projected full", name, "sample", nsample)
+    say("forward-projected full", name)
     x, router, _ = make_projection_inputs(w, DEV)
     gate, up, down = make_experts(w, DEV)
     ex = moe.SwiGluExperts(gate, up, down)
-    out = ex.forward_projected(x, router, w.top_k, renorm)
+    out = torch.full((w.T, w.H), float("nan"), dtype=x.dtype, device=DEV)
+    ex.forward_projected(x, router, w.top_k, renorm, out=out)
     idx, wt, lo = moe.route_projected(x, router, w.top_k, renorm, logits_out=True)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(w.seed)
-    rows = np.unique(np.concatenate([rng.choice(w.T, size=min(nsample, w.T), replace=False), [0, w.T - 1]]))
-    check_logits(lo[torch.as_tensor(rows, device=DEV)], x, router, w.dtype, rows)
-    ref = sampled_oracle_forward(x, lo, rows, w.top_k, renorm, gate, up, down)
-    assert_close(out[torch.from_numpy(rows).to(DEV)], ref, w.dtype, "forward_projected (sampled)")
+    check_logits(lo, x, router, w.dtype)
+    ridx, _, _, _, ref = full_oracle_forward(x, lo, w.top_k, renorm, gate, up, down)
+    assert np.array_equal(idx.cpu().numpy().astype(np.int64), ridx.astype(np.int64))
+    assert_close(out, ref, w.dtype, "forward_projected (all tokens)")
     assert torch.isfinite(out).all()
