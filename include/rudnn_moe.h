@@ -136,6 +136,23 @@ rudnn_moe_status rudnn_moe_dispatch(const uint32_t* expert_indices, int64_t T, i
                                     int32_t* expert_offsets, int32_t* token_map, void* workspace,
                                     size_t workspace_size, hipStream_t stream);
 
+/*
+ * dispatch_no_alloc -- rudnn_moe_dispatch for callers that cannot allocate: code under HIP
+ * graph capture, serving loops that must not call hipMalloc, harnesses that forbid it.  Same
+ * arguments, results and errors as rudnn_moe_dispatch, without the workspace: the per-chunk
+ * expert counts live in a device array of RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES that the library
+ * holds on every GPU it runs on until the process ends (its device address is looked up on the
+ * first call on each device).  The call allocates nothing.  A call whose
+ * rudnn_moe_dispatch_workspace_size(T, top_k, E) exceeds that size returns
+ * RUDNN_MOE_ERR_UNSUPPORTED (e.g. E = 128 allows T * top_k up to about 33.5 million pairs).
+ * All calls on one GPU share the array: calls that may overlap on one GPU (several host threads
+ * or streams) race and must be ordered by the caller.
+ */
+#define RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES ((size_t)4 << 20)
+rudnn_moe_status rudnn_moe_dispatch_no_alloc(const uint32_t* expert_indices, int64_t T, int64_t top_k, int64_t E,
+                                             const void* input, rudnn_moe_dtype dtype, int64_t H, void* dispatched,
+                                             int32_t* expert_offsets, int32_t* token_map, hipStream_t stream);
+
 /* Bytes of device workspace rudnn_moe_experts_forward needs for `rows` dispatched rows
  * (the hidden activation [rows, I] plus the tile schedule). */
 size_t rudnn_moe_experts_workspace_size(const rudnn_moe_experts* ex, int64_t rows);

@@ -38,31 +38,6 @@ bool any_overlap(std::initializer_list<Range> outs, std::initializer_list<Range>
     return false;
 }
 
-rudnn_moe_status check_device(hipStream_t s, std::initializer_list<const void*> ptrs) {
-    int dev = -1;
-    if (s) {
-        if (hipStreamGetDevice(s, &dev) != hipSuccess) {
-            (void)hipGetLastError();
-            return RUDNN_MOE_ERR_DEVICE;
-        }
-    } else if (hipGetDevice(&dev) != hipSuccess) {
-        (void)hipGetLastError();
-        return RUDNN_MOE_ERR_DEVICE;
-    }
-    for (const void* p : ptrs) {
-        hipPointerAttribute_t a;
-        if (hipPointerGetAttributes(&a, p) != hipSuccess) {
-            (void)hipGetLastError();
-            return RUDNN_MOE_ERR_DEVICE;
-        }
-        if ((a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) || a.device != dev)
-            return RUDNN_MOE_ERR_DEVICE;
-    }
-    return RUDNN_MOE_OK;
-}
-
-rudnn_moe_status runtime(hipError_t e) { return e == hipSuccess ? RUDNN_MOE_OK : RUDNN_MOE_ERR_RUNTIME; }
-
 constexpr int64_t INT32_LIMIT = (int64_t)1 << 31;
 
 rudnn_moe_status check_route_args(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E,
@@ -126,6 +101,53 @@ rudnn_moe_status check_experts_rows(const rudnn_moe_experts* ex, int64_t rows) {
 }  // namespace
 
 namespace rudnn {
+
+rudnn_moe_status check_device(hipStream_t s, std::initializer_list<const void*> ptrs) {
+    int dev = -1;
+    if (s) {
+        if (hipStreamGetDevice(s, &dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return RUDNN_MOE_ERR_DEVICE;
+        }
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return RUDNN_MOE_ERR_DEVICE;
+    }
+    for (const void* p : ptrs) {
+        hipPointerAttribute_t a;
+        if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+            (void)hipGetLastError();
+            return RUDNN_MOE_ERR_DEVICE;
+        }
+        if ((a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) || a.device != dev)
+            return RUDNN_MOE_ERR_DEVICE;
+    }
+    return RUDNN_MOE_OK;
+}
+
+rudnn_moe_status runtime(hipError_t e) { return e == hipSuccess ? RUDNN_MOE_OK : RUDNN_MOE_ERR_RUNTIME; }
+
+rudnn_moe_status check_dispatch_args(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input,
+                                     rudnn_moe_dtype dt, int64_t H, const void* dispatched, const int32_t* offsets,
+                                     const int32_t* token_map) {
+    if (T < 0 || E < 1 || H < 1) return RUDNN_MOE_ERR_SHAPE;
+    if (k < 1 || k > E) return RUDNN_MOE_ERR_ARGUMENT;
+    if (!valid_dtype(dt)) return RUDNN_MOE_ERR_DTYPE;
+    if (E > MAX_EXPERTS || k > MAX_TOP_K || T * k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (!offsets) return RUDNN_MOE_ERR_ARGUMENT;
+    if (T > 0 && (!idx || !input || !dispatched || !token_map)) return RUDNN_MOE_ERR_ARGUMENT;
+    const size_t es = dtype_size(dt), pk = (size_t)(T * k), rb = (size_t)H * es;
+    if (any_overlap({{dispatched, pk * rb}, {offsets, 4 * (size_t)(E + 1)}, {token_map, pk * 4}},
+                    {{idx, pk * 4}, {input, (size_t)T * rb}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    return RUDNN_MOE_OK;
+}
+
+rudnn_moe_status dispatch_no_pairs(int32_t* offsets, int64_t E, hipStream_t stream) {
+    rudnn_moe_status st;
+    if ((st = check_device(stream, {offsets})) != RUDNN_MOE_OK) return st;
+    return runtime(launch_fill_i32(offsets, E + 1, 0, stream));
+}
 
 void timing_before(rudnn_moe_kernel k, hipStream_t s) {
     if (g_timing[k][0]) hipEventRecord(g_timing[k][0], s);
@@ -313,26 +335,15 @@ size_t rudnn_moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E) {
 rudnn_moe_status rudnn_moe_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input,
                                     rudnn_moe_dtype dt, int64_t H, void* dispatched, int32_t* offsets,
                                     int32_t* token_map, void* workspace, size_t workspace_size, hipStream_t stream) {
-    if (T < 0 || E < 1 || H < 1) return RUDNN_MOE_ERR_SHAPE;
-    if (k < 1 || k > E) return RUDNN_MOE_ERR_ARGUMENT;
-    if (!valid_dtype(dt)) return RUDNN_MOE_ERR_DTYPE;
-    if (E > MAX_EXPERTS || k > MAX_TOP_K || T * k >= INT32_LIMIT) return RUDNN_MOE_ERR_UNSUPPORTED;
-    if (!offsets) return RUDNN_MOE_ERR_ARGUMENT;
-    const size_t es = dtype_size(dt), pk = (size_t)(T * k), rb = (size_t)H * es;
+    rudnn_moe_status st = check_dispatch_args(idx, T, k, E, input, dt, H, dispatched, offsets, token_map);
+    if (st != RUDNN_MOE_OK) return st;
     const size_t need = rudnn_moe_dispatch_workspace_size(T, k, E);
-    if (T > 0) {
-        if (!idx || !input || !dispatched || !token_map) return RUDNN_MOE_ERR_ARGUMENT;
-        if (!workspace || workspace_size < need) return RUDNN_MOE_ERR_WORKSPACE;
-    }
-    if (any_overlap({{dispatched, pk * rb}, {offsets, 4 * (size_t)(E + 1)}, {token_map, pk * 4}, {workspace, need}},
-                    {{idx, pk * 4}, {input, (size_t)T * rb}}))
+    if (T > 0 && (!workspace || workspace_size < need)) return RUDNN_MOE_ERR_WORKSPACE;
+    const size_t es = dtype_size(dt), pk = (size_t)(T * k), rb = (size_t)H * es;
+    if (any_overlap({{workspace, need}}, {{dispatched, pk * rb}, {offsets, 4 * (size_t)(E + 1)}, {token_map, pk * 4},
+                                          {idx, pk * 4}, {input, (size_t)T * rb}}))
         return RUDNN_MOE_ERR_ARGUMENT;
-    rudnn_moe_status st;
-    if (T == 0) {
-        // no pairs: all offsets are zero
-        if ((st = check_device(stream, {offsets})) != RUDNN_MOE_OK) return st;
-        return runtime(launch_fill_i32(offsets, E + 1, 0, stream));
-    }
+    if (T == 0) return dispatch_no_pairs(offsets, E, stream);
     if ((st = check_device(stream, {idx, input, dispatched, offsets, token_map, workspace})) != RUDNN_MOE_OK) return st;
     return runtime(launch_dispatch(idx, T, k, E, input, rb, dispatched, offsets, token_map, (int32_t*)workspace,
                                    stream));

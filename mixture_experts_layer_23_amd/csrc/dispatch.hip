@@ -18,6 +18,8 @@
 //          in 16-byte vectors and written to the token's k dispatched rows (plain stores
 //          measured faster here than non-temporal ones).
 // HBM traffic: T*k*4 (ids, twice) + T*H*s (tokens, once) + T*k*H*s (rows) + T*k*4 (map).
+#include <mutex>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -204,3 +206,80 @@ hipError_t launch_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E,
 }
 
 }  // namespace rudnn
+
+// ---- rudnn_moe_dispatch_no_alloc: the per-chunk counts in a buffer the library owns ----
+//
+// `scratch` is a file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as an address (on the host
+// it is only a stand-in for the device symbol): the device address is looked up once per
+// device with hipGetSymbolAddress, that device current, and the kernels get that pointer.
+// Nothing in it needs clearing: the count kernel writes every entry the scan and rank kernels
+// read.  All calls on one GPU share the array, so calls that overlap on one GPU race.
+namespace rudnn {
+namespace {
+
+constexpr size_t DISPATCH_SCRATCH_BYTES = RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES;
+constexpr int MAX_DEVICES = 64;
+
+static __device__ __align__(256) int32_t scratch[DISPATCH_SCRATCH_BYTES / sizeof(int32_t)];
+
+std::mutex g_scratch_mutex;
+int32_t* g_scratch[MAX_DEVICES] = {};
+
+rudnn_moe_status stream_device(hipStream_t s, int* dev) {
+    const hipError_t e = s ? hipStreamGetDevice(s, dev) : hipGetDevice(dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return RUDNN_MOE_ERR_DEVICE;
+    }
+    return RUDNN_MOE_OK;
+}
+
+// The device address of `scratch` on `dev`, looked up on the first call for that device.
+rudnn_moe_status scratch_address(int dev, int32_t** out) {
+    if (dev < 0 || dev >= MAX_DEVICES) return RUDNN_MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) {
+            (void)hipGetLastError();
+            return RUDNN_MOE_ERR_DEVICE;
+        }
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return RUDNN_MOE_ERR_DEVICE;
+        }
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return RUDNN_MOE_ERR_RUNTIME;
+        }
+        g_scratch[dev] = (int32_t*)p;
+    }
+    *out = g_scratch[dev];
+    return RUDNN_MOE_OK;
+}
+
+}  // namespace
+}  // namespace rudnn
+
+using namespace rudnn;
+
+extern "C" rudnn_moe_status rudnn_moe_dispatch_no_alloc(const uint32_t* idx, int64_t T, int64_t k, int64_t E,
+                                                        const void* input, rudnn_moe_dtype dt, int64_t H,
+                                                        void* dispatched, int32_t* offsets, int32_t* token_map,
+                                                        hipStream_t stream) {
+    rudnn_moe_status st = check_dispatch_args(idx, T, k, E, input, dt, H, dispatched, offsets, token_map);
+    if (st != RUDNN_MOE_OK) return st;
+    if (dispatch_workspace_bytes(T * k, E) > DISPATCH_SCRATCH_BYTES) return RUDNN_MOE_ERR_UNSUPPORTED;
+    if (T == 0) return dispatch_no_pairs(offsets, E, stream);
+    if ((st = check_device(stream, {idx, input, dispatched, offsets, token_map})) != RUDNN_MOE_OK) return st;
+    int dev = -1;
+    int32_t* counts = nullptr;
+    if ((st = stream_device(stream, &dev)) != RUDNN_MOE_OK) return st;
+    if ((st = scratch_address(dev, &counts)) != RUDNN_MOE_OK) return st;
+    return runtime(launch_dispatch(idx, T, k, E, input, (size_t)H * dtype_size(dt), dispatched, offsets, token_map,
+                                   counts, stream));
+}

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/rudnn_moe.h"
 
 namespace rudnn {
@@ -41,6 +43,17 @@ inline size_t dispatch_workspace_bytes(int64_t pairs, int64_t E) {
     return dispatch_totals_offset(pairs, E) + align_up(sizeof(int32_t) * (size_t)E);
 }
 inline size_t dtype_size(rudnn_moe_dtype d) { return d == RUDNN_MOE_F32 ? 4 : 2; }
+
+// Host-side checks shared by the entry points (api.cpp).  check_device: every pointer is device
+// (or managed) memory of the stream's device.  check_dispatch_args: the argument checks of
+// rudnn_moe_dispatch except those of its workspace.  dispatch_no_pairs: the T = 0 case (all
+// offsets zero).
+rudnn_moe_status check_device(hipStream_t s, std::initializer_list<const void*> ptrs);
+rudnn_moe_status runtime(hipError_t e);
+rudnn_moe_status check_dispatch_args(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input,
+                                     rudnn_moe_dtype dt, int64_t H, const void* dispatched, const int32_t* offsets,
+                                     const int32_t* token_map);
+rudnn_moe_status dispatch_no_pairs(int32_t* offsets, int64_t E, hipStream_t stream);
 
 // Per-thread one-shot timing hook (rudnn_moe_time_next_launch).
 void timing_before(rudnn_moe_kernel k, hipStream_t s);

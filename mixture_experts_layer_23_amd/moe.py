@@ -84,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.rudnn_moe_dispatch_workspace_size.argtypes = [I64, I64, I64]
         L.rudnn_moe_dispatch_workspace_size.restype = SZ
         L.rudnn_moe_dispatch.argtypes = [P, I64, I64, I64, P, I32, I64, P, P, P, P, SZ, P]
+        L.rudnn_moe_dispatch_no_alloc.argtypes = [P, I64, I64, I64, P, I32, I64, P, P, P, P]
         L.rudnn_moe_experts_workspace_size.argtypes = [EXP, I64]
         L.rudnn_moe_experts_workspace_size.restype = SZ
         L.rudnn_moe_experts_forward.argtypes = [EXP, P, P, I64, P, P, SZ, P]
@@ -314,6 +315,24 @@ def dispatch(expert_indices: torch.Tensor, input: torch.Tensor, num_experts: int
     _check("rudnn_moe_dispatch", lib().rudnn_moe_dispatch(
         _ptr(expert_indices), T, k, num_experts, _ptr(input), _dt(input), H, _ptr(out.dispatched),
         _ptr(out.expert_offsets), _ptr(out.token_map), _ptr(workspace), workspace.numel(), _stream(input)))
+    return out
+
+
+# Bytes of the library's own per-device dispatch buffer (RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES).
+DISPATCH_NO_ALLOC_MAX_BYTES = 4 << 20
+
+
+def dispatch_no_alloc(expert_indices: torch.Tensor, input: torch.Tensor, num_experts: int,
+                      out: Dispatched) -> Dispatched:
+    """``dispatch`` through ``rudnn_moe_dispatch_no_alloc``: the caller passes every output buffer
+    and the library allocates nothing (its per-chunk counts live in a device array of its own)."""
+    expert_indices = _contig(expert_indices, "expert_indices")
+    input = _contig(input, "input")
+    T, k = expert_indices.shape
+    H = input.shape[1]
+    _check("rudnn_moe_dispatch_no_alloc", lib().rudnn_moe_dispatch_no_alloc(
+        _ptr(expert_indices), T, k, num_experts, _ptr(input), _dt(input), H, _ptr(out.dispatched),
+        _ptr(out.expert_offsets), _ptr(out.token_map), _stream(input)))
     return out
 
 

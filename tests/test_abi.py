@@ -28,10 +28,10 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
-    for required in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
+    for required in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_dispatch_no_alloc", "rudnn_moe_experts_forward", "rudnn_moe_combine",
                      "rudnn_moe_forward", "rudnn_moe_route_sigmoid_grouped", "rudnn_moe_forward_sigmoid_grouped",
                      "rudnn_moe_route_projected", "rudnn_moe_forward_projected", "rudnn_moe_selected_router_weights",
                      "rudnn_moe_selected_router_backward", "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward",
@@ -90,6 +90,32 @@ def test_dispatch_validation(L):
     assert call(tmap=None) == ARGUMENT
     assert call(disp=FAKE + 2**22 + 64) == ARGUMENT  # dispatched overlaps the input tokens
     assert call(ws=FAKE + 2**27 + 4) == ARGUMENT     # workspace overlaps the token map
+
+
+def test_dispatch_no_alloc_validation(L):
+    d = L.rudnn_moe_dispatch_no_alloc
+    args = dict(idx=FAKE, T=100, k=2, E=8, x=FAKE + 2**22, dt=2, H=64, disp=FAKE + 2**24, offs=FAKE + 2**26,
+                tmap=FAKE + 2**27)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return d(a["idx"], a["T"], a["k"], a["E"], a["x"], a["dt"], a["H"], a["disp"], a["offs"], a["tmap"], None)
+
+    assert call(H=0) == SHAPE
+    assert call(k=9) == ARGUMENT
+    assert call(dt=3) == DTYPE
+    assert call(tmap=None) == ARGUMENT
+    assert call(disp=FAKE + 2**22 + 64) == ARGUMENT
+    # the library's buffer holds the counts of at most RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES
+    limit = moe.DISPATCH_NO_ALLOC_MAX_BYTES
+    m = re.search(r"#define RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == limit
+    E, k = 128, 8
+    T_fit = max(T for T in range(1 << 21, 1 << 23, 1 << 15) if L.rudnn_moe_dispatch_workspace_size(T, k, E) <= limit)
+    big = T_fit + (1 << 15)
+    assert L.rudnn_moe_dispatch_workspace_size(big, k, E) > limit
+    assert call(T=big, k=k, E=E, disp=FAKE + 2**40, tmap=FAKE + 2**39, offs=FAKE + 2**38) == UNSUPPORTED
+    assert call(T=64, E=1024, k=64, offs=FAKE + 2**38) != UNSUPPORTED  # small calls fit at any E
 
 
 def _experts(E=8, H=64, I=96, dt=2, gate=FAKE, up=FAKE + 2**30, down=FAKE + 2**31):
