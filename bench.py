@@ -78,8 +78,10 @@ class Hip:
 
     def ms_if_recorded(self, a, b):
         """Elapsed time, or None when the pair was never recorded (its kernel did not launch)."""
+        self.L.hipEventSynchronize(b)
         v = ctypes.c_float()
         if self.L.hipEventElapsedTime(ctypes.byref(v), a, b) != 0:
+            self.L.hipGetLastError()  # the failed query must not leave an error for the next HIP call
             return None
         return float(v.value)
 
@@ -243,19 +245,27 @@ def main():
 
     # per-kernel breakdown (separate pass, every kernel timed)
     # what the softmax forward with ready logits launches
-    fwd_kernels = ["route", "dispatch_count", "dispatch_scan", "dispatch_rank", "dispatch_copy", "experts_plan",
+    fwd_kernels = ["route", "dispatch_count", "dispatch_scan", "dispatch_copy", "experts_plan",
                    "experts_gate_up", "experts_down", "combine", "experts_gate_up_reduce", "experts_down_reduce"]
     stage_ev = {kn: [(hip.event(), hip.event()) for _ in range(max(3, K // 4))] for kn in fwd_kernels}
     for i in range(max(3, K // 4)):
         for kn in fwd_kernels:
             moe.time_next_launch(kn, *stage_ev[kn][i])
         step()
+        for kn in fwd_kernels:  # a kernel this layer does not launch leaves its pair unrecorded
+            moe.time_next_launch(kn, None, None)
     torch.cuda.synchronize()
-    stage_ms = {kn: float(np.mean([hip.ms(a, b) for a, b in v])) for kn, v in stage_ev.items()}
+
+    def mean_recorded(pairs):
+        v = [hip.ms_if_recorded(a, b) for a, b in pairs]
+        v = [x for x in v if x is not None]
+        return float(np.mean(v)) if v else 0.0
+
+    stage_ms = {kn: mean_recorded(v) for kn, v in stage_ev.items()}
     dispatch_bytes = T * k * 4 * 2 + T * H * s + T * k * H * s + T * k * 4 + 4 * (E + 1)
     stages = {
         "route": {"us": stage_ms["route"] * 1e3, "bytes": T * E * s + T * k * (4 + s)},
-        "dispatch": {"us": sum(stage_ms[f"dispatch_{p}"] for p in ("count", "scan", "rank", "copy")) * 1e3,
+        "dispatch": {"us": sum(stage_ms[f"dispatch_{p}"] for p in ("count", "scan", "copy")) * 1e3,
                      "bytes": dispatch_bytes},
         "experts_gate_up": {"us": stage_ms["experts_gate_up"] * 1e3, "flops": gu_flops},
         "experts_down": {"us": stage_ms["experts_down"] * 1e3, "flops": dn_flops},
@@ -346,6 +356,41 @@ def main():
             us = float(np.median([hip.ms(a, b) for a, b in ev[name]])) * 1e3
             gbs = hbm_bytes[name] / (us / 1e6) / 1e9
             hbm[name] = {"us": us, "bytes": hbm_bytes[name], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+
+        # The whole routing+dispatch pass in its fused form: rudnn_moe_route_dispatch (routing with
+        # the per-chunk dispatch step, the scan, the copy with the map), then combine; caches
+        # evicted once before each pass.  Per-kernel times from a separate pass.
+        rd_kernels = ("route", "dispatch_scan", "dispatch_copy", "combine")
+        pass_ev = [(hip.event(), hip.event()) for _ in range(reps)]
+        kev = {n_: [(hip.event(), hip.event()) for _ in range(reps)] for n_ in rd_kernels}
+
+        def rd_pass():
+            moe.route_dispatch(lg2, k2, True, x2, out=d2, workspace=dws)
+            moe.combine(d2.dispatched, d2.token_map, wt2, out=o2)
+
+        for i in range(reps + 1):
+            flush()
+            if i > 0:
+                hip.record(pass_ev[i - 1][0], stream)
+            rd_pass()
+            if i > 0:
+                hip.record(pass_ev[i - 1][1], stream)
+        for i in range(reps):
+            flush()
+            for kn in rd_kernels:
+                moe.time_next_launch(kn, *kev[kn][i])
+            rd_pass()
+        torch.cuda.synchronize()
+        pass_us = float(np.median([hip.ms(a, b) for a, b in pass_ev])) * 1e3
+        k_us = {kn: float(np.median([hip.ms(a, b) for a, b in v])) * 1e3 for kn, v in kev.items()}
+        roof_us = (hbm_bytes["route"] + hbm_bytes["dispatch"] + hbm_bytes["combine"]) / (HBM_PEAK_GBS * 1e3)
+        hbm["fused_pass"] = {
+            "calls": "rudnn_moe_route_dispatch + rudnn_moe_combine, renormalize",
+            "us": pass_us, "tokens_per_s": T2 / (pass_us / 1e6),
+            "roofline_tokens_per_s": T2 / (roof_us / 1e6), "roofline_frac": roof_us / pass_us,
+            "kernels_us": k_us,
+            "route_and_scan_us": k_us["route"] + k_us["dispatch_scan"],
+        }
 
     # ---------------- group-limited sigmoid routing (section 10) ----------------
     sig = None

@@ -127,7 +127,8 @@ size_t rudnn_moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E);
  * Inside one expert this implementation orders rows by (t, j); the guide leaves that order
  * open, so callers must rely only on token_map.  Indices >= E are a caller error that is
  * contained: such a pair is not copied and combine yields a NaN row for its token.
- * workspace: at least rudnn_moe_dispatch_workspace_size(T, top_k, E) bytes, 256-B aligned.
+ * workspace: at least rudnn_moe_dispatch_workspace_size(T, top_k, E) bytes, 256-B aligned (per-chunk
+ * expert counts, the expert totals, and a 4-byte rank per pair).
  * Errors: SHAPE, ARGUMENT, DTYPE, UNSUPPORTED (E > 1024, T*k >= 2^31), WORKSPACE, DEVICE,
  * RUNTIME.
  */
@@ -137,6 +138,23 @@ rudnn_moe_status rudnn_moe_dispatch(const uint32_t* expert_indices, int64_t T, i
                                     size_t workspace_size, hipStream_t stream);
 
 /*
+ * route_dispatch -- section 4 routing followed by section 5 dispatch of the plan, in one call
+ * (route(logits, options) and then plan.dispatch(input)).  Writes exactly what rudnn_moe_route and
+ * then rudnn_moe_dispatch on its indices write: expert_indices and weights as rudnn_moe_route,
+ * dispatched, expert_offsets and token_map as rudnn_moe_dispatch (the same map).  Where the routing
+ * blocks can serve as dispatch chunks, the routing kernel also does dispatch's per-chunk counting
+ * and ranking, saving a pass.
+ *   logits [T, E] logits_dtype; input [T, H] dtype; outputs as in the two calls.
+ * workspace: at least rudnn_moe_dispatch_workspace_size(T, top_k, E) bytes, 256-B aligned.
+ * Errors: those of rudnn_moe_route and rudnn_moe_dispatch; overlapping buffers are ARGUMENT.
+ */
+rudnn_moe_status rudnn_moe_route_dispatch(const void* logits, rudnn_moe_dtype logits_dtype, int64_t T, int64_t E,
+                                          rudnn_moe_routing_options opt, const void* input, rudnn_moe_dtype dtype,
+                                          int64_t H, uint32_t* expert_indices, void* weights, void* dispatched,
+                                          int32_t* expert_offsets, int32_t* token_map, void* workspace,
+                                          size_t workspace_size, hipStream_t stream);
+
+/*
  * dispatch_no_alloc -- rudnn_moe_dispatch for callers that cannot allocate: code under HIP
  * graph capture, serving loops that must not call hipMalloc, harnesses that forbid it.  Same
  * arguments, results and errors as rudnn_moe_dispatch, without the workspace: the per-chunk
@@ -144,11 +162,11 @@ rudnn_moe_status rudnn_moe_dispatch(const uint32_t* expert_indices, int64_t T, i
  * holds on every GPU it runs on until the process ends (its device address is looked up on the
  * first call on each device).  The call allocates nothing.  A call whose
  * rudnn_moe_dispatch_workspace_size(T, top_k, E) exceeds that size returns
- * RUDNN_MOE_ERR_UNSUPPORTED (e.g. E = 128 allows T * top_k up to about 33.5 million pairs).
+ * RUDNN_MOE_ERR_UNSUPPORTED (e.g. E = 128 allows T * top_k up to about 4 million pairs).
  * All calls on one GPU share the array: calls that may overlap on one GPU (several host threads
  * or streams) race and must be ordered by the caller.
  */
-#define RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES ((size_t)4 << 20)
+#define RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES ((size_t)16 << 20)
 rudnn_moe_status rudnn_moe_dispatch_no_alloc(const uint32_t* expert_indices, int64_t T, int64_t top_k, int64_t E,
                                              const void* input, rudnn_moe_dtype dtype, int64_t H, void* dispatched,
                                              int32_t* expert_offsets, int32_t* token_map, hipStream_t stream);
@@ -423,10 +441,12 @@ const char* rudnn_moe_status_string(rudnn_moe_status s);
  */
 typedef RUDNN_MOE_ENUM {
     RUDNN_MOE_KERNEL_ROUTE = 0,
-    RUDNN_MOE_KERNEL_DISPATCH_COUNT = 1,
+    RUDNN_MOE_KERNEL_DISPATCH_COUNT = 1, /* per-chunk counts and ranks (a dispatch of its own; routing
+                                            with dispatch does this step in the routing kernel) */
     RUDNN_MOE_KERNEL_DISPATCH_SCAN = 2,
-    RUDNN_MOE_KERNEL_DISPATCH_RANK = 3,
-    RUDNN_MOE_KERNEL_DISPATCH_COPY = 4,
+    RUDNN_MOE_KERNEL_DISPATCH_RANK = 3,  /* not launched: the copy kernel forms the map (the number
+                                            is kept so the others keep theirs) */
+    RUDNN_MOE_KERNEL_DISPATCH_COPY = 4,  /* the rows and the token map */
     RUDNN_MOE_KERNEL_EXPERTS_PLAN = 5,
     RUDNN_MOE_KERNEL_EXPERTS_GATE_UP = 6,
     RUDNN_MOE_KERNEL_EXPERTS_DOWN = 7,

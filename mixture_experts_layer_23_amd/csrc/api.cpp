@@ -143,6 +143,26 @@ rudnn_moe_status check_dispatch_args(const uint32_t* idx, int64_t T, int64_t k, 
     return RUDNN_MOE_OK;
 }
 
+// Softmax routing followed by dispatch: in one pass where the routing blocks can serve as the
+// dispatch chunks (route_dispatch_chunk > 0), else the two one after the other.
+hipError_t route_and_dispatch(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E, int64_t k, bool renorm,
+                              uint32_t* idx, void* w, const void* input, size_t row_bytes, void* dispatched,
+                              int32_t* offsets, int32_t* token_map, void* ws, hipStream_t stream) {
+    const int64_t chunk = route_dispatch_chunk(T, E, k);
+    hipError_t e;
+    if (chunk > 0) {
+        e = launch_route(logits, ldt, T, E, k, renorm, idx, w, stream, ws);
+        if (e == hipSuccess)
+            e = launch_dispatch_after_local(idx, T, k, E, chunk, input, row_bytes, dispatched, offsets, token_map, ws,
+                                            stream);
+    } else {
+        e = launch_route(logits, ldt, T, E, k, renorm, idx, w, stream);
+        if (e == hipSuccess)
+            e = launch_dispatch(idx, T, k, E, input, row_bytes, dispatched, offsets, token_map, ws, stream);
+    }
+    return e;
+}
+
 rudnn_moe_status dispatch_no_pairs(int32_t* offsets, int64_t E, hipStream_t stream) {
     rudnn_moe_status st;
     if ((st = check_device(stream, {offsets})) != RUDNN_MOE_OK) return st;
@@ -329,7 +349,7 @@ rudnn_moe_status rudnn_moe_dispatch_backward(const void* d, rudnn_moe_dtype dt, 
 
 size_t rudnn_moe_dispatch_workspace_size(int64_t T, int64_t top_k, int64_t E) {
     if (T < 0 || top_k < 1 || E < 1) return 0;
-    return dispatch_workspace_bytes(T * top_k, E);
+    return dispatch_workspace_bytes(T, top_k, E);
 }
 
 rudnn_moe_status rudnn_moe_dispatch(const uint32_t* idx, int64_t T, int64_t k, int64_t E, const void* input,
@@ -345,8 +365,33 @@ rudnn_moe_status rudnn_moe_dispatch(const uint32_t* idx, int64_t T, int64_t k, i
         return RUDNN_MOE_ERR_ARGUMENT;
     if (T == 0) return dispatch_no_pairs(offsets, E, stream);
     if ((st = check_device(stream, {idx, input, dispatched, offsets, token_map, workspace})) != RUDNN_MOE_OK) return st;
-    return runtime(launch_dispatch(idx, T, k, E, input, rb, dispatched, offsets, token_map, (int32_t*)workspace,
-                                   stream));
+    return runtime(launch_dispatch(idx, T, k, E, input, rb, dispatched, offsets, token_map, workspace, stream));
+}
+
+rudnn_moe_status rudnn_moe_route_dispatch(const void* logits, rudnn_moe_dtype ldt, int64_t T, int64_t E,
+                                          rudnn_moe_routing_options opt, const void* input, rudnn_moe_dtype dt,
+                                          int64_t H, uint32_t* idx, void* w, void* dispatched, int32_t* offsets,
+                                          int32_t* token_map, void* workspace, size_t workspace_size,
+                                          hipStream_t stream) {
+    rudnn_moe_status st = check_route_args(logits, ldt, T, E, opt, idx, w);
+    if (st != RUDNN_MOE_OK) return st;
+    const int64_t k = opt.top_k;
+    if ((st = check_dispatch_args(idx, T, k, E, input, dt, H, dispatched, offsets, token_map)) != RUDNN_MOE_OK)
+        return st;
+    const size_t need = rudnn_moe_dispatch_workspace_size(T, k, E);
+    if (T > 0 && (!workspace || workspace_size < need)) return RUDNN_MOE_ERR_WORKSPACE;
+    const size_t es = dtype_size(dt), pk = (size_t)(T * k), rb = (size_t)H * es, ls = dtype_size(ldt);
+    // outputs (indices, weights, rows, offsets, map, workspace) against each other and the inputs
+    if (any_overlap({{idx, pk * 4}, {w, pk * ls}, {dispatched, pk * rb}, {offsets, 4 * (size_t)(E + 1)},
+                     {token_map, pk * 4}, {workspace, need}},
+                    {{logits, (size_t)(T * E) * ls}, {input, (size_t)T * rb}}))
+        return RUDNN_MOE_ERR_ARGUMENT;
+    if (T == 0) return dispatch_no_pairs(offsets, E, stream);
+    if ((st = check_device(stream, {logits, input, idx, w, dispatched, offsets, token_map, workspace})) !=
+        RUDNN_MOE_OK)
+        return st;
+    return runtime(route_and_dispatch(logits, ldt, T, E, k, opt.renormalize != 0, idx, w, input, rb, dispatched,
+                                      offsets, token_map, workspace, stream));
 }
 
 size_t rudnn_moe_experts_workspace_size(const rudnn_moe_experts* ex, int64_t rows) {
@@ -556,9 +601,10 @@ rudnn_moe_status forward_common(const rudnn_moe_experts* ex, const void* input, 
         e = launch_route_sigmoid_grouped(logits, ldt, bias, T, E, k, sig->groups, sig->selected_groups,
                                          sig->group_top_two != 0, sig->renormalize != 0, sig->scale, idx, w, stream);
     else
-        e = launch_route(logits, ldt, T, E, k, renormalize != 0, idx, w, stream);
-    if (e == hipSuccess)
-        e = launch_dispatch(idx, T, k, E, input, (size_t)H * es, disp, offsets, map, (int32_t*)(ws + L.dws), stream);
+        e = route_and_dispatch(logits, ldt, T, E, k, renormalize != 0, idx, w, input, (size_t)H * es, disp, offsets,
+                               map, ws + L.dws, stream);
+    if (e == hipSuccess && (router || sig))
+        e = launch_dispatch(idx, T, k, E, input, (size_t)H * es, disp, offsets, map, ws + L.dws, stream);
     if (e == hipSuccess) e = launch_experts(ex, disp, offsets, T * k, y, ws + L.ews, stream);
     if (e == hipSuccess) e = launch_combine(y, ex->dtype, map, w, ldt, T, k, H, output, stream);
     return runtime(e);

@@ -179,6 +179,7 @@ __device__ __forceinline__ void route_row(const typename RouteBits<LT>::raw (&ra
             if (nan_row) {
                 // NaN row: NaN weights, indices 0..k-1 (every probability NaN, read as a full tie)
                 idx[row * k + j] = (uint32_t)j;
+                si[j] = (uint32_t)j;  // si keeps the stored ids (read by the dispatch epilogue)
                 w[row * k + j] = from_f32<LT>(__builtin_nanf(""));
             } else {
                 idx[row * k + j] = si[j];
@@ -341,6 +342,7 @@ __device__ __forceinline__ void route_row_sorted(const uint16_t (&raw)[NPER], in
         for (int j = l; j < k; j += G) {
             if (nan_row) {
                 idx[row * k + j] = (uint32_t)j;
+                si[j] = (uint32_t)j;
                 w[row * k + j] = from_f32<LT>(__builtin_nanf(""));
             } else {
                 idx[row * k + j] = si[j];

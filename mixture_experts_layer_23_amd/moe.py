@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
         L.rudnn_moe_dispatch_workspace_size.restype = SZ
         L.rudnn_moe_dispatch.argtypes = [P, I64, I64, I64, P, I32, I64, P, P, P, P, SZ, P]
         L.rudnn_moe_dispatch_no_alloc.argtypes = [P, I64, I64, I64, P, I32, I64, P, P, P, P]
+        L.rudnn_moe_route_dispatch.argtypes = [P, I32, I64, I64, RoutingOptions, P, I32, I64, P, P, P, P, P, P, SZ, P]
         L.rudnn_moe_experts_workspace_size.argtypes = [EXP, I64]
         L.rudnn_moe_experts_workspace_size.restype = SZ
         L.rudnn_moe_experts_forward.argtypes = [EXP, P, P, I64, P, P, SZ, P]
@@ -318,8 +319,33 @@ def dispatch(expert_indices: torch.Tensor, input: torch.Tensor, num_experts: int
     return out
 
 
+def route_dispatch(logits: torch.Tensor, top_k: int, renormalize: bool, input: torch.Tensor, out: Dispatched | None = None,
+                   workspace=None):
+    """``route`` then ``dispatch`` of its plan in one call (``rudnn_moe_route_dispatch``).  Returns
+    ``(expert_indices [T, k] int32 holding the uint32 ids, weights [T, k] logits dtype, Dispatched)``."""
+    logits = _contig(logits, "logits")
+    input = _contig(input, "input")
+    T, E = logits.shape
+    H = input.shape[1]
+    dev = input.device
+    idx = torch.empty(T, top_k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, top_k, dtype=logits.dtype, device=dev)
+    if out is None:
+        out = Dispatched(torch.empty(T * top_k, H, dtype=input.dtype, device=dev),
+                         torch.empty(E + 1, dtype=torch.int32, device=dev),
+                         torch.empty(T, top_k, dtype=torch.int32, device=dev))
+    need = lib().rudnn_moe_dispatch_workspace_size(T, top_k, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("rudnn_moe_route_dispatch", lib().rudnn_moe_route_dispatch(
+        _ptr(logits), _dt(logits), T, E, RoutingOptions(top_k, int(renormalize)), _ptr(input), _dt(input), H, _ptr(idx),
+        _ptr(w), _ptr(out.dispatched), _ptr(out.expert_offsets), _ptr(out.token_map), _ptr(workspace), workspace.numel(),
+        _stream(input)))
+    return idx, w, out
+
+
 # Bytes of the library's own per-device dispatch buffer (RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES).
-DISPATCH_NO_ALLOC_MAX_BYTES = 4 << 20
+DISPATCH_NO_ALLOC_MAX_BYTES = 16 << 20
 
 
 def dispatch_no_alloc(expert_indices: torch.Tensor, input: torch.Tensor, num_experts: int,

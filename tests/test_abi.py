@@ -28,10 +28,10 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
-    for required in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_dispatch_no_alloc", "rudnn_moe_experts_forward", "rudnn_moe_combine",
+    for required in ("rudnn_moe_route", "rudnn_moe_dispatch", "rudnn_moe_dispatch_no_alloc", "rudnn_moe_route_dispatch", "rudnn_moe_experts_forward", "rudnn_moe_combine",
                      "rudnn_moe_forward", "rudnn_moe_route_sigmoid_grouped", "rudnn_moe_forward_sigmoid_grouped",
                      "rudnn_moe_route_projected", "rudnn_moe_forward_projected", "rudnn_moe_selected_router_weights",
                      "rudnn_moe_selected_router_backward", "rudnn_moe_combine_backward", "rudnn_moe_dispatch_backward",
@@ -111,11 +111,37 @@ def test_dispatch_no_alloc_validation(L):
     m = re.search(r"#define RUDNN_MOE_DISPATCH_NO_ALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
     assert m and int(m.group(1)) << int(m.group(2)) == limit
     E, k = 128, 8
-    T_fit = max(T for T in range(1 << 21, 1 << 23, 1 << 15) if L.rudnn_moe_dispatch_workspace_size(T, k, E) <= limit)
+    T_fit = max(T for T in range(1 << 14, 1 << 23, 1 << 14) if L.rudnn_moe_dispatch_workspace_size(T, k, E) <= limit)
     big = T_fit + (1 << 15)
     assert L.rudnn_moe_dispatch_workspace_size(big, k, E) > limit
     assert call(T=big, k=k, E=E, disp=FAKE + 2**40, tmap=FAKE + 2**39, offs=FAKE + 2**38) == UNSUPPORTED
     assert call(T=64, E=1024, k=64, offs=FAKE + 2**38) != UNSUPPORTED  # small calls fit at any E
+
+
+def test_route_dispatch_validation(L):
+    f = L.rudnn_moe_route_dispatch
+    ws = L.rudnn_moe_dispatch_workspace_size(100, 2, 8)
+    args = dict(lg=FAKE, ldt=2, T=100, E=8, k=2, x=FAKE + 2**22, dt=2, H=64, idx=FAKE + 2**23, w=FAKE + 2**23 + 4096,
+                disp=FAKE + 2**24, offs=FAKE + 2**26, tmap=FAKE + 2**27, ws=FAKE + 2**28, wsz=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["lg"], a["ldt"], a["T"], a["E"], opts(a["k"]), a["x"], a["dt"], a["H"], a["idx"], a["w"], a["disp"],
+                 a["offs"], a["tmap"], a["ws"], a["wsz"], None)
+
+    assert call(E=0) == SHAPE
+    assert call(H=0) == SHAPE
+    assert call(k=9) == ARGUMENT
+    assert call(ldt=7) == DTYPE
+    assert call(dt=7) == DTYPE
+    assert call(E=2048) == UNSUPPORTED
+    assert call(wsz=ws - 1) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(tmap=None) == ARGUMENT
+    assert call(idx=FAKE + 64) == ARGUMENT             # indices overlap the logits
+    assert call(disp=FAKE + 2**22 + 64) == ARGUMENT    # dispatched rows overlap the input
+    assert call(ws=FAKE + 2**23 + 8) == ARGUMENT       # workspace overlaps the indices
+    assert L.rudnn_moe_dispatch_workspace_size(100, 2, 8) >= 4 * 100 * 2  # a rank per pair
 
 
 def _experts(E=8, H=64, I=96, dt=2, gate=FAKE, up=FAKE + 2**30, down=FAKE + 2**31):

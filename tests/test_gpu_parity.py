@@ -133,6 +133,51 @@ def test_dispatch_parity_full_size(name):
     assert torch.equal(d.dispatched.cpu().view(ib), rdisp.view(ib))
 
 
+ROUTE_DISPATCH_CASES = {
+    # routing blocks of 1024 threads serve as dispatch chunks (128 rows x 8 pairs), both renorm modes
+    "route_dispatch_renorm": (WORKLOADS["route_dispatch"], True),
+    "route_dispatch_plain": (WORKLOADS["route_dispatch"], False),
+    # a ragged last routing block (T not a multiple of 128 rows)
+    "route_dispatch_ragged": (WORKLOADS["route_dispatch"].with_T(9001).replace(H=256), True),
+    # 256-thread routing blocks (32 rows x 8 pairs) and a skewed load with empty experts, fp16
+    "skewed": (WORKLOADS["skewed"], False),
+    # NaN and tied rows; one chunk
+    "tiny": (WORKLOADS["tiny"], True),
+    "mixtral": (WORKLOADS["mixtral"], True),
+    "decode": (WORKLOADS["decode"], True),
+    # 1024 experts: 4 rows per 256-thread block are too few pairs, so routing and dispatch run apart ...
+    "e1024_apart": (Workload("e1024a", 300, 64, None, 1024, 8, "bf16", "f32", (True,), 1.1, 211), True),
+    # ... and with enough rows, 1024-thread routing blocks of 16 rows serve as the chunks
+    "e1024_fused": (Workload("e1024f", 5000, 64, None, 1024, 8, "bf16", "f32", (False,), 1.1, 212), False),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTE_DISPATCH_CASES))
+def test_route_dispatch_equals_route_then_dispatch(name):
+    """rudnn_moe_route_dispatch writes exactly what rudnn_moe_route followed by rudnn_moe_dispatch
+    writes (indices, weights, rows, offsets and map bit for bit), and the map is the oracle's."""
+    w, renorm = ROUTE_DISPATCH_CASES[name]
+    say("route_dispatch", name, "T", w.T, "E", w.E, "k", w.top_k, "H", w.H)
+    logits, _ = make_logits(w)
+    x = make_tokens(w, DEV)
+    lg = logits.to(DEV)
+    idx1, w1 = moe.route(lg, w.top_k, renorm)
+    d1 = moe.dispatch(idx1, x, w.E)
+    idx2, w2, d2 = moe.route_dispatch(lg, w.top_k, renorm, x)
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+    wb = torch.int32 if w2.dtype == torch.float32 else torch.int16
+    assert torch.equal(w1.view(wb), w2.view(wb))
+    assert torch.equal(d1.expert_offsets, d2.expert_offsets)
+    assert torch.equal(d1.token_map, d2.token_map)
+    xb = torch.int32 if x.dtype == torch.float32 else torch.int16
+    assert torch.equal(d1.dispatched.view(xb), d2.dispatched.view(xb))
+    ridx = idx2.cpu().numpy().astype(np.uint32)
+    _, roffs, rmap, _ = oracle.dispatch(ridx, torch.zeros(w.T, 1), w.E, copy_rows=False)
+    assert np.array_equal(d2.expert_offsets.cpu().numpy(), roffs)
+    assert np.array_equal(d2.token_map.cpu().numpy(), rmap)
+
+
 def test_dispatch_invalid_indices_are_contained():
     say("dispatch-invalid")
     w = WORKLOADS["route_dispatch"].with_T(300).replace(H=64, special=(0,) * 7)
