@@ -235,8 +235,9 @@ typedef struct {
 
 /*
  * route_sigmoid_grouped -- section 10 (route_sigmoid_grouped(logits, bias, options) ->
- * RoutingPlan).  For each row t of logits [T, E], in FP32: s_e = 1 / (1 + exp(-x_e)); the
- * corrected score c_e = s_e + bias[e] (bias only steers the selection).  A group's score is
+ * RoutingPlan).  For each row t of logits [T, E], in FP32: s_e = 1 / (1 + exp(-x_e)),
+ * evaluated in FP64 and rounded once to FP32 (so the same on every run and device); the
+ * corrected score c_e = s_e + bias[e] in FP32 (bias only steers the selection).  A group's score is
  * its largest c, or the sum of its two largest with group_top_two; the selected_groups
  * highest-scoring groups are chosen (equal scores: lower group id), then the top_k experts
  * of those groups by c (equal c: lower id), listed by descending c.  weights[t, j] = s of

@@ -4,8 +4,8 @@
 //
 // A group of G adjacent lanes owns one row of logits [T, E] (the lane layout of the softmax
 // router: lane l of the group holds experts [l * NPER, (l + 1) * NPER), NPER = 16).  Per row, in FP32:
-//   1. s_e = 1 / (1 + exp(-x_e)); corrected score c_e = s_e + bias_e (the bias only steers the
-//      choice).  s and c go to LDS.
+//   1. s_e = 1 / (1 + exp(-x_e)), evaluated in FP64 and rounded once to FP32 (sigmoid_f32);
+//      corrected score c_e = s_e + bias_e (the bias only steers the choice).  s and c go to LDS.
 //   2. Group scores from LDS, lane l taking groups l, l + G, ...: the largest c of the group,
 //      or the sum of its two largest (group_top_two).  A NaN corrected score or a NaN group
 //      score makes the row a NaN row (indices 0..k-1, NaN weights).
@@ -32,6 +32,13 @@ __device__ __forceinline__ uint64_t sig_key(float v, uint32_t id) {
     const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
     return ((uint64_t)ord << 32) | (uint32_t)(0xffffffffu - id);
 }
+
+// The sigmoid rounded once to FP32 from an FP64 evaluation: FP64 exp and a correctly rounded FP64
+// division put the FP64 value within a few FP64 ulps of the exact one, so the FP32 result is the
+// correctly rounded sigmoid unless the exact value lies within about 2^-50 (relative) of an FP32
+// rounding midpoint.  An FP32 reciprocal of 1 + exp(-x) would leave the last FP32 bit uncertain,
+// and with it the order of near-equal scores.  +inf -> 1, -inf -> 0, NaN -> NaN.
+__device__ __forceinline__ float sigmoid_f32(float x) { return (float)(1.0 / (1.0 + exp(-(double)x))); }
 
 // VEC: every lane's NPER logits (and bias entries) are whole, 16-byte aligned vectors inside the
 // row (E % NPER == 0): one vector load each, and the scores go to LDS as 16-byte stores.
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __
         float sgv[NPER];
 #pragma unroll
         for (int i = 0; i < NPER; ++i) {
-            sgv[i] = __builtin_amdgcn_rcpf(1.0f + expf(-xv[i]));  // +inf -> 1, -inf -> 0, NaN -> NaN
+            sgv[i] = sigmoid_f32(xv[i]);
             c[i] = bias ? sgv[i] + bv[i] : sgv[i];
             bad |= in && c[i] != c[i];
         }
@@ -100,7 +107,7 @@ __global__ __launch_bounds__(SIG_THREADS) void route_sigmoid_kernel(const LT* __
             const int e = e0 + s;
             const int ec = e < E ? e : E - 1;
             const float xv = to_f32(x[ec]);
-            const float sg = __builtin_amdgcn_rcpf(1.0f + expf(-xv));  // +inf -> 1, -inf -> 0, NaN -> NaN
+            const float sg = sigmoid_f32(xv);
             const float cv = bias ? sg + bias[ec] : sg;
             c[s] = cv;
             if (e < E) {

@@ -2,11 +2,11 @@
 forward that uses it: the HIP library through its C ABI against the CPU oracle on the same
 seeded inputs.
 
-Both sides decide in FP32, but their FP32 sigmoids need not agree to the last bit, so two
-experts (or groups) whose corrected scores lie within a few ulp of each other may be taken in
-either order.  Rows where the indices differ must be such near-tie rows (checked on the
-oracle's own FP32 scores recomputed here), be few, and still select a valid set; every other
-row matches bit for bit.  Weights follow the tolerance rule of the other parity tests."""
+Both sides decide in FP32 on the sigmoid rounded once to FP32 from a higher-precision
+evaluation, so the indices must match bit for bit on every row, deliberate ties and NaN rows
+included.  The FP32 sigmoid itself is checked bit for bit on every bf16 and f16 logit value
+and on a million random FP32 ones.  Weights follow the tolerance rule of the other parity
+tests."""
 import json
 import math
 import os
@@ -14,7 +14,6 @@ import os
 import numpy as np
 import pytest
 import torch
-from scipy.special import expit
 
 from mixture_experts_layer_23_amd import moe
 from mixture_experts_layer_23_amd.inputs import (SIGMOID_SPECIAL_KINDS, WORKLOADS, SigmoidRouting, Workload,
@@ -24,7 +23,6 @@ from parity_util import assert_close, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-NEAR = 1e-6  # corrected scores closer than this may be ordered either way (a few FP32 ulp)
 
 _CACHE = {}
 
@@ -52,30 +50,6 @@ def gpu_route(logits, bias, o):
     return idx.cpu().numpy().astype(np.int64), w.cpu()
 
 
-def scores(logits, bias, groups, top_two):
-    """FP32 corrected scores and group scores as the guide defines them (sigmoid in double
-    rounded once to FP32, the FP32 bias added in FP32)."""
-    c = expit(logits.double().numpy()).astype(np.float32)
-    if bias is not None:
-        c = (c + bias.numpy()).astype(np.float32)
-    T, E = c.shape
-    cg = -np.sort(-c.reshape(T, groups, E // groups), axis=2)
-    gs = cg[:, :, 0] if not top_two else (cg[:, :, 0] + cg[:, :, 1]).astype(np.float32)
-    return c, gs
-
-
-def near_tie_row(c, gs, sel, k, groups):
-    """True if the group boundary or the expert ranking up to k has a gap below NEAR."""
-    g_sorted = -np.sort(-gs.astype(np.float64))
-    if np.any(np.abs(np.diff(g_sorted[:sel + 1])) < NEAR):
-        return True
-    per = len(c) // groups
-    chosen = np.argsort(-gs.astype(np.float64), kind="stable")[:sel]
-    elig = np.concatenate([np.arange(g * per, (g + 1) * per) for g in chosen])
-    e_sorted = -np.sort(-c[elig].astype(np.float64))
-    return bool(np.any(np.abs(np.diff(e_sorted[:k + 1])) < NEAR))
-
-
 def compare_route(logits, bias, sg: SigmoidRouting, k, dt, special=None):
     o = opts(sg, k)
     idx, wt = gpu_route(logits, bias, o)
@@ -83,21 +57,11 @@ def compare_route(logits, bias, sg: SigmoidRouting, k, dt, special=None):
                                                 sg.renormalize, sg.scale)
     ridx = ridx.astype(np.int64)
     diff = np.nonzero((idx != ridx).any(axis=1))[0]
-    if len(diff):
-        c, gs = scores(logits, bias, sg.groups, sg.group_top_two)
-        for t in diff:
-            assert near_tie_row(c[t], gs[t], sg.selected_groups, k, sg.groups), f"row {t}: {idx[t]} vs {ridx[t]}"
-            assert sorted(set(idx[t].tolist())) == sorted(idx[t].tolist()), f"row {t}: repeated expert"
-        assert len(diff) <= max(2, len(idx) // 1000), f"{len(diff)} rows differ"
-        say("near-tie rows ordered differently:", len(diff))
-    same = np.setdiff1d(np.arange(len(idx)), diff)
-    assert_close(wt[same], rwt[same], dt, "weights")
+    assert len(diff) == 0, f"{len(diff)} rows differ, first {diff[0]}: {idx[diff[0]]} vs {ridx[diff[0]]}"
+    assert_close(wt, rwt, dt, "weights")
     if special is not None:
         for t in special.get("nan", []):
             assert idx[t].tolist() == list(range(k)) and torch.isnan(wt[t]).all()
-        for kind in ("expert_tie", "group_tie"):
-            for t in special.get(kind, []):
-                assert t not in diff, f"deliberate tie row {t} ({kind}) resolved differently"
     return idx, wt
 
 
@@ -106,6 +70,36 @@ def test_route_full_size():
     say("sigmoid route", w.name, "T", w.T, "E", w.E, "k", w.top_k, w.sigmoid)
     logits, bias, special = inputs(w)
     compare_route(logits, bias, w.sigmoid, w.top_k, w.logits_dtype, special)
+
+
+def sigmoid_probe_logits():
+    """FP32 logits [T, 64]: every bf16 and every f16 value (exactly representable in FP32), a
+    million random FP32 bit patterns and a million uniform values over [-110, 40] (the range
+    where the FP32 sigmoid is neither 0 nor 1, down to its subnormals); NaNs left out (a NaN
+    makes the whole row a NaN row), zeros pad the last row."""
+    rng = np.random.default_rng(2027)
+    bf = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    hf = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float32)
+    rnd = rng.integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    act = rng.uniform(-110.0, 40.0, 1 << 20).astype(np.float32)
+    v = np.concatenate([bf, hf, rnd, act])
+    v = v[~np.isnan(v)]
+    v = np.concatenate([v, np.zeros((-len(v)) % 64, np.float32)])
+    return torch.from_numpy(v.reshape(-1, 64))
+
+
+def test_sigmoid_values_bit_exact():
+    """With k = E, one group, no renormalisation and scale 1, each FP32 weight is the FP32
+    sigmoid of its expert's logit itself, so the weights compare the two sigmoids bit for bit."""
+    logits = sigmoid_probe_logits()
+    say("sigmoid values", tuple(logits.shape))
+    o = moe.GroupRoutingOptions(64, 1, 1, 0, 0, 1.0)
+    idx, wt = gpu_route(logits, None, o)
+    ridx, rwt, _ = oracle.route_sigmoid_grouped(logits, None, 64, 1, 1, False, False, 1.0)
+    assert np.array_equal(idx, ridx.astype(np.int64))
+    bad = np.nonzero((wt.view(torch.int32) != rwt.view(torch.int32)).numpy())
+    assert len(bad[0]) == 0, (f"{len(bad[0])} sigmoids differ, first logit "
+                              f"{float(logits[bad[0][0], idx[bad[0][0], bad[1][0]]])!r}")
 
 
 EDGE = [
