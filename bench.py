@@ -510,6 +510,33 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+FORWARD_KERNELS = ("route", "dispatch_count", "dispatch_scan", "dispatch_copy", "experts_plan", "experts_gate_up",
+                   "experts_gate_up_reduce", "experts_down", "experts_down_reduce", "combine")
+
+
+def kernel_breakdown(moe, hip, fn, reps=5, kernels=FORWARD_KERNELS):
+    """Mean µs of each kernel ``fn`` launches (HIP events on its launch stream through the
+    library's timing hook), over ``reps`` calls; kernels that never launched are left out."""
+    import numpy as np
+    import torch
+
+    ev = {kn: [(hip.event(), hip.event()) for _ in range(reps)] for kn in kernels}
+    for i in range(reps):
+        for kn in kernels:
+            moe.time_next_launch(kn, *ev[kn][i])
+        fn()
+        for kn in kernels:  # a kernel this call does not launch leaves its pair unrecorded
+            moe.time_next_launch(kn, None, None)
+    torch.cuda.synchronize()
+    out = {}
+    for kn, pairs in ev.items():
+        v = [hip.ms_if_recorded(a, b) for a, b in pairs]
+        v = [x for x in v if x is not None]
+        if v:
+            out[kn] = float(np.mean(v)) * 1e3
+    return out
+
+
 def measure_other_forwards(moe, hip, stream, dev, steps=20):
     """rudnn_moe_forward on the decode-shaped, skewed and tiny layers (inputs resident in HBM,
     back-to-back steps): ms per forward, tokens/s, and the expert weights streamed per second
@@ -552,6 +579,8 @@ def measure_other_forwards(moe, hip, stream, dev, steps=20):
                "expert_TFLOPps": flops / (ms / 1e3) / 1e12}
         if w.dtype != "f32":  # the FP32 layer runs on the vector FMAs, not the matrix cores
             ent["mfma_frac"] = ent["expert_TFLOPps"] / MFMA_PEAK_TFLOPS[w.dtype]
+        ent["kernels_us"] = kernel_breakdown(
+            moe, hip, lambda: ex.forward(x, lg, w.top_k, renorm, out=out, workspace=ws))
         res[name] = ent
         del lg, x, g, u, d, ex, out, ws
         torch.cuda.empty_cache()
