@@ -87,23 +87,29 @@ class Hip:
 
 
 class ProfilerRegion:
-    """roctx resume/pause around the timed steps: under ``rocprofv3 --selected-regions`` the kernel
-    trace then holds exactly the timed launches (outside rocprofv3 these calls do nothing)."""
+    """roctx marks around the timed steps: a range named ``bench timed steps`` (under
+    ``rocprofv3 --marker-trace`` the kernels that run inside it are exactly the timed launches)
+    and resume/pause for ``--selected-regions``.  Outside rocprofv3 these calls do nothing."""
+
+    NAME = b"bench timed steps"
 
     def __init__(self):
         try:
             self.L = ctypes.CDLL("librocprofiler-sdk-roctx.so.1")
             self.L.roctxProfilerResume.argtypes = [ctypes.c_uint64]
             self.L.roctxProfilerPause.argtypes = [ctypes.c_uint64]
-        except OSError:
+            self.L.roctxRangePushA.argtypes = [ctypes.c_char_p]
+        except (OSError, AttributeError):
             self.L = None
 
     def resume(self):
         if self.L is not None:
             self.L.roctxProfilerResume(0)
+            self.L.roctxRangePushA(self.NAME)
 
     def pause(self):
         if self.L is not None:
+            self.L.roctxRangePop()
             self.L.roctxProfilerPause(0)
 
 
