@@ -21,8 +21,12 @@
  *     RUDNN_MOE_ERR_RUNTIME (the HIP runtime refused a launch after earlier launches of the
  *     same call were enqueued).
  *   - T = 0 (no tokens) is a successful no-op.
- *   - No global state: calls are reentrant and may run concurrently on different streams
- *     with different buffers.  (The optional timing hook at the end is per host thread.)
+ *   - Calls are reentrant and may run concurrently on different streams with different
+ *     buffers.  The library keeps only set-once process state (each kernel's LDS-size
+ *     attribute, each device's compute-unit count, both written once with the same value),
+ *     and for rudnn_moe_dispatch_no_alloc its per-device scratch array (calls of that entry
+ *     point that overlap on one GPU race on it).  The optional timing hook at the end is per
+ *     host thread.
  */
 #ifndef RUDNN_MOE_H
 #define RUDNN_MOE_H

@@ -38,6 +38,7 @@
 // SPLIT_SLOTS / R, each at least SPLIT_MIN_STEPS K steps), so the last round fills the machine.
 // A segment stores its FP32 partial sums; a small reduce kernel then adds the S partials of each
 // split tile in segment order (deterministic) and applies the epilogue.
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -883,15 +884,19 @@ size_t experts_workspace_bytes(int64_t E, int64_t H, int64_t I, rudnn_moe_dtype 
            split_partials_bytes(dt);
 }
 
-// Compute units of the current device (the size of one round of tiles).
+// Compute units of the current device (the size of one round of tiles), cached per device
+// (atomics: threads may fill the same entry at once, always with the same value).
 static int device_cus() {
-    static int cache[64] = {};
+    static std::atomic<int> cache[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (dev < 64) cache[dev] = cus;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 

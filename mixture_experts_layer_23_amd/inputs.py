@@ -224,6 +224,19 @@ def make_logits(w: Workload):
     return logits, special
 
 
+def make_tied_logits(T: int, E: int, dtype: str, seed: int, levels: int = 0) -> torch.Tensor:
+    """Router logits with no separation between entries, so that equal values are frequent:
+    N(0, 1) rounded to ``dtype`` (bf16 holds 128 values per binade, so a row of 1024 repeats
+    many), or with ``levels`` > 0 drawn uniformly from the ``levels`` integers centred on 0
+    (every row then is mostly ties).  CPU tensor [T, E] in ``dtype``."""
+    rng = _np_rng(seed, 0)
+    if levels > 0:
+        vals = (rng.integers(0, levels, (T, E)) - levels // 2).astype(np.float32)
+    else:
+        vals = _round_to(rng.standard_normal((T, E), dtype=np.float32), dtype)
+    return torch.from_numpy(vals).to(DTYPES[dtype])
+
+
 def make_sigmoid_logits(w: Workload):
     """Router logits and FP32 correction bias for a group-limited sigmoid workload.
 

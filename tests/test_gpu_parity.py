@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from mixture_experts_layer_23_amd import moe
-from mixture_experts_layer_23_amd.inputs import DTYPES, WORKLOADS, Workload, make_experts, make_tokens
+from mixture_experts_layer_23_amd.inputs import DTYPES, WORKLOADS, Workload, make_experts, make_tied_logits, make_tokens
 from mixture_experts_layer_23_amd.inputs import make_logits as _make_logits
 from oracle import oracle
 from parity_util import assert_close, full_oracle_forward, say
@@ -88,6 +88,27 @@ def test_route_edge_shapes(T, E, k, dt, renorm):
     idx, wt = gpu_route(logits, k, renorm)
     ridx, rwt, _ = oracle.route(logits, k, renorm)
     assert np.array_equal(idx, ridx.astype(np.int64))
+    assert_close(wt, rwt, dt, "weights")
+
+
+TIED_CASES = [
+    # (T, E, k, dtype, levels): bf16 rows of 512 and 1024 experts (32 and 64 lanes per row), where
+    # equal logits are common, and coarse integer logits where nearly every comparison is a tie
+    (300, 1024, 8, "bf16", 0), (129, 1024, 64, "bf16", 0), (200, 512, 16, "bf16", 0), (97, 1024, 1, "bf16", 0),
+    (150, 1024, 8, "bf16", 7), (150, 256, 12, "bf16", 5), (64, 1024, 64, "f16", 3), (80, 96, 8, "f32", 4),
+]
+
+
+@pytest.mark.parametrize("T,E,k,dt,levels", TIED_CASES)
+@pytest.mark.parametrize("renorm", [True, False])
+def test_route_with_tied_logits(T, E, k, dt, levels, renorm):
+    """No separation between logits: equal logits are resolved by the lower id on both sides, and
+    distinct ones keep their order through the double softmax of the oracle."""
+    say("route-tied", T, E, k, dt, levels, renorm)
+    logits = make_tied_logits(T, E, dt, 800 + T + E + k + levels, levels)
+    idx, wt = gpu_route(logits, k, renorm)
+    ridx, rwt, _ = oracle.route(logits, k, renorm)
+    assert np.array_equal(idx, ridx.astype(np.int64)), f"{int((idx != ridx).any(axis=1).sum())} rows differ"
     assert_close(wt, rwt, dt, "weights")
 
 
