@@ -8,9 +8,11 @@
 //   dgate_e = dg^T x,  dup_e = du^T x,  ddown_e = dy^T h     (FP32, sums over the expert's rows)
 // silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z).
 //
-// One MFMA kernel serves all five products: C[m, n] = sum_k A(m, k) B(n, k) on BM x BN tiles
+// Two MFMA kernels serve the five products, C[m, n] = sum_k A(m, k) B(n, k) on BM x BN tiles
 // (256 x 256, eight wavefronts of 128 x 64), K staged 128 bytes per row (v_mfma_f32_32x32x16 for
-// BF16/F16, 32x32x2f32 for FP32).  An operand is either "K-major" (k contiguous: staged as
+// BF16/F16, 32x32x2f32 for FP32): for 16-bit types the DMA form below (operands copied straight
+// into LDS; fragments of an operand that is not K-major read with the LDS transpose read), and
+// for FP32 (or operands beyond 2 GiB) the register-staged kernel described next.  An operand is either "K-major" (k contiguous: staged as
 // 16-byte pieces) or "X-major" (its row/column index contiguous): a thread then loads 4 rows of k
 // by CE consecutive x (CE = elements per 16 bytes), transposes them in registers and stores CE
 // runs of 4 k values into the [x][k] LDS tile.  The operand tiles go through registers (two
@@ -168,6 +170,118 @@ struct Epi {
     void* h;              // EPI_SWIGLU: [rows, I] dtype
 };
 
+// The tile of workgroup blockIdx.x: ROWS tiles the experts' dispatched rows (m-tiles from the
+// device-side plan) by N; KROWS takes every (expert, m-tile, n-tile) with the expert's rows as K.
+// False if the workgroup has no tile.
+struct TileSel {
+    int e, m0, n0, mlim, nlim, kb, kn;  // expert, tile origin, valid rows and columns, K origin and length
+    int64_t row0;                       // ROWS: first dispatched row of the tile
+};
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ bool pick_tile(const Plan& plan, const int32_t* __restrict__ offsets, int rows, int M,
+                                          int N, int K, int E, int NT, int MT, TileSel& t) {
+    t.row0 = 0;
+    if (MODE == ROWS) {
+        const int64_t L = blockIdx.x, Mt = L / NT;
+        if (Mt >= plan.mt_begin[E]) return false;
+        int lo = 0, hi = E - 1;  // largest e with mt_begin[e] <= Mt
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (plan.mt_begin[mid] <= Mt)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        t.e = lo;
+        const int mt = (int)(Mt - plan.mt_begin[t.e]);
+        t.n0 = (int)(L % NT) * BN;
+        t.m0 = 0;
+        t.row0 = plan.row_begin[t.e] + (int64_t)mt * BM;
+        t.mlim = min(BM, plan.row_count[t.e] - mt * BM);
+        t.kb = 0, t.kn = K;
+    } else {
+        const int64_t L = blockIdx.x;
+        t.e = (int)(L / ((int64_t)MT * NT));
+        const int r = (int)(L % ((int64_t)MT * NT));
+        t.m0 = (r / NT) * BM, t.n0 = (r % NT) * BN;
+        t.mlim = min(BM, M - t.m0);
+        const int a = min(max(offsets[t.e], 0), rows), b = min(max(offsets[t.e + 1], 0), rows);
+        t.kb = a, t.kn = max(b - a, 0);
+    }
+    t.nlim = min(BN, N - t.n0);
+    return true;
+}
+
+// The products' epilogue, shared by both GEMM kernels.  The accumulator blocks hold C^T (the
+// operands went in B fragment first) in ROWS mode and C in KROWS mode; see the two branches.
+template <typename T, int MODE, int EPI, int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[FM][FN], int wm, int wn, int lane, int mlim, int nlim,
+                                         int e, int M, int m0, int n0, int64_t row0, int N, const Epi& ep) {
+    const int fr = lane & 31, fh = lane >> 5;
+    if constexpr (MODE == KROWS) {
+        // Weight gradients (FP32): the operands went in token fragment first, so lane l holds
+        // column l % 32 and rows 8 (v / 4) + 4 fh + v % 4 of each block; a store instruction writes
+        // two whole 128-byte row pieces.
+        static_assert(EPI == EPI_F32, "weight gradients are FP32");
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int nl = wn * TN + j * 32 + fr;
+                if (nl >= nlim) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int ml = wm * TM + i * 32 + 8 * (v / 4) + 4 * fh + v % 4;
+                    if (ml < mlim)
+                        reinterpret_cast<float*>(ep.c)[((int64_t)e * M + m0 + ml) * ep.ldc + n0 + nl] = acc[i][j][v];
+                }
+            }
+        return;
+    }
+    // ---- epilogue: lane holds row m = fr of each 32-row block, columns 8 (v / 4) + 4 fh + v % 4 ----
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int ml = wm * TM + i * 32 + fr;
+        if (ml >= mlim) continue;
+        const int64_t crow = MODE == ROWS ? row0 + ml : (int64_t)e * M + m0 + ml;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn * TN + j * 32 + 8 * q + 4 * fh;
+                if (nl >= nlim) continue;  // N is a multiple of 4: a run of 4 is wholly in or out
+                const int n = n0 + nl;
+                const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
+                            v3 = acc[i][j][4 * q + 3];
+                if (EPI == EPI_F32) {
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.c) + crow * ep.ldc + n) =
+                        make_float4(v0, v1, v2, v3);
+                } else if (EPI == EPI_DT) {
+                    store4<T>(reinterpret_cast<T*>(ep.c) + crow * ep.ldc + n, v0, v1, v2, v3);
+                } else {  // dh -> dg, du, h; N = I
+                    const float dh[4] = {v0, v1, v2, v3};
+                    const float* gr = ep.gu + crow * 2 * (int64_t)N + n;
+                    const float4 g4 = *reinterpret_cast<const float4*>(gr);
+                    const float4 u4 = *reinterpret_cast<const float4*>(gr + N);
+                    const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
+                    float dgv[4], duv[4], hv[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float g = gv[t], u = uv[t];
+                        const float s = 1.f / (1.f + expf(-g));
+                        dgv[t] = dh[t] * u * (s * (1.f + g * (1.f - s)));
+                        duv[t] = dh[t] * (g * s);
+                        hv[t] = g * s * u;
+                    }
+                    T* dg = reinterpret_cast<T*>(ep.dgu) + crow * 2 * (int64_t)N + n;
+                    store4<T>(dg, dgv[0], dgv[1], dgv[2], dgv[3]);
+                    store4<T>(dg + N, duv[0], duv[1], duv[2], duv[3]);
+                    store4<T>(reinterpret_cast<T*>(ep.h) + crow * (int64_t)N + n, hv[0], hv[1], hv[2], hv[3]);
+                }
+            }
+    }
+}
+
 // C = A B^T on BM x BN tiles; see the file comment.
 template <typename T, typename C, int MODE, int EPI, bool AK, bool BK>
 __global__ __launch_bounds__(C::THREADS) void gemm_kernel(Opnd A, Opnd B, int M, int N, int K, int E, Plan plan,
@@ -191,36 +305,10 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(Opnd A, Opnd B, int M,
     extern __shared__ __align__(1024) unsigned char lds[];
 
     // ---- which tile ----
-    int e, m0, n0, mlim, kb, kn;  // expert, tile origin, valid rows, K origin and length
-    int64_t row0 = 0;             // ROWS: first dispatched row of the tile
-    if (MODE == ROWS) {
-        const int64_t L = blockIdx.x, Mt = L / NT;
-        if (Mt >= plan.mt_begin[E]) return;
-        int lo = 0, hi = E - 1;  // largest e with mt_begin[e] <= Mt
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (plan.mt_begin[mid] <= Mt)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        e = lo;
-        const int mt = (int)(Mt - plan.mt_begin[e]);
-        n0 = (int)(L % NT) * BN;
-        m0 = 0;
-        row0 = plan.row_begin[e] + (int64_t)mt * BM;
-        mlim = min(BM, plan.row_count[e] - mt * BM);
-        kb = 0, kn = K;
-    } else {
-        const int64_t L = blockIdx.x;
-        e = (int)(L / ((int64_t)MT * NT));
-        const int r = (int)(L % ((int64_t)MT * NT));
-        m0 = (r / NT) * BM, n0 = (r % NT) * BN;
-        mlim = min(BM, M - m0);
-        const int a = min(max(offsets[e], 0), rows), b = min(max(offsets[e + 1], 0), rows);
-        kb = a, kn = max(b - a, 0);
-    }
-    const int nlim = min(BN, N - n0);
+    TileSel ts;
+    if (!pick_tile<MODE, BM, BN>(plan, offsets, rows, M, N, K, E, NT, MT, ts)) return;
+    const int e = ts.e, m0 = ts.m0, n0 = ts.n0, mlim = ts.mlim, nlim = ts.nlim, kb = ts.kb, kn = ts.kn;
+    const int64_t row0 = ts.row0;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -405,68 +493,192 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(Opnd A, Opnd B, int M,
         if (kt + 1 < KT) step(kt + 1, even);
     }
 
-    if constexpr (MODE == KROWS) {
-        // Weight gradients (FP32): the operands went in token fragment first, so lane l holds
-        // column l % 32 and rows 8 (v / 4) + 4 fh + v % 4 of each block; a store instruction writes
-        // two whole 128-byte row pieces.
-        static_assert(EPI == EPI_F32, "weight gradients are FP32");
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int nl = wn * TN + j * 32 + fr;
-                if (nl >= nlim) continue;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int ml = wm * TM + i * 32 + 8 * (v / 4) + 4 * fh + v % 4;
-                    if (ml < mlim)
-                        reinterpret_cast<float*>(ep.c)[((int64_t)e * M + m0 + ml) * ep.ldc + n0 + nl] = acc[i][j][v];
-                }
+    epilogue<T, MODE, EPI, FM, FN, TM, TN>(acc, wm, wn, lane, mlim, nlim, e, M, m0, n0, row0, N, ep);
+}
+
+
+// ---------------------------------------------------------------------------------------
+// DMA form (16-bit types).  Both operand tiles go straight from global memory into LDS with
+// buffer_load_dwordx4 ... lds (no register staging), K 64 elements per step, two stages:
+//   K-major tile (k contiguous in memory): [x][k], 256 rows of 128 bytes, chunk c of row x at
+//   slot c ^ swz(x) -- the forward GEMM's layout; an MFMA fragment is one 16-byte LDS read.
+//   X-major tile (x contiguous in memory): kept as it lies, [k][x], 64 k rows of 512 bytes (256
+//   x values), chunk c (8 x values) of row k at slot c ^ sxm(k).  Its MFMA fragments are read
+//   with the LDS transpose read ds_read_b64_tr_b16: in each group of 16 lanes, lane i reads 4
+//   16-bit values at its own address (row i of a 16 x 4 block) and lane j receives column
+//   j % 4 of rows j / 4, j / 4 + 4, j / 4 + 8, j / 4 + 12 (measured on gfx950).  Lane i naming
+//   (k0 + i / 4, x0 + 4 (i % 4)) therefore gives lane j the values (k0 .. k0 + 3, x0 + j): two
+//   such reads make the 8 consecutive k of one x that an MFMA operand lane holds.
+// One wavefront copy moves 1 KiB: 8 rows of a K-major tile or 2 k rows of an X-major one; a
+// step is 32 copies per operand, dealt to the wavefronts round-robin.  A copy reads rows of one
+// operand part only (the part boundary is a multiple of 8 rows), so its buffer is uniform.
+// Rows or x past the tile's valid range re-read its last valid row or chunk (their outputs are
+// never stored); k past the end is zero-filled.
+constexpr int XROWB = 512;  // bytes of one staged X-major k row
+
+// A transpose read touches, per group of 16 lanes, 4 consecutive k rows and 4 consecutive
+// chunks, the wavefront's other groups the next 4 chunks or the k rows 8 further on; with this
+// swizzle those 32 pieces sit in 32 different slots.
+__device__ __forceinline__ int sxm(int k) { return 4 * (k & 3) + 16 * ((k >> 3) & 1); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One 16-byte LDS-direct copy per lane: the wavefront's 64 pieces land at dst + 16 lane.  (A
+// __device__ function, not a lambda: the buffer intrinsics exist only in device code.)
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, unsigned char* dst) {
+    constexpr int GFX9_RSRC_WORD3 = 0x00020000;  // 32-bit data format, no swizzle
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, GFX9_RSRC_WORD3),
+        (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+// The LDS transpose read (ds_read_b64_tr_b16) of the 8 bytes at p; see the DMA form's comment.
+__device__ __forceinline__ v4s read_tr(const unsigned char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+}
+
+template <typename T, typename C, int MODE, int EPI, bool AK, bool BK>
+__global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(Opnd A, Opnd B, int M, int N, int K, int E, Plan plan,
+                                                              const int32_t* __restrict__ offsets, int rows, int NT,
+                                                              int MT, Epi ep) {
+    static_assert(sizeof(T) == 2, "the DMA form stages 16-bit operands");
+    constexpr int BM = C::BM, BN = C::BN, THREADS = C::THREADS, NWAVES = THREADS / 64;
+    constexpr int TM = BM / C::WM, TN = BN / C::WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    constexpr int BKE = ROWB / 2;              // K elements per step (64)
+    constexpr int TILE = 256 * ROWB;           // bytes of one operand tile per stage
+    constexpr int SLOTS = 64 / NWAVES;         // copies per wavefront per step (32 per operand)
+    static_assert(BM == 256 && BN == 256 && 64 % NWAVES == 0, "operand tiles of 256 x 64, whole copies per wave");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wavefront tiles are whole MFMA blocks");
+    typedef typename Mma<T>::frag frag;
+    extern __shared__ __align__(1024) unsigned char lds[];
+
+    TileSel ts;
+    if (!pick_tile<MODE, BM, BN>(plan, offsets, rows, M, N, K, E, NT, MT, ts)) return;
+    const int e = ts.e, m0 = ts.m0, n0 = ts.n0, mlim = ts.mlim, nlim = ts.nlim, kb = ts.kb, kn = ts.kn;
+    const int64_t row0 = ts.row0;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+
+    // The first element of operand part `part` of expert ee (copy offsets are bytes from it).
+    auto part_base = [&](const Opnd& o, int part, int ee) __attribute__((always_inline)) {
+        return (void*)(reinterpret_cast<const T*>(part ? o.p1 : o.p0) + (int64_t)ee * o.estride);
+    };
+    // Copy q of this wavefront for step kt of operand `is_a` into stage st.
+    auto copy = [&](const Opnd& o, bool is_a, bool kmajor, int xlim, unsigned char* st, int gi, int kt)
+        __attribute__((always_inline)) {
+        unsigned char* dst = st + gi * 1024;
+        const int k0 = kt * BKE;
+        if (kmajor) {
+            // rows x = 8 gi + lane / 8 of the tile, chunk slot lane % 8
+            const int x = 8 * gi + lane / 8, xc = min(x, xlim - 1);
+            const int xf = min(8 * gi, xlim - 1);  // the copy's first row: its part
+            const int64_t of = is_a ? (MODE == ROWS ? row0 + xf : (int64_t)(m0 + xf)) : (int64_t)(n0 + xf);
+            const int part = of >= o.split;
+            const int64_t oc = is_a ? (MODE == ROWS ? row0 + xc : (int64_t)(m0 + xc)) : (int64_t)(n0 + xc);
+            const int kk = k0 + ((lane & 7) ^ swz(x)) * 8;
+            if (kk < kn) {
+                const uint32_t off = (uint32_t)((oc - (part ? o.split : 0)) * o.ld + kb + kk) * 2u;
+                dma16(part_base(o, part, MODE == ROWS && is_a ? 0 : e), off, dst);
+            } else {
+                *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
             }
-        return;
-    }
-    // ---- epilogue: lane holds row m = fr of each 32-row block, columns 8 (v / 4) + 4 fh + v % 4 ----
+        } else {
+            // k rows 2 gi + lane / 32 of the step, chunk slot lane % 32
+            const int kr = 2 * gi + (lane >> 5), k = k0 + kr;
+            const int kf = min(k0 + 2 * gi, max(kn - 1, 0));  // the copy's first row: its part
+            const int part = (kb + kf) >= o.split;
+            const int c = min((lane & 31) ^ sxm(kr), (xlim - 1) >> 3);
+            const int64_t xo = is_a ? (int64_t)(m0 + 8 * c) : (int64_t)(n0 + 8 * c);
+            if (k < kn) {
+                const uint32_t off = (uint32_t)((kb + k - (part ? o.split : 0)) * o.ld + xo) * 2u;
+                dma16(part_base(o, part, MODE == KROWS ? 0 : e), off, dst);
+            } else {
+                *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int ml = wm * TM + i * 32 + fr;
-        if (ml >= mlim) continue;
-        const int64_t crow = MODE == ROWS ? row0 + ml : (int64_t)e * M + m0 + ml;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int nl = wn * TN + j * 32 + 8 * q + 4 * fh;
-                if (nl >= nlim) continue;  // N is a multiple of 4: a run of 4 is wholly in or out
-                const int n = n0 + nl;
-                const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
-                            v3 = acc[i][j][4 * q + 3];
-                if (EPI == EPI_F32) {
-                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.c) + crow * ep.ldc + n) =
-                        make_float4(v0, v1, v2, v3);
-                } else if (EPI == EPI_DT) {
-                    store4<T>(reinterpret_cast<T*>(ep.c) + crow * ep.ldc + n, v0, v1, v2, v3);
-                } else {  // dh -> dg, du, h; N = I
-                    const float dh[4] = {v0, v1, v2, v3};
-                    const float* gr = ep.gu + crow * 2 * (int64_t)N + n;
-                    const float4 g4 = *reinterpret_cast<const float4*>(gr);
-                    const float4 u4 = *reinterpret_cast<const float4*>(gr + N);
-                    const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
-                    float dgv[4], duv[4], hv[4];
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // Per-lane fragment offsets.  K-major: row fr of a 32-row block, chunk (2 ks + fh) ^ swz(fr).
+    // X-major: the transpose read of lane l (group g = l / 16, i = l % 16) for 32-x block xb and
+    // half r of substep ks: k = 16 ks + 8 (g / 2) + 4 r + i / 4, x = 32 xb + 16 (g % 2) + 4 (i % 4),
+    // at byte k * 512 + ((x / 8) ^ sxm(k)) * 16 + (x % 8) * 2 = tr_base + (16 ks + 4 r) * 512 +
+    // ((xb ^ tr_sw) << 6).
+    const int fr = lane & 31, fh = lane >> 5;
+    const int tg = lane >> 4, ti = lane & 15;
+    const int tr_base = (8 * (tg >> 1) + (ti >> 2)) * XROWB + (2 * (tg & 1) + ((ti & 3) >> 1)) * 16 + 8 * (ti & 1);
+    const int tr_sw = (ti >> 2) + 4 * (tg >> 1);
+    auto frag_k = [&](const unsigned char* t, int row, int ks) __attribute__((always_inline)) {
+        return *reinterpret_cast<const frag*>(t + (row + fr) * ROWB + (((ks * 2 + fh) ^ swz(fr)) * 16));
+    };
+    auto frag_x = [&](const unsigned char* t, int xb, int ks) __attribute__((always_inline)) {
+        const unsigned char* p = t + tr_base + ks * 16 * XROWB + ((xb ^ tr_sw) << 6);
+        const v4s lo = read_tr(p), hi = read_tr(p + 4 * XROWB);
+        frag f;
+        __builtin_memcpy(&f, &lo, 8);
+        __builtin_memcpy(reinterpret_cast<unsigned char*>(&f) + 8, &hi, 8);
+        return f;
+    };
+
+    // Step kt: the copies of step kt + 1 go out over the first two MFMA substeps (into the stage
+    // read in step kt - 1), and the fragments of substep ks + 1 are read while the MFMAs of
+    // substep ks run.
+    auto issue_part = [&](int kt, int q0, int q1) __attribute__((always_inline)) {
+        unsigned char* st = lds + (kt & 1) * 2 * TILE;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const float g = gv[t], u = uv[t];
-                        const float s = 1.f / (1.f + expf(-g));
-                        dgv[t] = dh[t] * u * (s * (1.f + g * (1.f - s)));
-                        duv[t] = dh[t] * (g * s);
-                        hv[t] = g * s * u;
-                    }
-                    T* dg = reinterpret_cast<T*>(ep.dgu) + crow * 2 * (int64_t)N + n;
-                    store4<T>(dg, dgv[0], dgv[1], dgv[2], dgv[3]);
-                    store4<T>(dg + N, duv[0], duv[1], duv[2], duv[3]);
-                    store4<T>(reinterpret_cast<T*>(ep.h) + crow * (int64_t)N + n, hv[0], hv[1], hv[2], hv[3]);
-                }
-            }
+        for (int q = q0; q < q1; ++q) {
+            const int g = wave + q * NWAVES;  // 0..63: A copies, then B copies
+            if (g < 32)
+                copy(A, true, AK, mlim, st, g, kt);
+            else
+                copy(B, false, BK, nlim, st + TILE, g - 32, kt);
+        }
+    };
+    const int KT = (kn + BKE - 1) / BKE;
+    if (KT > 0) issue_part(0, 0, SLOTS);
+    for (int kt = 0; kt < KT; ++kt) {
+        wait_vmcnt<0>();  // this wavefront's copies of step kt have landed
+        __syncthreads();  // everyone's have; everyone is done with the other stage (step kt - 1)
+        const unsigned char* ta = lds + (kt & 1) * 2 * TILE;
+        const unsigned char* tb = ta + TILE;
+        frag fa[2][FM], fb[2][FN];
+        auto fetch = [&](int ks, int buf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                fa[buf][i] = AK ? frag_k(ta, wm * TM + i * 32, ks) : frag_x(ta, (wm * TM) / 32 + i, ks);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                fb[buf][j] = BK ? frag_k(tb, wn * TN + j * 32, ks) : frag_x(tb, (wn * TN) / 32 + j, ks);
+        };
+        fetch(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < BKE / 16; ++ks) {
+            if (kt + 1 < KT && ks < 2) issue_part(kt + 1, ks * SLOTS / 2, (ks + 1) * SLOTS / 2);
+            if (ks + 1 < BKE / 16) fetch(ks + 1, (ks + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = MODE == ROWS ? Mma<T>::run(fb[ks & 1][j], fa[ks & 1][i], acc[i][j])
+                                             : Mma<T>::run(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+
+    epilogue<T, MODE, EPI, FM, FN, TM, TN>(acc, wm, wn, lane, mlim, nlim, e, M, m0, n0, row0, N, ep);
 }
 
 }  // namespace bwd
@@ -483,6 +695,11 @@ size_t experts_backward_workspace_bytes(int64_t E, int64_t I, rudnn_moe_dtype dt
 
 namespace {
 
+#ifndef RUDNN_BWD_DMA
+#define RUDNN_BWD_DMA 1
+#endif
+constexpr bool bwd_dma_enabled() { return RUDNN_BWD_DMA != 0; }
+
 // Tiles: products over the dispatched rows (ROWS) and the weight gradients (KROWS).
 #ifndef RUDNN_BWD_ROWS_TILE
 #define RUDNN_BWD_ROWS_TILE 256, 256, 2, 4
@@ -493,17 +710,33 @@ namespace {
 typedef bwd::Cfg<RUDNN_BWD_ROWS_TILE> RowsCfg;
 typedef bwd::Cfg<RUDNN_BWD_KROWS_TILE> KRowsCfg;
 
+// C = A B^T for one product; a_rows / b_rows: rows of each part of A / B in memory (their byte
+// extents decide whether the 16-bit DMA form's 32-bit buffer offsets reach every element).
 template <typename T, int MODE, int EPI, bool AK, bool BK>
 void gemm(bwd::Opnd A, bwd::Opnd B, int M, int N, int K, int E, bwd::Plan plan, const int32_t* offsets, int rows,
-          bwd::Epi ep, rudnn_moe_kernel kid, hipStream_t s) {
+          bwd::Epi ep, int64_t a_rows, int64_t b_rows, rudnn_moe_kernel kid, hipStream_t s) {
     typedef typename std::conditional<MODE == bwd::ROWS, RowsCfg, KRowsCfg>::type C;
     const int NT = (N + C::BN - 1) / C::BN, MT = (M + C::BM - 1) / C::BM;
     const int64_t blocks = MODE == bwd::ROWS ? ((int64_t)rows / C::BM + E) * NT : (int64_t)E * MT * NT;
     if (blocks <= 0) return;
+    timing_before(kid, s);
+    constexpr int64_t OFFSET_LIMIT = 0x7fffffff;
+    if constexpr (sizeof(T) == 2) {
+        if (bwd_dma_enabled() && a_rows * A.ld * 2 <= OFFSET_LIMIT && b_rows * B.ld * 2 <= OFFSET_LIMIT) {
+            constexpr int LDS = 4 * 256 * bwd::ROWB;  // two stages of two 32 KiB operand tiles
+            static const hipError_t attr = hipFuncSetAttribute(
+                (const void*)bwd::gemm_dma_kernel<T, C, MODE, EPI, AK, BK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                LDS);
+            (void)attr;
+            bwd::gemm_dma_kernel<T, C, MODE, EPI, AK, BK><<<dim3((unsigned)blocks), dim3(C::THREADS), LDS, s>>>(
+                A, B, M, N, K, E, plan, offsets, rows, NT, MT, ep);
+            timing_after(kid, s);
+            return;
+        }
+    }
     static const hipError_t attr = hipFuncSetAttribute((const void*)bwd::gemm_kernel<T, C, MODE, EPI, AK, BK>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     (void)attr;
-    timing_before(kid, s);
     bwd::gemm_kernel<T, C, MODE, EPI, AK, BK><<<dim3((unsigned)blocks), dim3(C::THREADS), C::LDS_BYTES, s>>>(
         A, B, M, N, K, E, plan, offsets, rows, NT, MT, ep);
     timing_after(kid, s);
@@ -530,27 +763,27 @@ void run(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int
     if (!cache)
         gemm<T, bwd::ROWS, bwd::EPI_F32, true, true>({x, x, H, 0, NOSPLIT}, {ex->gate, ex->up, H, IH, I}, R, 2 * I, H,
                                                      E, plan, offsets, R,
-                                                     {gu, 2 * (int64_t)I, nullptr, nullptr, nullptr},
+                                                     {gu, 2 * (int64_t)I, nullptr, nullptr, nullptr}, R, I,
                                                      RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_GU, s);
     // dh = dy down_e (B(n = i, k = c) = down[e, c, i]: X-major), epilogue -> dg | du, h
     gemm<T, bwd::ROWS, bwd::EPI_SWIGLU, true, false>({dy, dy, H, 0, NOSPLIT}, {ex->down, ex->down, I, IH, NOSPLIT}, R, I,
-                                                     H, E, plan, offsets, R, {nullptr, 0, gu, dgu, hbuf},
+                                                     H, E, plan, offsets, R, {nullptr, 0, gu, dgu, hbuf}, R, H,
                                                      RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DH, s);
     // dx = [dg | du] [gate; up]  (B(n = c, k = i') = gate[e, i', c] or up[e, i' - I, c]: X-major)
     gemm<T, bwd::ROWS, bwd::EPI_DT, true, false>({dgu, dgu, 2 * (int64_t)I, 0, NOSPLIT}, {ex->gate, ex->up, H, IH, I}, R,
-                                                 H, 2 * I, E, plan, offsets, R, {dx, H, nullptr, nullptr, nullptr},
-                                                 RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DX, s);
+                                                 H, 2 * I, E, plan, offsets, R, {dx, H, nullptr, nullptr, nullptr}, R,
+                                                 I, RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DX, s);
     // dgate_e = dg^T x, dup_e = du^T x  (both X-major, K = the expert's rows)
     gemm<T, bwd::KROWS, bwd::EPI_F32, false, false>({dgu, dgu, 2 * (int64_t)I, 0, NOSPLIT}, {x, x, H, 0, NOSPLIT}, I, H,
-                                                    0, E, plan, offsets, R, {dgate, H, nullptr, nullptr, nullptr},
-                                                    RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DW, s);
+                                                    0, E, plan, offsets, R, {dgate, H, nullptr, nullptr, nullptr}, R,
+                                                    R, RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DW, s);
     gemm<T, bwd::KROWS, bwd::EPI_F32, false, false>({dgu + I, dgu + I, 2 * (int64_t)I, 0, NOSPLIT},
                                                     {x, x, H, 0, NOSPLIT}, I, H, 0, E, plan, offsets, R,
-                                                    {dup, H, nullptr, nullptr, nullptr},
+                                                    {dup, H, nullptr, nullptr, nullptr}, R, R,
                                                     RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DW, s);
     // ddown_e = dy^T h
     gemm<T, bwd::KROWS, bwd::EPI_F32, false, false>({dy, dy, H, 0, NOSPLIT}, {hbuf, hbuf, I, 0, NOSPLIT}, H, I, 0, E,
-                                                    plan, offsets, R, {ddown, I, nullptr, nullptr, nullptr},
+                                                    plan, offsets, R, {ddown, I, nullptr, nullptr, nullptr}, R, R,
                                                     RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DW, s);
 }
 

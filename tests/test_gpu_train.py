@@ -169,6 +169,10 @@ BWD_LAYERS = {
     "bf16_small": Workload("eb_bf16", 300, 256, 512, 8, 2, "bf16", "bf16", (True,), None, 1002),
     "f16_ragged": Workload("eb_f16", 77, 136, 72, 33, 5, "f16", "f16", (False,), None, 1003),
     "bf16_skewed": Workload("eb_skew", 600, 264, 136, 16, 4, "bf16", "bf16", (True,), 1.5, 1004),
+    # several m-, n- and K-tiles per product (K 64 per step), ragged expert row counts
+    "bf16_multi_tile": Workload("eb_multi", 700, 512, 1024, 6, 2, "bf16", "bf16", (True,), 1.2, 1008),
+    # dims that are multiples of 8 but not of 64 (K and x tails), skewed load, fp16
+    "f16_multi_ragged": Workload("eb_multi_r", 900, 392, 200, 5, 3, "f16", "f16", (False,), 1.0, 1009),
 }
 
 
