@@ -52,7 +52,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #ifndef RUDNN_DMA_SPREAD
-#define RUDNN_DMA_SPREAD 2
+#define RUDNN_DMA_SPREAD 1
 #endif
 #ifndef RUDNN_SPLIT_MIN_STEPS
 #define RUDNN_SPLIT_MIN_STEPS 8
@@ -263,7 +263,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // global form against the LDS-read counter as well and then waits for every outstanding LDS
 // read (lgkmcnt 0) before each MFMA group; with buffer copies it waits for exactly the operand
 // fragments each MFMA needs.  The copies of one step are numbered as slots (token groups first, then
-// weight groups) and dealt to the wavefronts round-robin, so each wave owns SLOTS copies.
+// weight groups) and dealt round-robin to the first half of the wavefronts only, one per SIMD
+// (wavefronts w and w + 4 of the eight share a SIMD): a copying wavefront stalls while its
+// copies queue for issue, and its SIMD's other wavefront keeps the matrix core busy meanwhile.
+// With every wavefront copying, all eight stalled together at the start of each step (measured:
+// Mixtral-shaped experts 2.521-2.523 ms with half the wavefronts copying, 2.557-2.561 ms with all).
 // A row past the end of its matrix re-reads the last row (such rows are never stored); in the
 // last step of a K that is not a multiple of BK, chunks at k >= K are zeroed instead of copied.
 // Offsets from a tile's base pointers are 32-bit: a tile spans at most a few MB of a matrix.
@@ -328,8 +332,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int KS = BK / 16;             // MFMA steps per staged tile
     constexpr int A_BYTES = BM * ROWB, STAGE_BYTES = (BM + NB) * ROWB;
-    constexpr int SLOTS = (BM + NB) * ROWB / 1024 / NWAVES;  // copies per wave per stage
-    static_assert((BM + NB) * ROWB % (1024 * NWAVES) == 0, "copies must split evenly over the wavefronts");
+    constexpr int CW = NWAVES / 2;                           // copying wavefronts, one per SIMD
+    constexpr int SLOTS = (BM + NB) * ROWB / 1024 / CW;      // copies per copying wave per stage
+    static_assert((BM + NB) * ROWB % (1024 * CW) == 0, "copies must split evenly over the wavefronts");
     static_assert(BM * ROWB % 1024 == 0 && BN * ROWB % 1024 == 0, "regions are whole 1 KiB copies");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are made of 32x32 MFMA blocks");
     typedef typename Mfma<T>::frag frag;
@@ -372,12 +377,13 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     // all copies of step kt (the tail form zeroes chunks past K)
     auto issue_all = [&](int kt) __attribute__((always_inline)) {
         unsigned char* st = smem_raw + (kt % STAGES) * STAGE_BYTES;
+        if (wave >= CW) return;
         if (ragged_k && kt == KT - 1) {
 #pragma unroll
-            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, NWAVES, true>(q, st, src, kt * BK, wave, lane);
+            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, CW, true>(q, st, src, kt * BK, wave, lane);
         } else {
 #pragma unroll
-            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, NWAVES, false>(q, st, src, kt * BK, wave, lane);
+            for (int q = 0; q < SLOTS; ++q) stage_slot<Cfg, NSETS, CW, false>(q, st, src, kt * BK, wave, lane);
         }
     };
 
@@ -433,12 +439,13 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if constexpr (decltype(with_issue)::value) {
-                // copies for the next step go out early: spread over the first DMA_SPREAD MFMA steps
+                // copies for the next step go out at once, from the copying wavefronts: spread over
+                // the first DMA_SPREAD MFMA steps (one by default)
                 constexpr int SP = RUDNN_DMA_SPREAD < KS ? RUDNN_DMA_SPREAD : KS;
-                if (ks < SP) {
+                if (ks < SP && wave < CW) {
 #pragma unroll
                     for (int q = ks * SLOTS / SP; q < (ks + 1) * SLOTS / SP; ++q)
-                        stage_slot<Cfg, NSETS, NWAVES, false>(q, st_next, src, kt_next * BK, wave, lane);
+                        stage_slot<Cfg, NSETS, CW, false>(q, st_next, src, kt_next * BK, wave, lane);
                 }
             }
             if constexpr (decltype(with_mfma)::value) {
@@ -472,12 +479,13 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             if constexpr (decltype(with_issue)::value) {
-                // copies for the next step go out early: spread over the first DMA_SPREAD MFMA steps
+                // copies for the next step go out at once, from the copying wavefronts: spread over
+                // the first DMA_SPREAD MFMA steps (one by default)
                 constexpr int SP = RUDNN_DMA_SPREAD < KS ? RUDNN_DMA_SPREAD : KS;
-                if (ks < SP) {
+                if (ks < SP && wave < CW) {
 #pragma unroll
                     for (int q = ks * SLOTS / SP; q < (ks + 1) * SLOTS / SP; ++q)
-                        stage_slot<Cfg, NSETS, NWAVES, false>(q, st_next, src, kt_next * BK, wave, lane);
+                        stage_slot<Cfg, NSETS, CW, false>(q, st_next, src, kt_next * BK, wave, lane);
                 }
             }
             if constexpr (decltype(with_mfma)::value) {
