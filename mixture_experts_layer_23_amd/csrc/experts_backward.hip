@@ -21,7 +21,9 @@
 // Two operand sources may be stacked along the operand's outer index (gate over up).
 // Grouping: ROWS tiles the expert's rows along M (a device-side plan of m-tiles per expert);
 // KROWS uses the expert's rows as the contraction axis, every (expert, m, n) tile (an expert
-// without rows gets zeros).
+// without rows gets zeros).  In the DMA form the ROWS products with a plain epilogue split the
+// tiles of a last, partial round along K (see BSplit); split_reduce finishes them.
+#include <atomic>
 #include <type_traits>
 
 #include "device.hpp"
@@ -170,7 +172,28 @@ struct Epi {
     void* h;              // EPI_SWIGLU: [rows, I] dtype
 };
 
-// The tile of workgroup blockIdx.x: ROWS tiles the experts' dispatched rows (m-tiles from the
+// Tail split of the products over the dispatched rows: tiles run one per CU in rounds; when the
+// tile count leaves a last, partial round of R tiles, each of those is cut along K into S
+// segments (S = CUs / R, at most SPLIT_SLOTS / R, each at least SPLIT_MIN_STEPS K steps), so the
+// last round fills the machine; the grid has SPLIT_SLOTS units beyond the tiles for them.
+constexpr int SPLIT_SLOTS = 256, SPLIT_MIN_STEPS = 8;
+struct BSplit {
+    int64_t full;  // tiles run whole (they come first)
+    int R, S;      // split tiles, segments each (R = 0, S = 1: no split)
+};
+__device__ __forceinline__ BSplit bsplit_plan(int64_t tiles, int KT, int cus) {
+    BSplit sp;
+    int64_t R = tiles >= cus ? tiles % cus : tiles;
+    int S = R > 0 ? (int)min((int64_t)cus / R, (int64_t)SPLIT_SLOTS / R) : 1;
+    S = min(S, KT / SPLIT_MIN_STEPS);
+    if (S < 2) S = 1, R = 0;
+    sp.full = tiles - R;
+    sp.R = (int)R;
+    sp.S = S;
+    return sp;
+}
+
+// Tile L of a product: ROWS tiles the experts' dispatched rows (m-tiles from the
 // device-side plan) by N; KROWS takes every (expert, m-tile, n-tile) with the expert's rows as K.
 // False if the workgroup has no tile.
 struct TileSel {
@@ -179,10 +202,10 @@ struct TileSel {
 };
 template <int MODE, int BM, int BN>
 __device__ __forceinline__ bool pick_tile(const Plan& plan, const int32_t* __restrict__ offsets, int rows, int M,
-                                          int N, int K, int E, int NT, int MT, TileSel& t) {
+                                          int N, int K, int E, int NT, int MT, int64_t L, TileSel& t) {
     t.row0 = 0;
     if (MODE == ROWS) {
-        const int64_t L = blockIdx.x, Mt = L / NT;
+        const int64_t Mt = L / NT;
         if (Mt >= plan.mt_begin[E]) return false;
         int lo = 0, hi = E - 1;  // largest e with mt_begin[e] <= Mt
         while (lo < hi) {
@@ -200,7 +223,6 @@ __device__ __forceinline__ bool pick_tile(const Plan& plan, const int32_t* __res
         t.mlim = min(BM, plan.row_count[t.e] - mt * BM);
         t.kb = 0, t.kn = K;
     } else {
-        const int64_t L = blockIdx.x;
         t.e = (int)(L / ((int64_t)MT * NT));
         const int r = (int)(L % ((int64_t)MT * NT));
         t.m0 = (r / NT) * BM, t.n0 = (r % NT) * BN;
@@ -306,7 +328,7 @@ __global__ __launch_bounds__(C::THREADS) void gemm_kernel(Opnd A, Opnd B, int M,
 
     // ---- which tile ----
     TileSel ts;
-    if (!pick_tile<MODE, BM, BN>(plan, offsets, rows, M, N, K, E, NT, MT, ts)) return;
+    if (!pick_tile<MODE, BM, BN>(plan, offsets, rows, M, N, K, E, NT, MT, blockIdx.x, ts)) return;
     const int e = ts.e, m0 = ts.m0, n0 = ts.n0, mlim = ts.mlim, nlim = ts.nlim, kb = ts.kb, kn = ts.kn;
     const int64_t row0 = ts.row0;
 
@@ -541,10 +563,10 @@ __device__ __forceinline__ v4s read_tr(const unsigned char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
 }
 
-template <typename T, typename C, int MODE, int EPI, bool AK, bool BK>
+template <typename T, typename C, int MODE, int EPI, bool AK, bool BK, bool SPLIT>
 __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(Opnd A, Opnd B, int M, int N, int K, int E, Plan plan,
                                                               const int32_t* __restrict__ offsets, int rows, int NT,
-                                                              int MT, Epi ep) {
+                                                              int MT, Epi ep, int cus, float* __restrict__ partials) {
     static_assert(sizeof(T) == 2, "the DMA form stages 16-bit operands");
     constexpr int BM = C::BM, BN = C::BN, THREADS = C::THREADS, NWAVES = THREADS / 64;
     constexpr int TM = BM / C::WM, TN = BN / C::WN;
@@ -565,7 +587,24 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(Opnd A, Opnd B, in
     extern __shared__ __align__(1024) unsigned char lds[];
 
     TileSel ts;
-    if (!pick_tile<MODE, BM, BN>(plan, offsets, rows, M, N, K, E, NT, MT, ts)) return;
+    // Tail split (SPLIT, ROWS mode): the tiles of a last, partial round of CU-count tiles are cut
+    // along K into S segments whose FP32 partial sums split_reduce adds up (see BSplit).
+    int64_t L = blockIdx.x;
+    int ks0 = 0, ks1 = -1, slot = -1;  // K steps [ks0, ks1) of this unit (ks1 < 0: the whole K)
+    if constexpr (SPLIT) {
+        static_assert(MODE == ROWS, "only products over the dispatched rows are split");
+        const int KTall = (K + BKE - 1) / BKE;
+        const BSplit sp = bsplit_plan((int64_t)plan.mt_begin[E] * NT, KTall, cus);
+        if (L >= sp.full) {
+            const int64_t v = L - sp.full;
+            if (v >= (int64_t)sp.R * sp.S) return;
+            const int seg = (int)(v % sp.S);
+            L = sp.full + v / sp.S;
+            ks0 = (int)((int64_t)seg * KTall / sp.S), ks1 = (int)((int64_t)(seg + 1) * KTall / sp.S);
+            slot = (int)v;
+        }
+    }
+    if (!pick_tile<MODE, BM, BN>(plan, offsets, rows, M, N, K, E, NT, MT, L, ts)) return;
     const int e = ts.e, m0 = ts.m0, n0 = ts.n0, mlim = ts.mlim, nlim = ts.nlim, kb = ts.kb, kn = ts.kn;
     const int64_t row0 = ts.row0;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -655,9 +694,9 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(Opnd A, Opnd B, in
                 copy(B, false, BK, nlim, st + TILE, g - 32, kt);
         }
     };
-    const int KT = (kn + BKE - 1) / BKE;
-    if (KT > 0) issue_part(0, 0, SLOTS);
-    for (int kt = 0; kt < KT; ++kt) {
+    const int KT = ks1 >= 0 ? ks1 : (kn + BKE - 1) / BKE;
+    if (ks0 < KT) issue_part(ks0, 0, SLOTS);
+    for (int kt = ks0; kt < KT; ++kt) {
         wait_vmcnt<0>();  // this wavefront's copies of step kt have landed
         __syncthreads();  // everyone's have; everyone is done with the other stage (step kt - 1)
         const unsigned char* ta = lds + (kt & 1) * 2 * TILE;
@@ -686,19 +725,61 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(Opnd A, Opnd B, in
         }
     }
 
+    if (SPLIT && slot >= 0) {  // a segment: FP32 partial sums of the tile, [slot][BM][BN]
+        const Epi pe{partials + (int64_t)slot * BM * BN, BN, nullptr, nullptr, nullptr};
+        epilogue<T, MODE, EPI_F32, FM, FN, TM, TN>(acc, wm, wn, lane, mlim, nlim, e, M, m0, 0, 0, N, pe);
+        return;
+    }
     epilogue<T, MODE, EPI, FM, FN, TM, TN>(acc, wm, wn, lane, mlim, nlim, e, M, m0, n0, row0, N, ep);
+}
+
+// Adds the S partial sums of every split tile in segment order (deterministic) and stores the
+// product in the dtype (EPI_DT) or FP32: a thread takes four adjacent columns of one row.
+template <typename T, int EPI, int BM, int BN>
+__global__ __launch_bounds__(256) void split_reduce(const float* __restrict__ partials, int K, int N, int E, Plan plan,
+                                                    const int32_t* __restrict__ offsets, int rows, int NT, int cus,
+                                                    Epi ep) {
+    static_assert(EPI == EPI_DT || EPI == EPI_F32, "plain epilogues only");
+    constexpr int BKE = ROWB / (int)sizeof(T);
+    const int KTall = (K + BKE - 1) / BKE;
+    const BSplit sp = bsplit_plan((int64_t)plan.mt_begin[E] * NT, KTall, cus);
+    constexpr int Q = BN / 4;  // column quads per row
+    const int64_t items = (int64_t)sp.R * BM * Q;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items; i += (int64_t)gridDim.x * blockDim.x) {
+        const int r = (int)(i / (BM * Q)), row = (int)(i / Q % BM), col = (int)(i % Q) * 4;
+        TileSel t;
+        pick_tile<ROWS, BM, BN>(plan, offsets, rows, 0, N, K, E, NT, 0, sp.full + r, t);
+        if (row >= t.mlim || col >= t.nlim) continue;
+        const float* p = partials + ((int64_t)r * sp.S * BM + row) * BN + col;
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sg = 0; sg < sp.S; ++sg) {
+            const float4 v = *reinterpret_cast<const float4*>(p + (int64_t)sg * BM * BN);
+            a.x += v.x, a.y += v.y, a.z += v.z, a.w += v.w;
+        }
+        const int64_t crow = t.row0 + row;
+        if (EPI == EPI_F32)
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.c) + crow * ep.ldc + t.n0 + col) = a;
+        else
+            store4<T>(reinterpret_cast<T*>(ep.c) + crow * ep.ldc + t.n0 + col, a.x, a.y, a.z, a.w);
+    }
 }
 
 }  // namespace bwd
 
 // ---- host side ----
 
-// Workspace: [dg | du] [rows, 2I] dtype, h [rows, I] dtype, the plan (3E + 1 ints), then (without
-// a cache) the recomputed pre-activations [g | u] [rows, 2I] FP32.
+// Workspace: [dg | du] [rows, 2I] dtype, h [rows, I] dtype, the plan (3E + 1 ints), (without a
+// cache) the recomputed pre-activations [g | u] [rows, 2I] FP32, then (16-bit types) the tail
+// split's partial-sum slots, SPLIT_SLOTS x 256 x 256 FP32.
+static size_t bwd_split_bytes(rudnn_moe_dtype dt) {
+    return dt == RUDNN_MOE_F32 ? 0 : align_up((size_t)bwd::SPLIT_SLOTS * 256 * 256 * sizeof(float));
+}
+
 size_t experts_backward_workspace_bytes(int64_t E, int64_t I, rudnn_moe_dtype dt, int64_t rows, bool cached) {
     const size_t es = dtype_size(dt);
     return align_up((size_t)rows * 2 * I * es) + align_up((size_t)rows * I * es) +
-           align_up(sizeof(int32_t) * (size_t)(3 * E + 1)) + (cached ? 0 : align_up((size_t)rows * 2 * I * 4));
+           align_up(sizeof(int32_t) * (size_t)(3 * E + 1)) + (cached ? 0 : align_up((size_t)rows * 2 * I * 4)) +
+           bwd_split_bytes(dt);
 }
 
 namespace {
@@ -718,11 +799,27 @@ constexpr bool bwd_dma_enabled() { return RUDNN_BWD_DMA != 0; }
 typedef bwd::Cfg<RUDNN_BWD_ROWS_TILE> RowsCfg;
 typedef bwd::Cfg<RUDNN_BWD_KROWS_TILE> KRowsCfg;
 
+// Compute units of the current device (one round of tiles), cached per device.
+static int bwd_device_cus() {
+    static std::atomic<int> cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 // C = A B^T for one product; a_rows / b_rows: rows of each part of A / B in memory (their byte
 // extents decide whether the 16-bit DMA form's 32-bit buffer offsets reach every element).
+// partials: the tail split's FP32 slots (products over the rows with a plain epilogue, DMA form).
 template <typename T, int MODE, int EPI, bool AK, bool BK>
 void gemm(bwd::Opnd A, bwd::Opnd B, int M, int N, int K, int E, bwd::Plan plan, const int32_t* offsets, int rows,
-          bwd::Epi ep, int64_t a_rows, int64_t b_rows, rudnn_moe_kernel kid, hipStream_t s) {
+          bwd::Epi ep, int64_t a_rows, int64_t b_rows, rudnn_moe_kernel kid, hipStream_t s, float* partials = nullptr) {
     typedef typename std::conditional<MODE == bwd::ROWS, RowsCfg, KRowsCfg>::type C;
     const int NT = (N + C::BN - 1) / C::BN, MT = (M + C::BM - 1) / C::BM;
     const int64_t blocks = MODE == bwd::ROWS ? ((int64_t)rows / C::BM + E) * NT : (int64_t)E * MT * NT;
@@ -732,12 +829,18 @@ void gemm(bwd::Opnd A, bwd::Opnd B, int M, int N, int K, int E, bwd::Plan plan, 
     if constexpr (sizeof(T) == 2) {
         if (bwd_dma_enabled() && a_rows * A.ld * 2 <= OFFSET_LIMIT && b_rows * B.ld * 2 <= OFFSET_LIMIT) {
             constexpr int LDS = 4 * 256 * bwd::ROWB;  // two stages of two 32 KiB operand tiles
+            constexpr bool SPLIT = MODE == bwd::ROWS && EPI != bwd::EPI_SWIGLU;
             static const hipError_t attr = hipFuncSetAttribute(
-                (const void*)bwd::gemm_dma_kernel<T, C, MODE, EPI, AK, BK>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                LDS);
+                (const void*)bwd::gemm_dma_kernel<T, C, MODE, EPI, AK, BK, SPLIT>,
+                hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
             (void)attr;
-            bwd::gemm_dma_kernel<T, C, MODE, EPI, AK, BK><<<dim3((unsigned)blocks), dim3(C::THREADS), LDS, s>>>(
-                A, B, M, N, K, E, plan, offsets, rows, NT, MT, ep);
+            const int cus = bwd_device_cus();
+            const int64_t units = blocks + (SPLIT ? bwd::SPLIT_SLOTS : 0);
+            bwd::gemm_dma_kernel<T, C, MODE, EPI, AK, BK, SPLIT><<<dim3((unsigned)units), dim3(C::THREADS), LDS, s>>>(
+                A, B, M, N, K, E, plan, offsets, rows, NT, MT, ep, cus, partials);
+            if constexpr (SPLIT)
+                bwd::split_reduce<T, EPI, C::BM, C::BN><<<1024, 256, 0, s>>>(partials, K, N, E, plan, offsets, rows, NT,
+                                                                          cus, ep);
             timing_after(kid, s);
             return;
         }
@@ -759,8 +862,9 @@ void run(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int
     T* dgu = (T*)ws;
     T* hbuf = (T*)(ws + align_up((size_t)rows * 2 * I * es));
     int32_t* pl = (int32_t*)((unsigned char*)hbuf + align_up((size_t)rows * I * es));
-    float* gu = cache ? const_cast<float*>(cache)
-                      : (float*)((unsigned char*)pl + align_up(sizeof(int32_t) * (size_t)(3 * E + 1)));
+    unsigned char* after_plan = (unsigned char*)pl + align_up(sizeof(int32_t) * (size_t)(3 * E + 1));
+    float* gu = cache ? const_cast<float*>(cache) : (float*)after_plan;
+    float* partials = (float*)(after_plan + (cache ? 0 : align_up((size_t)rows * 2 * I * 4)));
     bwd::Plan plan{pl, pl + E, pl + 2 * E};
     timing_before(RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_PLAN, s);
     bwd::plan_kernel<<<1, 1024, 0, s>>>(offsets, E, R, RowsCfg::BM, pl, pl + E, pl + 2 * E);
@@ -772,7 +876,7 @@ void run(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int
         gemm<T, bwd::ROWS, bwd::EPI_F32, true, true>({x, x, H, 0, NOSPLIT}, {ex->gate, ex->up, H, IH, I}, R, 2 * I, H,
                                                      E, plan, offsets, R,
                                                      {gu, 2 * (int64_t)I, nullptr, nullptr, nullptr}, R, I,
-                                                     RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_GU, s);
+                                                     RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_GU, s, partials);
     // dh = dy down_e (B(n = i, k = c) = down[e, c, i]: X-major), epilogue -> dg | du, h
     gemm<T, bwd::ROWS, bwd::EPI_SWIGLU, true, false>({dy, dy, H, 0, NOSPLIT}, {ex->down, ex->down, I, IH, NOSPLIT}, R, I,
                                                      H, E, plan, offsets, R, {nullptr, 0, gu, dgu, hbuf}, R, H,
@@ -780,7 +884,7 @@ void run(const rudnn_moe_experts* ex, const void* x, const int32_t* offsets, int
     // dx = [dg | du] [gate; up]  (B(n = c, k = i') = gate[e, i', c] or up[e, i' - I, c]: X-major)
     gemm<T, bwd::ROWS, bwd::EPI_DT, true, false>({dgu, dgu, 2 * (int64_t)I, 0, NOSPLIT}, {ex->gate, ex->up, H, IH, I}, R,
                                                  H, 2 * I, E, plan, offsets, R, {dx, H, nullptr, nullptr, nullptr}, R,
-                                                 I, RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DX, s);
+                                                 I, RUDNN_MOE_KERNEL_EXPERTS_BACKWARD_DX, s, partials);
     // dgate_e = dg^T x, dup_e = du^T x  (both X-major, K = the expert's rows)
     gemm<T, bwd::KROWS, bwd::EPI_F32, false, false>({dgu, dgu, 2 * (int64_t)I, 0, NOSPLIT}, {x, x, H, 0, NOSPLIT}, I, H,
                                                     0, E, plan, offsets, R, {dgate, H, nullptr, nullptr, nullptr}, R,
