@@ -261,6 +261,53 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[FM][FN], int wm, in
         return;
     }
     // ---- epilogue: lane holds row m = fr of each 32-row block, columns 8 (v / 4) + 4 fh + v % 4 ----
+    if constexpr (EPI == EPI_SWIGLU) {
+        // dh -> dg, du, h (N = I).  Per 32-row block, all of the lane's g | u loads go out before any
+        // store (the stores could alias the loads, so the compiler would otherwise wait for each
+        // run's loads in turn: one memory round trip per four outputs).
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int ml = wm * TM + i * 32 + fr;
+            if (ml >= mlim) continue;
+            const int64_t crow = MODE == ROWS ? row0 + ml : (int64_t)e * M + m0 + ml;
+            const float* gr = ep.gu + crow * 2 * (int64_t)N + n0;
+            float4 g4[FN][4], u4[FN][4];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nl = wn * TN + j * 32 + 8 * q + 4 * fh;
+                    if (nl < nlim) {  // N is a multiple of 4: a run of 4 is wholly in or out
+                        g4[j][q] = *reinterpret_cast<const float4*>(gr + nl);
+                        u4[j][q] = *reinterpret_cast<const float4*>(gr + N + nl);
+                    }
+                }
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int nl = wn * TN + j * 32 + 8 * q + 4 * fh;
+                    if (nl >= nlim) continue;
+                    const int n = n0 + nl;
+                    const float gv[4] = {g4[j][q].x, g4[j][q].y, g4[j][q].z, g4[j][q].w};
+                    const float uv[4] = {u4[j][q].x, u4[j][q].y, u4[j][q].z, u4[j][q].w};
+                    float dgv[4], duv[4], hv[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float dh = acc[i][j][4 * q + t], g = gv[t], u = uv[t];
+                        const float s = 1.f / (1.f + expf(-g));
+                        dgv[t] = dh * u * (s * (1.f + g * (1.f - s)));
+                        duv[t] = dh * (g * s);
+                        hv[t] = g * s * u;
+                    }
+                    T* dg = reinterpret_cast<T*>(ep.dgu) + crow * 2 * (int64_t)N + n;
+                    store4<T>(dg, dgv[0], dgv[1], dgv[2], dgv[3]);
+                    store4<T>(dg + N, duv[0], duv[1], duv[2], duv[3]);
+                    store4<T>(reinterpret_cast<T*>(ep.h) + crow * (int64_t)N + n, hv[0], hv[1], hv[2], hv[3]);
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int ml = wm * TM + i * 32 + fr;
@@ -278,27 +325,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[FM][FN], int wm, in
                 if (EPI == EPI_F32) {
                     *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.c) + crow * ep.ldc + n) =
                         make_float4(v0, v1, v2, v3);
-                } else if (EPI == EPI_DT) {
+                } else {
                     store4<T>(reinterpret_cast<T*>(ep.c) + crow * ep.ldc + n, v0, v1, v2, v3);
-                } else {  // dh -> dg, du, h; N = I
-                    const float dh[4] = {v0, v1, v2, v3};
-                    const float* gr = ep.gu + crow * 2 * (int64_t)N + n;
-                    const float4 g4 = *reinterpret_cast<const float4*>(gr);
-                    const float4 u4 = *reinterpret_cast<const float4*>(gr + N);
-                    const float gv[4] = {g4.x, g4.y, g4.z, g4.w}, uv[4] = {u4.x, u4.y, u4.z, u4.w};
-                    float dgv[4], duv[4], hv[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const float g = gv[t], u = uv[t];
-                        const float s = 1.f / (1.f + expf(-g));
-                        dgv[t] = dh[t] * u * (s * (1.f + g * (1.f - s)));
-                        duv[t] = dh[t] * (g * s);
-                        hv[t] = g * s * u;
-                    }
-                    T* dg = reinterpret_cast<T*>(ep.dgu) + crow * 2 * (int64_t)N + n;
-                    store4<T>(dg, dgv[0], dgv[1], dgv[2], dgv[3]);
-                    store4<T>(dg + N, duv[0], duv[1], duv[2], duv[3]);
-                    store4<T>(reinterpret_cast<T*>(ep.h) + crow * (int64_t)N + n, hv[0], hv[1], hv[2], hv[3]);
                 }
             }
     }
