@@ -601,14 +601,13 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(Opnd A, Opnd B, in
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int BKE = ROWB / 2;              // K elements per step (64)
     constexpr int TILE = 256 * ROWB;           // bytes of one operand tile per stage
-    // Copying wavefronts: in the plain epilogues only the first half (one per SIMD: wavefronts w and
-    // w + 4 share one), all at the first MFMA substep, so each SIMD's other wavefront keeps its matrix
-    // core busy while the copies queue for issue (Mixtral-shaped layer: dinput 3.02 -> 2.76 ms, each
-    // weight gradient 1.41 -> 1.25 ms); for the SwiGLU epilogue's product (dh) every wavefront,
-    // spread over the first two substeps, which measured 2-3% faster there.
-    constexpr int CW = EPI == EPI_SWIGLU ? NWAVES : NWAVES / 2;
+    // Copying wavefronts: only the first half (one per SIMD: wavefronts w and w + 4 share one), all at
+    // the first MFMA substep, so each SIMD's other wavefront keeps its matrix core busy while the
+    // copies queue for issue (Mixtral-shaped layer, against every wavefront copying over the first
+    // two substeps: dinput 3.02 -> 2.76 ms, each weight gradient 1.41 -> 1.25 ms, dh 1.62 -> 1.61).
+    constexpr int CW = NWAVES / 2;
     constexpr int SLOTS = 64 / CW;             // copies per copying wavefront per step (32 per operand)
-    constexpr int SPREAD = CW == NWAVES ? 2 : 1;  // MFMA substeps the copies go out under
+    constexpr int SPREAD = 1;                  // MFMA substeps the copies go out under
     static_assert(BM == 256 && BN == 256 && 64 % CW == 0, "operand tiles of 256 x 64, whole copies per wave");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wavefront tiles are whole MFMA blocks");
     typedef typename Mma<T>::frag frag;
