@@ -197,7 +197,12 @@ __device__ __forceinline__ bool find_tile(const Plan& plan, int E, int N, int* s
     return true;
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z) from the hardware exp and reciprocal (v_exp_f32, v_rcp_f32): a few FP32
+// ulps from the exact value, far below the 16-bit rounding of h that follows, and about 20 fewer
+// VALU instructions per output than an IEEE division -- the epilogue runs while the matrix cores
+// idle (Mixtral-shaped gate/up 1.77 -> 1.73 ms, skewed 0.56-0.58 -> 0.54 ms on one box).
+// e^-z = inf for z < -88 gives -0 (z * 0), as the division does; z = -inf gives NaN either way.
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------------------------------
 // MFMA grouped GEMM (bf16 / f16)

@@ -295,7 +295,8 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[FM][FN], int wm, in
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const float dh = acc[i][j][4 * q + t], g = gv[t], u = uv[t];
-                        const float s = 1.f / (1.f + expf(-g));
+                        // hardware exp and reciprocal, as the forward's silu (a few FP32 ulps)
+                        const float s = __builtin_amdgcn_rcpf(1.f + __expf(-g));
                         dgv[t] = dh * u * (s * (1.f + g * (1.f - s)));
                         duv[t] = dh * (g * s);
                         hv[t] = g * s * u;
