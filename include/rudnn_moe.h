@@ -188,6 +188,8 @@ size_t rudnn_moe_experts_workspace_size(const rudnn_moe_experts* ex, int64_t row
  *                   rudnn_moe_dispatch; never read on the host); rows = T*k
  *   expert_output   [rows, H] dtype, written for rows < expert_offsets[E]
  * BF16/F16 run on the matrix cores (MFMA) with FP32 accumulators; F32 runs in FP32 FMA.
+ * In the BF16/F16 path silu takes the hardware exp and reciprocal (a few FP32 ulps from
+ * z / (1 + exp(-z)), below the 16-bit rounding of h).
  * workspace: at least rudnn_moe_experts_workspace_size(ex, rows) bytes, 256-B aligned.
  * Errors: SHAPE, DTYPE, ARGUMENT, UNSUPPORTED, WORKSPACE, DEVICE, RUNTIME.
  */
