@@ -211,6 +211,31 @@ def test_experts_backward_parity(name):
     assert all(torch.equal(a, b) for a, b in zip(again, cached))
 
 
+@pytest.mark.parametrize("name,scale", [("bf16_multi_tile", 40.0), ("f16_multi_ragged", 25.0)])
+def test_experts_backward_large_preactivations(name, scale):
+    """Token rows scaled so that the pre-activations g reach far past the FP32 exp overflow (|g| > 88):
+    the dh epilogue's hardware exp/reciprocal sigmoid gives s = 0 or 1 there, so dg, du and h take
+    their limits on both sides; the products over the rows (dinput with its K-split tail, the weight
+    gradients) see the large operands."""
+    w = BWD_LAYERS[name]
+    say("experts backward, large pre-activations", name, "scale", scale)
+    logits, _ = make_logits(w)
+    x = (make_tokens(w, DEV).float() * scale).to(DTYPES[w.dtype])
+    gate, up, down = make_experts(w, DEV)
+    ex = moe.SwiGluExperts(gate, up, down)
+    idx, wt = moe.route(logits.to(DEV), w.top_k, w.renormalize[0])
+    d = moe.dispatch(idx, x, w.E)
+    g = torch.Generator(device=DEV).manual_seed(w.seed + 7)
+    dy = (torch.randn(d.dispatched.shape, generator=g, device=DEV) * 0.1).to(DTYPES[w.dtype])
+    y, cache = ex.forward_dispatched_training(d)
+    dx, dgate, dup, ddown = cache.backward(dy)
+    rdx, rdg, rdu, rdd = oracle.experts_backward(d.dispatched.cpu(), d.expert_offsets.cpu().numpy(), gate.cpu(),
+                                                 up.cpu(), down.cpu(), dy.cpu())
+    for got, ref, what in ((dx, rdx, "grad_dispatched"), (dgate, rdg, "dgate"), (dup, rdu, "dup"), (ddown, rdd, "ddown")):
+        assert torch.isfinite(torch.as_tensor(ref)).all(), what
+        assert_close(got, ref, w.dtype, what)
+
+
 def _check_preactivations(pre, dispatched, offsets, gate, up, rows):
     """cache[r] = [gate_e . x_r | up_e . x_r] for the listed rows: float64 products of the same
     operands, within the FP32 accumulation bound (H + 2) 2^-24 sum_h |x_h w_h| (per element; the
