@@ -647,133 +647,147 @@ __global__ __launch_bounds__(C::THREADS) void gemm_dma_kernel(Opnd A, Opnd B, in
             slot = (int)v;
         }
     }
-    if (!pick_tile<MODE, BM, BN>(plan, offsets, rows, M, N, K, E, NT, MT, L, ts)) return;
-    const int e = ts.e, m0 = ts.m0, n0 = ts.n0, mlim = ts.mlim, nlim = ts.nlim, kb = ts.kb, kn = ts.kn;
-    const int64_t row0 = ts.row0;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / C::WN, wn = wave % C::WN;
+    // The tile's work.  The products over the rows with a plain epilogue (dinput, the recomputed
+    // g | u; the ones with the tail split) run it inside a one-pass loop: in that form the compiler
+    // keeps the copy addresses of the K loop in scalar registers (per step about 80 vector
+    // instructions in a copying wavefront instead of 225, and no readfirstlane per copy; 243 -> 214
+    // VGPRs), and dinput takes 1.95-1.97 ms instead of 2.25-2.29 on the Mixtral-shaped layer.  The
+    // others keep the straight form (the wrapper made dh slower).
+    auto body = [&]() __attribute__((always_inline)) {
+        if (!pick_tile<MODE, BM, BN>(plan, offsets, rows, M, N, K, E, NT, MT, L, ts)) return;
+        const int e = ts.e, m0 = ts.m0, n0 = ts.n0, mlim = ts.mlim, nlim = ts.nlim, kb = ts.kb, kn = ts.kn;
+        const int64_t row0 = ts.row0;
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave / C::WN, wn = wave % C::WN;
 
-    // The first element of operand part `part` of expert ee (copy offsets are bytes from it).
-    auto part_base = [&](const Opnd& o, int part, int ee) __attribute__((always_inline)) {
-        return (void*)(reinterpret_cast<const T*>(part ? o.p1 : o.p0) + (int64_t)ee * o.estride);
-    };
-    // Copy q of this wavefront for step kt of operand `is_a` into stage st.
-    auto copy = [&](const Opnd& o, bool is_a, bool kmajor, int xlim, unsigned char* st, int gi, int kt)
-        __attribute__((always_inline)) {
-        unsigned char* dst = st + gi * 1024;
-        const int k0 = kt * BKE;
-        if (kmajor) {
-            // rows x = 8 gi + lane / 8 of the tile, chunk slot lane % 8
-            const int x = 8 * gi + lane / 8, xc = min(x, xlim - 1);
-            const int xf = min(8 * gi, xlim - 1);  // the copy's first row: its part
-            const int64_t of = is_a ? (MODE == ROWS ? row0 + xf : (int64_t)(m0 + xf)) : (int64_t)(n0 + xf);
-            const int part = of >= o.split;
-            const int64_t oc = is_a ? (MODE == ROWS ? row0 + xc : (int64_t)(m0 + xc)) : (int64_t)(n0 + xc);
-            const int kk = k0 + ((lane & 7) ^ swz(x)) * 8;
-            if (kk < kn) {
-                const uint32_t off = (uint32_t)((oc - (part ? o.split : 0)) * o.ld + kb + kk) * 2u;
-                dma16(part_base(o, part, MODE == ROWS && is_a ? 0 : e), off, dst);
+        // The first element of operand part `part` of expert ee (copy offsets are bytes from it).
+        auto part_base = [&](const Opnd& o, int part, int ee) __attribute__((always_inline)) {
+            return (void*)(reinterpret_cast<const T*>(part ? o.p1 : o.p0) + (int64_t)ee * o.estride);
+        };
+        // Copy q of this wavefront for step kt of operand `is_a` into stage st.
+        auto copy = [&](const Opnd& o, bool is_a, bool kmajor, int xlim, unsigned char* st, int gi, int kt)
+            __attribute__((always_inline)) {
+            unsigned char* dst = st + gi * 1024;
+            const int k0 = kt * BKE;
+            if (kmajor) {
+                // rows x = 8 gi + lane / 8 of the tile, chunk slot lane % 8
+                const int x = 8 * gi + lane / 8, xc = min(x, xlim - 1);
+                const int xf = min(8 * gi, xlim - 1);  // the copy's first row: its part
+                const int64_t of = is_a ? (MODE == ROWS ? row0 + xf : (int64_t)(m0 + xf)) : (int64_t)(n0 + xf);
+                const int part = of >= o.split;
+                const int64_t oc = is_a ? (MODE == ROWS ? row0 + xc : (int64_t)(m0 + xc)) : (int64_t)(n0 + xc);
+                const int kk = k0 + ((lane & 7) ^ swz(x)) * 8;
+                if (kk < kn) {
+                    const uint32_t off = (uint32_t)((oc - (part ? o.split : 0)) * o.ld + kb + kk) * 2u;
+                    dma16(part_base(o, part, MODE == ROWS && is_a ? 0 : e), off, dst);
+                } else {
+                    *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+                }
             } else {
-                *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+                // k rows 2 gi + lane / 32 of the step, chunk slot lane % 32
+                const int kr = 2 * gi + (lane >> 5), k = k0 + kr;
+                const int kf = min(k0 + 2 * gi, max(kn - 1, 0));  // the copy's first row: its part
+                const int part = (kb + kf) >= o.split;
+                const int c = min((lane & 31) ^ sxm(kr), (xlim - 1) >> 3);
+                const int64_t xo = is_a ? (int64_t)(m0 + 8 * c) : (int64_t)(n0 + 8 * c);
+                if (k < kn) {
+                    const uint32_t off = (uint32_t)((kb + k - (part ? o.split : 0)) * o.ld + xo) * 2u;
+                    dma16(part_base(o, part, MODE == KROWS ? 0 : e), off, dst);
+                } else {
+                    *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+                }
             }
-        } else {
-            // k rows 2 gi + lane / 32 of the step, chunk slot lane % 32
-            const int kr = 2 * gi + (lane >> 5), k = k0 + kr;
-            const int kf = min(k0 + 2 * gi, max(kn - 1, 0));  // the copy's first row: its part
-            const int part = (kb + kf) >= o.split;
-            const int c = min((lane & 31) ^ sxm(kr), (xlim - 1) >> 3);
-            const int64_t xo = is_a ? (int64_t)(m0 + 8 * c) : (int64_t)(n0 + 8 * c);
-            if (k < kn) {
-                const uint32_t off = (uint32_t)((kb + k - (part ? o.split : 0)) * o.ld + xo) * 2u;
-                dma16(part_base(o, part, MODE == KROWS ? 0 : e), off, dst);
-            } else {
-                *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
+        };
 
-    f32x16 acc[FM][FN];
+        f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    // Per-lane fragment offsets.  K-major: row fr of a 32-row block, chunk (2 ks + fh) ^ swz(fr).
-    // X-major: the transpose read of lane l (group g = l / 16, i = l % 16) for 32-x block xb and
-    // half r of substep ks: k = 16 ks + 8 (g / 2) + 4 r + i / 4, x = 32 xb + 16 (g % 2) + 4 (i % 4),
-    // at byte k * 512 + ((x / 8) ^ sxm(k)) * 16 + (x % 8) * 2 = tr_base + (16 ks + 4 r) * 512 +
-    // ((xb ^ tr_sw) << 6).
-    const int fr = lane & 31, fh = lane >> 5;
-    const int tg = lane >> 4, ti = lane & 15;
-    const int tr_base = (8 * (tg >> 1) + (ti >> 2)) * XROWB + (2 * (tg & 1) + ((ti & 3) >> 1)) * 16 + 8 * (ti & 1);
-    const int tr_sw = (ti >> 2) + 4 * (tg >> 1);
-    auto frag_k = [&](const unsigned char* t, int row, int ks) __attribute__((always_inline)) {
-        return *reinterpret_cast<const frag*>(t + (row + fr) * ROWB + (((ks * 2 + fh) ^ swz(fr)) * 16));
-    };
-    auto frag_x = [&](const unsigned char* t, int xb, int ks) __attribute__((always_inline)) {
-        const unsigned char* p = t + tr_base + ks * 16 * XROWB + ((xb ^ tr_sw) << 6);
-        const v4s lo = read_tr(p), hi = read_tr(p + 4 * XROWB);
-        frag f;
-        __builtin_memcpy(&f, &lo, 8);
-        __builtin_memcpy(reinterpret_cast<unsigned char*>(&f) + 8, &hi, 8);
-        return f;
-    };
-
-    // Step kt: the copies of step kt + 1 go out over the first SPREAD MFMA substeps (into the stage
-    // read in step kt - 1), and the fragments of substep ks + 1 are read while the MFMAs of
-    // substep ks run.
-    auto issue_part = [&](int kt, int q0, int q1) __attribute__((always_inline)) {
-        unsigned char* st = lds + (kt & 1) * 2 * TILE;
-        if (wave >= CW) return;
-#pragma unroll
-        for (int q = q0; q < q1; ++q) {
-            const int g = wave + q * CW;  // 0..63: A copies, then B copies
-            if (g < 32)
-                copy(A, true, AK, mlim, st, g, kt);
-            else
-                copy(B, false, BK, nlim, st + TILE, g - 32, kt);
-        }
-    };
-    const int KT = ks1 >= 0 ? ks1 : (kn + BKE - 1) / BKE;
-    if (ks0 < KT) issue_part(ks0, 0, SLOTS);
-    for (int kt = ks0; kt < KT; ++kt) {
-        wait_vmcnt<0>();  // this wavefront's copies of step kt have landed
-        __syncthreads();  // everyone's have; everyone is done with the other stage (step kt - 1)
-        const unsigned char* ta = lds + (kt & 1) * 2 * TILE;
-        const unsigned char* tb = ta + TILE;
-        frag fa[2][FM], fb[2][FN];
-        auto fetch = [&](int ks, int buf) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-                fa[buf][i] = AK ? frag_k(ta, wm * TM + i * 32, ks) : frag_x(ta, (wm * TM) / 32 + i, ks);
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                fb[buf][j] = BK ? frag_k(tb, wn * TN + j * 32, ks) : frag_x(tb, (wn * TN) / 32 + j, ks);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+        // Per-lane fragment offsets.  K-major: row fr of a 32-row block, chunk (2 ks + fh) ^ swz(fr).
+        // X-major: the transpose read of lane l (group g = l / 16, i = l % 16) for 32-x block xb and
+        // half r of substep ks: k = 16 ks + 8 (g / 2) + 4 r + i / 4, x = 32 xb + 16 (g % 2) + 4 (i % 4),
+        // at byte k * 512 + ((x / 8) ^ sxm(k)) * 16 + (x % 8) * 2 = tr_base + (16 ks + 4 r) * 512 +
+        // ((xb ^ tr_sw) << 6).
+        const int fr = lane & 31, fh = lane >> 5;
+        const int tg = lane >> 4, ti = lane & 15;
+        const int tr_base = (8 * (tg >> 1) + (ti >> 2)) * XROWB + (2 * (tg & 1) + ((ti & 3) >> 1)) * 16 + 8 * (ti & 1);
+        const int tr_sw = (ti >> 2) + 4 * (tg >> 1);
+        auto frag_k = [&](const unsigned char* t, int row, int ks) __attribute__((always_inline)) {
+            return *reinterpret_cast<const frag*>(t + (row + fr) * ROWB + (((ks * 2 + fh) ^ swz(fr)) * 16));
         };
-        fetch(0, 0);
+        auto frag_x = [&](const unsigned char* t, int xb, int ks) __attribute__((always_inline)) {
+            const unsigned char* p = t + tr_base + ks * 16 * XROWB + ((xb ^ tr_sw) << 6);
+            const v4s lo = read_tr(p), hi = read_tr(p + 4 * XROWB);
+            frag f;
+            __builtin_memcpy(&f, &lo, 8);
+            __builtin_memcpy(reinterpret_cast<unsigned char*>(&f) + 8, &hi, 8);
+            return f;
+        };
+
+        // Step kt: the copies of step kt + 1 go out over the first SPREAD MFMA substeps (into the stage
+        // read in step kt - 1), and the fragments of substep ks + 1 are read while the MFMAs of
+        // substep ks run.
+        auto issue_part = [&](int kt, int q0, int q1) __attribute__((always_inline)) {
+            unsigned char* st = lds + (kt & 1) * 2 * TILE;
+            if (wave >= CW) return;
 #pragma unroll
-        for (int ks = 0; ks < BKE / 16; ++ks) {
-            if (kt + 1 < KT && ks < SPREAD) issue_part(kt + 1, ks * SLOTS / SPREAD, (ks + 1) * SLOTS / SPREAD);
-            if (ks + 1 < BKE / 16) fetch(ks + 1, (ks + 1) & 1);
+            for (int q = q0; q < q1; ++q) {
+                const int g = wave + q * CW;  // 0..63: A copies, then B copies
+                if (g < 32)
+                    copy(A, true, AK, mlim, st, g, kt);
+                else
+                    copy(B, false, BK, nlim, st + TILE, g - 32, kt);
+            }
+        };
+        const int KT = ks1 >= 0 ? ks1 : (kn + BKE - 1) / BKE;
+        if (ks0 < KT) issue_part(ks0, 0, SLOTS);
+        for (int kt = ks0; kt < KT; ++kt) {
+            wait_vmcnt<0>();  // this wavefront's copies of step kt have landed
+            __syncthreads();  // everyone's have; everyone is done with the other stage (step kt - 1)
+            const unsigned char* ta = lds + (kt & 1) * 2 * TILE;
+            const unsigned char* tb = ta + TILE;
+            frag fa[2][FM], fb[2][FN];
+            auto fetch = [&](int ks, int buf) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FM; ++i)
+                    fa[buf][i] = AK ? frag_k(ta, wm * TM + i * 32, ks) : frag_x(ta, (wm * TM) / 32 + i, ks);
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = MODE == ROWS ? Mma<T>::run(fb[ks & 1][j], fa[ks & 1][i], acc[i][j])
-                                             : Mma<T>::run(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
+                    fb[buf][j] = BK ? frag_k(tb, wn * TN + j * 32, ks) : frag_x(tb, (wn * TN) / 32 + j, ks);
+            };
+            fetch(0, 0);
+#pragma unroll
+            for (int ks = 0; ks < BKE / 16; ++ks) {
+                if (kt + 1 < KT && ks < SPREAD) issue_part(kt + 1, ks * SLOTS / SPREAD, (ks + 1) * SLOTS / SPREAD);
+                if (ks + 1 < BKE / 16) fetch(ks + 1, (ks + 1) & 1);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = MODE == ROWS ? Mma<T>::run(fb[ks & 1][j], fa[ks & 1][i], acc[i][j])
+                                                 : Mma<T>::run(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-    }
 
-    if (SPLIT && slot >= 0) {  // a segment: FP32 partial sums of the tile, [slot][BM][BN]
-        const Epi pe{partials + (int64_t)slot * BM * BN, BN, nullptr, nullptr, nullptr};
-        epilogue<T, MODE, EPI_F32, FM, FN, TM, TN>(acc, wm, wn, lane, mlim, nlim, e, M, m0, 0, 0, N, pe);
-        return;
+        if (SPLIT && slot >= 0) {  // a segment: FP32 partial sums of the tile, [slot][BM][BN]
+            const Epi pe{partials + (int64_t)slot * BM * BN, BN, nullptr, nullptr, nullptr};
+            epilogue<T, MODE, EPI_F32, FM, FN, TM, TN>(acc, wm, wn, lane, mlim, nlim, e, M, m0, 0, 0, N, pe);
+            return;
+        }
+        epilogue<T, MODE, EPI, FM, FN, TM, TN>(acc, wm, wn, lane, mlim, nlim, e, M, m0, n0, row0, N, ep);
+    };
+    if constexpr (MODE == ROWS && EPI != EPI_SWIGLU) {
+#pragma unroll 1
+        for (int pass = 0; pass < 1; ++pass) body();
+    } else {
+        body();
     }
-    epilogue<T, MODE, EPI, FM, FN, TM, TN>(acc, wm, wn, lane, mlim, nlim, e, M, m0, n0, row0, N, ep);
 }
 
 // Adds the S partial sums of every split tile in segment order (deterministic) and stores the
