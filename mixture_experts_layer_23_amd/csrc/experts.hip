@@ -273,14 +273,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // copies queue for issue, and its SIMD's other wavefront keeps the matrix core busy meanwhile.
 // With every wavefront copying, all eight stalled together at the start of each step (measured:
 // Mixtral-shaped experts 2.521-2.523 ms with half the wavefronts copying, 2.557-2.561 ms with all).
-// A row past the end of its matrix re-reads the last row (such rows are never stored); in the
-// last step of a K that is not a multiple of BK, chunks at k >= K are zeroed instead of copied.
+// A row past the end of its region reads zeros through the buffer's range check (or, in the
+// general form, re-reads the last row); such rows are never stored.  In the last step of a K that
+// is not a multiple of BK, chunks at k >= K are zeroed instead of copied.
 // Offsets from a tile's base pointers are 32-bit: a tile spans at most a few MB of a matrix.
 struct StageSrc {
     __amdgpu_buffer_rsrc_t ra;   // token rows of the tile
     __amdgpu_buffer_rsrc_t rb0;  // weight rows (gate, or down)
     __amdgpu_buffer_rsrc_t rb1;  // up weight rows (gate_up only)
     int ld_bytes, last_a, last_b, K, esize;
+    int voff;  // 128-byte rows: this lane's byte offset within any copy (row lane / 8, swizzled chunk)
 };
 
 template <typename Cfg, int NSETS, int NWAVES, bool TAIL>
@@ -305,6 +307,19 @@ __device__ __forceinline__ void stage_slot(int slot, unsigned char* st, const St
     // Only with two stages, whose steps wait for every copy (vmcnt 0): with deeper pipelines
     // the per-step copy counts that the waits assume must not vary.
     if (Cfg::STAGES == 2 && slot < GA / NWAVES && g * RPG > last) return;
+    unsigned char* const dst0 = st + gi * 1024;
+    if constexpr (CPR == 8 && !TAIL) {
+        // Row g * 8 + lane / 8 and chunk (lane % 8) ^ swz(row), where swz(row) = lane / 8 ^ (g & 1)
+        // and g has the parity of the wavefront (the region offsets and the wavefront stride are
+        // even): a per-lane offset fixed for the tile (src.voff) plus a uniform part, so a copy costs
+        // one vector add.  Rows past the region's last valid row read zeros through the buffer's
+        // range check (the range covers exactly the rows a tile may read); their outputs are never
+        // stored.
+        static_assert(GA % 2 == 0 && GB % 2 == 0 && NWAVES % 2 == 0, "copy groups keep the wavefront's parity");
+        const uint32_t off = (uint32_t)src.voff + (uint32_t)(g * RPG * src.ld_bytes + k0 * src.esize);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst0, 16, off, 0, 0, 0);
+        return;
+    }
     const int r = g * RPG + lane / CPR;
     const int kk = k0 + ((lane % CPR) ^ swz<CPR>(r)) * 8;
     const int rr = r < last ? r : last;
@@ -365,6 +380,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::OCC) void grouped_gemm_mfma(cons
     src.last_b = N - 1 - n0;
     src.K = K;
     src.esize = (int)sizeof(T);
+    src.voff = (lane / CPR) * src.ld_bytes + (((lane % CPR) ^ (lane / CPR) ^ (wave & 1)) * 8) * src.esize;
     {
         // raw buffers over exactly the rows a tile may read (the copies clamp to them anyway)
         constexpr int GFX9_RSRC_WORD3 = 0x00020000;  // 32-bit data format, no swizzle
